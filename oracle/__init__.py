@@ -1,0 +1,22 @@
+"""CPU oracle for grouped-query attention over a preallocated KV cache.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything in this
+package. The HIP library never calls it and it never calls the HIP library:
+the two share no code, headers, helpers or constants.
+
+Everything is plain numpy in float64, slow on purpose, written so a reader can
+check it against the pages by eye:
+
+  * ``direct``     -- the cache (append / truncate / reset / bytes) and the
+                      "direct reference" attention: KV heads repeated, a loop
+                      over every query, a plain softmax over keys 0..pos.
+  * ``vectorised`` -- a second, independently written formulation (grouped
+                      reshape, an index-arithmetic mask, guarded softmax),
+                      used to cross-check ``direct``.
+
+Where the pages are silent or disagree, the reading taken is stated in the
+docstring of the function that depends on it.
+"""
+
+from . import direct, vectorised  # noqa: F401
