@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark: GQA decode over a preallocated KV cache on one MI355X.
+
+One step = one pass of the whole hot path over one batch: in-place append of
+each row's new token, grouped-query attention, and the rollback of the cache
+length (so every step sees the same lengths). Workload: Llama-3.1-8B-shaped
+decode, one layer, Hq=32, Hkv=8, d=128, bfloat16, B=32 rows of 4,096 cached
+tokens in 8,192-token reservations, T=1 (attention over 4,097 keys). Inputs are
+seeded synthetic N(0,1)/sqrt(d) values; no weights.
+
+Prints one JSON line. `value` is decode-attention HBM throughput over whole
+steps: algorithmic bytes per step (live K+V, q, out, and the append's read and
+write) divided by the wall time per step. `roofline` reports the attention
+call alone against MI355X's 8 TB/s, timed with HIP events on the stream the
+kernels run on. `prefill` gives chunked-prefill TFLOP/s (B=4, 10,240-token
+prompts fed as 512-token chunks) against the 2.5 PFLOP/s dense bf16 peak.
+`cpu_baseline` times the float64 CPU oracle on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def dev_bf16(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def attention_bytes(lens_after, n_new, hq, hkv, d, T, elem=2):
+    """Algorithmic bytes of one attention call: live K+V, real q, every out slot."""
+    kv = sum(int(s) for s in lens_after) * hkv * d * 2 * elem
+    q = sum(int(n) for n in n_new) * hq * d * elem
+    out = len(lens_after) * hq * T * d * elem
+    return kv + q + out
+
+
+def attention_flops(lens_after, n_new, hq, d):
+    """4*d FLOP per visible (query, key) pair per query head."""
+    pairs = 0
+    for s, n in zip(lens_after, n_new):
+        base = int(s) - int(n)
+        pairs += sum(base + t + 1 for t in range(int(n)))
+    return 4 * d * hq * pairs
+
+
+def fill_decode_cache(torch, cache, shape, seed, tokens, chunk=2048):
+    import workloads as W
+    B = shape.batch
+    hist = []
+    for start in range(0, tokens, chunk):
+        n = min(chunk, tokens - start)
+        ks = np.empty((B, shape.kv_heads, n, shape.head_dim), np.uint16)
+        vs = np.empty_like(ks)
+        for b in range(B):
+            ks[b], vs[b] = W.prefix_kv(shape, seed, b, start, n)
+        hist.append((ks, vs))
+        cache.append(dev_bf16(torch, ks), dev_bf16(torch, vs), [n] * B)
+    return hist
+
+
+def run_decode(torch, steps, warmup):
+    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    import workloads as W
+    sh = W.LLAMA8B_DECODE
+    seed, cached = 1, 4096
+    B, hq, hkv, d = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim
+    # two caches used in turn: each step streams 537 MB that the previous step
+    # did not touch, so the 256 MB last-level cache cannot serve it
+    caches = [KVCache(B, hkv, sh.max_len, d) for _ in range(2)]
+    hist = None
+    for c in caches:
+        hist = fill_decode_cache(torch, c, sh, seed, cached)
+    n = [1] * B
+    q, k, v = W.step_inputs(sh, seed, 10_000, 1, n, pad="normal")
+    qd, kd, vd = dev_bf16(torch, q), dev_bf16(torch, k), dev_bf16(torch, v)
+    out = torch.empty_like(qd)
+    # workspace sized after the append (lengths 4,097)
+    for c in caches:
+        c.append(kd, vd, n)
+    ws_bytes = max(c.workspace_bytes(hq, 1, n) for c in caches)
+    for c in caches:
+        c.truncate([cached] * B)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+
+    def step(i, ev=None):
+        c = caches[i & 1]
+        c.append(kd, vd, n)
+        if ev is not None:
+            ev[0].record()
+        gqa_attention(qd, c, n, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        c.truncate([cached] * B)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+
+    # attention call timed with events on the current stream (a separate pass
+    # over the same steps, so event recording does not perturb the wall clock)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    att_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    att_avg = sum(att_ms) / len(att_ms)
+
+    lens_after = [cached + 1] * B
+    att_b = attention_bytes(lens_after, n, hq, hkv, d, 1)
+    app_b = 2 * 2 * sum(n) * hkv * d * 2
+    return {
+        "shape": sh, "seed": seed, "hist": hist, "q": q, "k": k, "v": v,
+        "wall_s": wall, "att_ms_avg": att_avg, "att_ms_p50": att_ms[len(att_ms) // 2],
+        "att_ms_p10": att_ms[len(att_ms) // 10], "att_ms_p90": att_ms[(9 * len(att_ms)) // 10],
+        "att_bytes": att_b, "append_bytes": app_b, "lens_after": lens_after,
+    }
+
+
+def run_prefill(torch, reps=3):
+    """Chunked prefill: reset, then 20 x (append a 512-token chunk, attention T=512)."""
+    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    import workloads as W
+    sh = W.LLAMA8B_CHUNKED_PREFILL
+    B, hq, hkv, d = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim
+    cache = KVCache(B, hkv, sh.max_len, d)
+    n = [512] * B
+    chunks = []
+    for c in range(20):
+        q, k, v = W.step_inputs(sh, 3, c, 512, n, pad="normal")
+        chunks.append((dev_bf16(torch, q), dev_bf16(torch, k), dev_bf16(torch, v)))
+    out = torch.empty_like(chunks[0][0])
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    flops = [attention_flops([512 * (c + 1)] * B, n, hq, d) for c in range(20)]
+    times = np.zeros(20)
+    for rep in range(reps + 1):
+        cache.reset()
+        evs = []
+        for c, (qd, kd, vd) in enumerate(chunks):
+            cache.append(kd, vd, n)
+            need = cache.workspace_bytes(hq, 512, n)
+            if need > ws.numel():
+                ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gqa_attention(qd, cache, n, out=out, workspace=ws)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        if rep > 0:
+            times += np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    times /= reps
+    total_flops = float(sum(flops))
+    total_s = float(times.sum())
+    tflops = total_flops / total_s / 1e12
+    return {
+        "metric": "chunked prefill attention TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s",
+        "peak": BF16_PEAK_TFLOPS, "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "ms_per_prompt": round(total_s * 1e3, 4),
+        "flop_per_prompt": total_flops,
+        "last_chunk_tflops": round(flops[-1] / times[-1] / 1e12, 2),
+        "config": {"workload": sh.name, "batch": B, "prompt": 10240, "chunk": 512},
+    }
+
+
+def cpu_baseline(res, max_rows=32, budget_s=20.0):
+    """The float64 oracle on the host, one decode step over as many rows as fit the budget."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:       # pragma: no cover
+        threadpool_limits = None
+    from oracle import direct
+    sh = res["shape"]
+    hq, hkv, d = sh.q_heads, sh.kv_heads, sh.head_dim
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    rows_done = 0
+    t0 = time.perf_counter()
+    try:
+        if ctx is not None:
+            ctx.__enter__()
+        for b in range(min(max_rows, sh.batch)):
+            kr = np.concatenate([h[0][b] for h in res["hist"]] + [res["k"][b, :, :1]], axis=1)
+            vr = np.concatenate([h[1][b] for h in res["hist"]] + [res["v"][b, :, :1]], axis=1)
+            direct.attention_row(kr, vr, kr.shape[1], 1, res["q"][b], "bf16", [(h, 0) for h in range(hq)])
+            rows_done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    b_per_row = attention_bytes([res["lens_after"][0]], [1], hq, hkv, d, 1)
+    gbs = rows_done * b_per_row / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_done} of {sh.batch} rows of one decode step (all {hq} heads), "
+                      f"{dt:.2f} s, float64 numpy, 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    res = run_decode(torch, args.steps, args.warmup)
+    step_bytes = res["att_bytes"] + res["append_bytes"]
+    value = step_bytes / res["wall_s"] / 1e9
+    achieved = res["att_bytes"] / (res["att_ms_avg"] * 1e-3) / 1e9
+    line = {
+        "metric": "decode attn HBM GB/s (% peak), Llama-8B shape B=32 S=4096; prefill TFLOP/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["wall_s"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)/sqrt(d) q, k, v; no weights)",
+        "config": {"workload": res["shape"].name, "batch": 32, "q_heads": 32, "kv_heads": 8,
+                   "head_dim": 128, "cached": 4096, "keys": 4097, "T": 1, "max_len": 8192,
+                   "layers": 1, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gqa attention call (decode_kernel + finalize_kernel)",
+                     "bytes_per_launch": res["att_bytes"],
+                     "ms_avg": round(res["att_ms_avg"], 5), "ms_p10": round(res["att_ms_p10"], 5),
+                     "ms_p50": round(res["att_ms_p50"], 5), "ms_p90": round(res["att_ms_p90"], 5)},
+    }
+    if not args.no_prefill:
+        line["prefill"] = run_prefill(torch)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(res)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+"""Grouped-query attention over a contiguous, preallocated KV cache on MI355X.
+
+Thin Python layer over the C ABI of ``libgqakv.so`` (include/gqa_kv.h): torch
+provides device memory and the current stream; every step of the path runs in
+the library's HIP kernels.
+
+    cache = KVCache(batch, kv_heads, max_len, head_dim, dtype=torch.bfloat16)
+    cache.append(k_new, v_new, n_new)          # in place at each row's length
+    out = gqa_attention(q, cache, n_new)       # decode, verify or chunked prefill
+    cache.truncate(new_lens)                   # rollback without copying
+
+Follows "Implement grouped-query attention over a preallocated KV cache, with
+no torch.cat, for both prefill chunks and decode" (inferenceinterviews.com,
+"A strong answer") and the cache of "16. Prefill, decode and the KV cache"
+(inference.shantanugoel.com, "Layout and validity").
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+__all__ = ["KVCache", "gqa_attention", "library_path"]
+
+_DTYPES = {torch.float32: _lib.KV_DTYPE_F32, torch.bfloat16: _lib.KV_DTYPE_BF16}
+
+
+def library_path():
+    return _lib.LIB_PATH
+
+
+def _stream_ptr():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _row_counts(n_new, batch):
+    if isinstance(n_new, torch.Tensor):
+        vals = n_new.detach().to("cpu").tolist()
+    elif isinstance(n_new, int):
+        vals = [n_new] * batch
+    else:
+        vals = [int(x) for x in n_new]
+    if len(vals) != batch:
+        raise ValueError(f"n_new has {len(vals)} entries for {batch} rows")
+    return vals
+
+
+class KVCache:
+    """K and V [B, Hkv, max_len, d] allocated once on the GPU, plus per-row lengths.
+
+    ``k`` and ``v`` are the preallocated buffers themselves (their data
+    pointers never change); ``lens`` is the host copy of the per-row lengths and
+    ``lens_dev`` the device copy the library keeps in stream order.
+    """
+
+    def __init__(self, batch, kv_heads, max_len, head_dim, dtype=torch.bfloat16, device="cuda"):
+        if dtype not in _DTYPES:
+            raise ValueError(f"dtype {dtype} not supported (float32 or bfloat16)")
+        self._lib = _lib.load()
+        device = torch.device(device)
+        if device.type != "cuda":
+            raise ValueError("the cache lives in GPU memory (device='cuda')")
+        shape = (batch, kv_heads, max_len, head_dim)
+        self.k = torch.zeros(shape, dtype=dtype, device=device)
+        self.v = torch.zeros(shape, dtype=dtype, device=device)
+        self.lens_dev = torch.zeros(max(batch, 1), dtype=torch.int32, device=device)
+        self.dtype = dtype
+        self.batch, self.kv_heads, self.max_len, self.head_dim = shape
+        self._ws = None
+        h = ctypes.c_void_p()
+        with torch.cuda.device(device):
+            st = self._lib.kv_cache_create(batch, kv_heads, max_len, head_dim, _DTYPES[dtype],
+                                           ctypes.c_void_p(self.k.data_ptr()),
+                                           ctypes.c_void_p(self.v.data_ptr()),
+                                           ctypes.c_void_p(self.lens_dev.data_ptr()),
+                                           _stream_ptr(), ctypes.byref(h))
+        _lib.check(st, self._lib)
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.kv_cache_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def device(self):
+        return self.k.device
+
+    @property
+    def lens(self):
+        arr = (ctypes.c_int32 * max(1, self.batch))()
+        _lib.check(self._lib.kv_get_lens(self._h, arr), self._lib)
+        return list(arr)[: self.batch]
+
+    @property
+    def bytes(self):
+        """Bytes of the reservation (all of K and V)."""
+        return int(self._lib.kv_cache_bytes(self._h))
+
+    @property
+    def live_bytes(self):
+        """Bytes of the valid K and V prefixes."""
+        return int(self._lib.kv_live_bytes(self._h))
+
+    def _check_tensor(self, x, name, heads):
+        if not isinstance(x, torch.Tensor) or x.device != self.device or x.dtype != self.dtype:
+            raise ValueError(f"{name} must be a {self.dtype} tensor on {self.device}")
+        if x.dim() != 4 or x.shape[0] != self.batch or x.shape[1] != heads or x.shape[3] != self.head_dim:
+            raise ValueError(f"{name} must be [B={self.batch}, {heads}, T, d={self.head_dim}], got {tuple(x.shape)}")
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def append(self, k_new, v_new, n_new):
+        """Write n_new[b] tokens of row b in place at its current length."""
+        self._check_tensor(k_new, "k_new", self.kv_heads)
+        self._check_tensor(v_new, "v_new", self.kv_heads)
+        if k_new.shape != v_new.shape:
+            raise ValueError("k_new and v_new differ in shape")
+        n = _row_counts(n_new, self.batch)
+        st = self._lib.kv_append(self._h, ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
+                                 k_new.shape[2], _lib.int32_array(n), _stream_ptr())
+        _lib.check(st, self._lib)
+
+    def truncate(self, new_lens):
+        """Roll every row back to new_lens[b] tokens (a scalar applies to all rows)."""
+        if isinstance(new_lens, int):
+            new_lens = [new_lens] * self.batch
+        n = _row_counts(new_lens, self.batch)
+        _lib.check(self._lib.kv_truncate(self._h, _lib.int32_array(n), _stream_ptr()), self._lib)
+
+    def reset(self):
+        self.truncate(0)
+
+    def set_policy(self, path=0, keys_per_split=0):
+        """0/1/2 = automatic / split-K decode kernel / chunked-prefill kernel."""
+        _lib.check(self._lib.kv_cache_set_policy(self._h, int(path), int(keys_per_split)), self._lib)
+
+    def workspace_bytes(self, q_heads, T, n_new):
+        n = _row_counts(n_new, self.batch)
+        size = ctypes.c_size_t()
+        _lib.check(self._lib.gqa_attention_workspace_size(self._h, q_heads, T, _lib.int32_array(n),
+                                                          ctypes.byref(size)), self._lib)
+        return int(size.value)
+
+    def _workspace(self, nbytes):
+        if nbytes == 0:
+            return None
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+
+def gqa_attention(q, cache: KVCache, n_new, out=None, workspace=None):
+    """Attention output [B, Hq, T, d] for the n_new[b] tokens each row just appended.
+
+    q: [B, Hq, T, d] (Hq a multiple of the cache's Hkv); padded slots
+    t >= n_new[b] come back as zeros. ``workspace`` (a uint8 CUDA tensor) may be
+    given to avoid the cache's own grow-once scratch buffer.
+    """
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-d tensor [B, Hq, T, d]")
+    cache._check_tensor(q, "q", q.shape[1])
+    B, hq, T, d = q.shape
+    n = _row_counts(n_new, B)
+    arr = _lib.int32_array(n)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        cache._check_tensor(out, "out", hq)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    lib = cache._lib
+    size = ctypes.c_size_t()
+    _lib.check(lib.gqa_attention_workspace_size(cache.handle, hq, T, arr, ctypes.byref(size)), lib)
+    need = int(size.value)
+    if workspace is None:
+        ws = cache._workspace(need)
+    else:
+        if workspace.device != cache.device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the cache's device")
+        ws = workspace
+    ws_ptr = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
+    ws_len = ws.numel() if ws is not None else 0
+    st = lib.gqa_attention(cache.handle, ctypes.c_void_p(q.data_ptr()), hq, T, arr,
+                           ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_len, _stream_ptr())
+    _lib.check(st, lib)
+    return out

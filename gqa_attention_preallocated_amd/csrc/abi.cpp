@@ -1,0 +1,524 @@
+// C ABI of the preallocated-KV-cache GQA library: validation, host lengths,
+// work planning and kernel launches. Declarations and contracts live in
+// include/gqa_kv.h.
+//
+// Pages cited: [GQA] "Implement grouped-query attention over a preallocated KV
+// cache, with no torch.cat, for both prefill chunks and decode"; [CH16]
+// "16. Prefill, decode and the KV cache".
+
+#include "gqa_kv.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <array>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+using namespace gqakv;
+
+struct kv_cache {
+    int32_t batch, kv_heads, max_len, head_dim;
+    kv_dtype dtype;
+    int32_t elem_bytes;
+    void *k, *v;
+    int32_t *lens_dev;
+    std::vector<int32_t> lens;   // host copy, authoritative, updated at enqueue
+    int32_t path_policy = 0;     // 0 auto, 1 split-K decode kernel, 2 prefill kernel
+    int32_t keys_per_split = 0;  // 0 auto
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+kv_status fail(kv_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+kv_status ok() {
+    g_err.clear();
+    return KV_OK;
+}
+
+kv_status device_fail(hipError_t e, const char *what) {
+    return fail(KV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// attention plan
+// ---------------------------------------------------------------------------
+struct RowPlan {
+    int32_t b, len, nnew;
+    int32_t nq, nsplit, lsplit;
+    int64_t pbase;     // -1: direct write
+    int64_t work;      // key tiles x query tiles x kv heads (ordering key)
+};
+
+struct Plan {
+    int group = 0;
+    int nsub = 1;                      // decode subtiles (16 columns each)
+    int dec_cols = 16;
+    std::vector<RowPlan> dec, pre;     // rows per kernel
+    std::vector<int32_t> zero_rows;    // rows with no new tokens (all slots zero)
+    int64_t records = 0;               // partial records (d + 2 floats each)
+    bool need_final = false;
+};
+
+// Target number of decode work items (one wave each) for a full chip: enough
+// to keep several waves per SIMD streaming K/V.
+constexpr int64_t kDecodeWaveTarget = 4096;
+// Prefill work-group slots on the chip (256 CUs x 2 resident work groups).
+constexpr int64_t kPrefillSlots = 512;
+
+void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new, Plan &p) {
+    const int G = q_heads / c->kv_heads;
+    p.group = G;
+    std::vector<int> dec_rows, pre_rows;
+    int max_dec_cols = 0;
+    for (int b = 0; b < c->batch; ++b) {
+        const int n = n_new[b];
+        if (n == 0) {
+            p.zero_rows.push_back(b);
+            continue;
+        }
+        bool use_dec;
+        if (c->path_policy == 1) use_dec = G <= 64;
+        else if (c->path_policy == 2) use_dec = false;
+        else use_dec = (int64_t)G * n <= 64;
+        if (use_dec) {
+            dec_rows.push_back(b);
+            max_dec_cols = std::max<int>(max_dec_cols, (int)std::min<int64_t>((int64_t)G * n, 64));
+        } else {
+            pre_rows.push_back(b);
+        }
+    }
+    // decode: one column width for the launch, at least G so a tile holds a query
+    int need = std::max(max_dec_cols, G);
+    p.nsub = need <= 16 ? 1 : (need <= 32 ? 2 : 4);
+    p.dec_cols = 16 * p.nsub;
+
+    // ---- decode rows: split keys so the launch has about kDecodeWaveTarget waves
+    {
+        const int tq = p.dec_cols / G;
+        int64_t units = 0;
+        for (int b : dec_rows) {
+            const int nq = (int)ceil_div(n_new[b], tq);
+            units += (int64_t)c->kv_heads * nq * ceil_div(c->lens[b], kDecodeKeyTile);
+        }
+        int64_t tps = std::max<int64_t>(4, ceil_div(units, kDecodeWaveTarget));   // tiles per split
+        for (int b : dec_rows) {
+            RowPlan r{};
+            r.b = b;
+            r.len = c->lens[b];
+            r.nnew = n_new[b];
+            r.nq = (int)ceil_div(r.nnew, tq);
+            const int64_t tiles = ceil_div(r.len, kDecodeKeyTile);
+            if (c->keys_per_split > 0) {
+                r.lsplit = (int)(ceil_div(c->keys_per_split, kDecodeKeyTile) * kDecodeKeyTile);
+                r.nsplit = (int)ceil_div(r.len, r.lsplit);
+            } else {
+                r.nsplit = (int)ceil_div(tiles, tps);
+                r.lsplit = (int)(ceil_div(tiles, r.nsplit) * kDecodeKeyTile);
+            }
+            r.work = tiles * r.nq;
+            p.dec.push_back(r);
+        }
+    }
+    // ---- prefill rows: split only rows whose longest item would dominate
+    {
+        const int tq = kPrefillCols / G;
+        int64_t total = 0, longest = 0;
+        for (int b : pre_rows) {
+            const int nq = (int)ceil_div(n_new[b], tq);
+            const int base = c->lens[b] - n_new[b];
+            for (int q = 0; q < nq; ++q) {
+                const int keys = base + std::min((q + 1) * tq, n_new[b]);
+                total += (int64_t)c->kv_heads * ceil_div(keys, kPrefillKeyTile);
+            }
+            longest = std::max<int64_t>(longest, ceil_div(c->lens[b], kPrefillKeyTile));
+        }
+        const int64_t cap = std::max<int64_t>(32, ceil_div(total, kPrefillSlots));   // tiles per item
+        for (int b : pre_rows) {
+            RowPlan r{};
+            r.b = b;
+            r.len = c->lens[b];
+            r.nnew = n_new[b];
+            r.nq = (int)ceil_div(r.nnew, tq);
+            const int64_t tiles = ceil_div(r.len, kPrefillKeyTile);
+            if (c->keys_per_split > 0) {
+                r.lsplit = (int)(ceil_div(c->keys_per_split, kPrefillKeyTile) * kPrefillKeyTile);
+                r.nsplit = (int)ceil_div(r.len, r.lsplit);
+            } else {
+                r.nsplit = (int)ceil_div(tiles, cap);
+                r.lsplit = (int)(ceil_div(tiles, r.nsplit) * kPrefillKeyTile);
+            }
+            r.work = tiles * r.nq;
+            p.pre.push_back(r);
+        }
+        (void)longest;
+    }
+    // heaviest rows first so long items start early
+    auto heavier = [](const RowPlan &x, const RowPlan &y) { return x.work > y.work; };
+    std::stable_sort(p.dec.begin(), p.dec.end(), heavier);
+    std::stable_sort(p.pre.begin(), p.pre.end(), heavier);
+
+    // ---- partial records for split rows
+    p.records = 0;
+    for (auto &r : p.dec) {
+        if (r.nsplit > 1) {
+            r.pbase = p.records;
+            p.records += (int64_t)c->kv_heads * r.nq * r.nsplit * p.dec_cols;
+        } else {
+            r.pbase = -1;
+        }
+    }
+    for (auto &r : p.pre) {
+        if (r.nsplit > 1) {
+            r.pbase = p.records;
+            p.records += (int64_t)c->kv_heads * r.nq * r.nsplit * kPrefillCols;
+        } else {
+            r.pbase = -1;
+        }
+    }
+    p.need_final = !p.zero_rows.empty();
+    for (auto &r : p.dec) p.need_final |= (r.nsplit > 1) || (r.nnew < T);
+    for (auto &r : p.pre) p.need_final |= (r.nsplit > 1) || (r.nnew < T);
+}
+
+size_t workspace_bytes_for(const kv_cache *c, const Plan &p) {
+    if (p.records == 0) return 0;
+    // acc region then (m, l) region, each 256-byte aligned
+    size_t acc = (size_t)p.records * c->head_dim * sizeof(float);
+    acc = (acc + 255) & ~(size_t)255;
+    return acc + (size_t)p.records * 2 * sizeof(float);
+}
+
+kv_status check_attention_args(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new) {
+    if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
+    if (q_heads <= 0 || q_heads % c->kv_heads != 0)
+        return fail(KV_ERR_INVALID_ARG, "q_heads %d is not a positive multiple of kv_heads %d", q_heads,
+                    c->kv_heads);
+    if (q_heads / c->kv_heads > 128)
+        return fail(KV_ERR_UNSUPPORTED, "group size %d > 128", q_heads / c->kv_heads);
+    if (T < 0) return fail(KV_ERR_INVALID_ARG, "T %d < 0", T);
+    if (c->batch > 0 && n_new == nullptr) return fail(KV_ERR_INVALID_ARG, "n_new is null");
+    for (int b = 0; b < c->batch; ++b) {
+        if (n_new[b] < 0 || n_new[b] > T)
+            return fail(KV_ERR_INVALID_ARG, "row %d: n_new %d outside 0..%d", b, n_new[b], T);
+        if (n_new[b] > c->lens[b])
+            return fail(KV_ERR_INVALID_ARG, "row %d: n_new %d > length %d (append before attention)", b,
+                        n_new[b], c->lens[b]);
+    }
+    return KV_OK;
+}
+
+void fill_attn_rows(const std::vector<RowPlan> &rows, size_t lo, size_t hi, int hkv, AttnRows &t) {
+    std::memset(&t, 0, sizeof t);
+    t.n_rows = (int32_t)(hi - lo);
+    int32_t item = 0;
+    for (size_t i = lo; i < hi; ++i) {
+        const RowPlan &r = rows[i];
+        const int j = (int)(i - lo);
+        t.b[j] = r.b;
+        t.len[j] = r.len;
+        t.nnew[j] = r.nnew;
+        t.nsplit[j] = r.nsplit;
+        t.lsplit[j] = r.lsplit;
+        t.pbase[j] = (int32_t)r.pbase;
+        t.item0[j] = item;
+        item += hkv * r.nq * r.nsplit;
+    }
+    t.item0[t.n_rows] = item;
+    t.total_items = item;
+}
+
+}  // namespace
+
+// ===========================================================================
+extern "C" {
+
+kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim,
+                          kv_dtype dtype, void *k_buf, void *v_buf, int32_t *lens_dev, void *stream,
+                          kv_cache **out) {
+    if (out == nullptr) return fail(KV_ERR_INVALID_ARG, "out is null");
+    *out = nullptr;
+    if (dtype != KV_DTYPE_F32 && dtype != KV_DTYPE_BF16)
+        return fail(KV_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+        return fail(KV_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", head_dim);
+    if (batch < 0 || kv_heads <= 0 || max_len <= 0)
+        return fail(KV_ERR_INVALID_ARG, "bad shape batch=%d kv_heads=%d max_len=%d", batch, kv_heads, max_len);
+    if (batch > 0 && (k_buf == nullptr || v_buf == nullptr))
+        return fail(KV_ERR_INVALID_ARG, "k_buf/v_buf is null");
+    if (!aligned16(k_buf) || !aligned16(v_buf) || !aligned16(lens_dev))
+        return fail(KV_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+    if ((int64_t)batch * kv_heads * max_len * head_dim >= (int64_t(1) << 40))
+        return fail(KV_ERR_INVALID_ARG, "cache too large");
+    kv_cache *c = new (std::nothrow) kv_cache;
+    if (c == nullptr) return fail(KV_ERR_DEVICE, "out of host memory");
+    c->batch = batch;
+    c->kv_heads = kv_heads;
+    c->max_len = max_len;
+    c->head_dim = head_dim;
+    c->dtype = dtype;
+    c->elem_bytes = dtype == KV_DTYPE_F32 ? 4 : 2;
+    c->k = k_buf;
+    c->v = v_buf;
+    c->lens_dev = lens_dev;
+    c->lens.assign(batch, 0);
+    if (lens_dev != nullptr) {
+        for (int lo = 0; lo < batch; lo += kMaxRows) {
+            LensTable t{};
+            t.n_rows = std::min(kMaxRows, batch - lo);
+            for (int i = 0; i < t.n_rows; ++i) {
+                t.b[i] = lo + i;
+                t.len[i] = 0;
+            }
+            hipError_t e = launch_set_lens(lens_dev, t, (hipStream_t)stream);
+            if (e != hipSuccess) {
+                delete c;
+                return device_fail(e, "kv_cache_create");
+            }
+        }
+    }
+    *out = c;
+    return ok();
+}
+
+void kv_cache_destroy(kv_cache *c) { delete c; }
+
+kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T, const int32_t *n_new,
+                    void *stream) {
+    if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
+    if (T < 0) return fail(KV_ERR_INVALID_ARG, "T %d < 0", T);
+    if (c->batch > 0 && n_new == nullptr) return fail(KV_ERR_INVALID_ARG, "n_new is null");
+    int64_t total = 0;
+    // [GQA] "A strong answer": a row that would pass max_len raises; here every
+    // row is checked before anything is enqueued, so a failure changes nothing
+    for (int b = 0; b < c->batch; ++b) {
+        if (n_new[b] < 0 || n_new[b] > T)
+            return fail(KV_ERR_INVALID_ARG, "row %d: n_new %d outside 0..%d", b, n_new[b], T);
+        const int64_t s = c->lens[b], n = n_new[b];
+        if (s + n > c->max_len)
+            return fail(KV_ERR_CAPACITY, "row %d: %lld tokens > max_len %d", b, (long long)(s + n), c->max_len);
+        total += n;
+    }
+    if (total > 0) {
+        if (k_new == nullptr || v_new == nullptr) return fail(KV_ERR_INVALID_ARG, "k_new/v_new is null");
+        if (!aligned16(k_new) || !aligned16(v_new))
+            return fail(KV_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+    }
+    std::vector<int> rows;
+    for (int b = 0; b < c->batch; ++b)
+        if (n_new[b] > 0) rows.push_back(b);
+    const int64_t row_bytes = (int64_t)c->head_dim * c->elem_bytes;
+    for (size_t lo = 0; lo < rows.size(); lo += kMaxRows) {
+        AppendArgs a{};
+        a.k = c->k;
+        a.v = c->v;
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.lens_dev = c->lens_dev;
+        a.row_bytes = row_bytes;
+        a.batch = c->batch;
+        a.hkv = c->kv_heads;
+        a.max_len = c->max_len;
+        a.T = T;
+        const size_t hi = std::min(rows.size(), lo + kMaxRows);
+        a.t.n_rows = (int32_t)(hi - lo);
+        int32_t blocks = 0;
+        for (size_t i = lo; i < hi; ++i) {
+            const int j = (int)(i - lo), b = rows[i];
+            a.t.b[j] = b;
+            a.t.start[j] = c->lens[b];
+            a.t.n[j] = n_new[b];
+            a.t.nchunk[j] = (int32_t)ceil_div((int64_t)n_new[b] * row_bytes, kAppendChunk);
+            a.t.block0[j] = blocks;
+            blocks += c->kv_heads * a.t.nchunk[j];
+        }
+        a.t.block0[a.t.n_rows] = blocks;
+        hipError_t e = launch_append(a, blocks, (hipStream_t)stream);
+        if (e != hipSuccess) return device_fail(e, "kv_append");
+    }
+    // the length moves only after the write is enqueued ([GQA] "Common mistakes")
+    for (int b = 0; b < c->batch; ++b) c->lens[b] += n_new[b];
+    return ok();
+}
+
+kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new,
+                                       size_t *bytes) {
+    if (bytes == nullptr) return fail(KV_ERR_INVALID_ARG, "bytes is null");
+    *bytes = 0;
+    kv_status s = check_attention_args(c, q_heads, T, n_new);
+    if (s != KV_OK) return s;
+    if (c->batch == 0 || T == 0) return ok();
+    Plan p;
+    plan_attention(c, q_heads, T, n_new, p);
+    *bytes = workspace_bytes_for(c, p);
+    return ok();
+}
+
+kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
+                        void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    kv_status s = check_attention_args(c, q_heads, T, n_new);
+    if (s != KV_OK) return s;
+    if (c->batch == 0 || T == 0) return ok();
+    if (q == nullptr || out == nullptr) return fail(KV_ERR_INVALID_ARG, "q/out is null");
+    if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
+        return fail(KV_ERR_INVALID_ARG, "q/out/workspace must be 16-byte aligned");
+    Plan p;
+    plan_attention(c, q_heads, T, n_new, p);
+    const size_t need = workspace_bytes_for(c, p);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+    if (p.records > INT32_MAX / 2) return fail(KV_ERR_UNSUPPORTED, "too many split partials");
+
+    hipStream_t st = (hipStream_t)stream;
+    float *ws_acc = (float *)workspace;
+    size_t acc_bytes = ((size_t)p.records * c->head_dim * sizeof(float) + 255) & ~(size_t)255;
+    float *ws_ml = need > 0 ? (float *)((char *)workspace + acc_bytes) : nullptr;
+
+    AttnArgs a{};
+    a.q = q;
+    a.out = out;
+    a.k = c->k;
+    a.v = c->v;
+    a.ws_acc = ws_acc;
+    a.ws_ml = ws_ml;
+    a.batch = c->batch;
+    a.T = T;
+    a.hq = q_heads;
+    a.hkv = c->kv_heads;
+    a.group = p.group;
+    a.max_len = c->max_len;
+    a.head_dim = c->head_dim;
+    a.records = p.records;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c->head_dim));
+
+    for (size_t lo = 0; lo < p.pre.size(); lo += kMaxRows) {
+        fill_attn_rows(p.pre, lo, std::min(p.pre.size(), lo + kMaxRows), c->kv_heads, a.rows);
+        hipError_t e = launch_prefill((int)c->dtype, c->head_dim, a, st);
+        if (e != hipSuccess) return device_fail(e, "gqa_attention (prefill kernel)");
+    }
+    for (size_t lo = 0; lo < p.dec.size(); lo += kMaxRows) {
+        fill_attn_rows(p.dec, lo, std::min(p.dec.size(), lo + kMaxRows), c->kv_heads, a.rows);
+        hipError_t e = launch_decode((int)c->dtype, c->head_dim, p.nsub, a, st);
+        if (e != hipSuccess) return device_fail(e, "gqa_attention (decode kernel)");
+    }
+    if (p.need_final) {
+        // rows needing a combine or zero slots
+        std::vector<std::array<int32_t, 5>> fr;   // b, nnew, nsplit, pbase, cols
+        for (int b : p.zero_rows) fr.push_back({b, 0, 0, 0, 0});
+        for (auto &r : p.dec)
+            if (r.nsplit > 1 || r.nnew < T)
+                fr.push_back({r.b, r.nnew, r.nsplit > 1 ? r.nsplit : 0, (int32_t)std::max<int64_t>(r.pbase, 0),
+                              p.dec_cols});
+        for (auto &r : p.pre)
+            if (r.nsplit > 1 || r.nnew < T)
+                fr.push_back({r.b, r.nnew, r.nsplit > 1 ? r.nsplit : 0, (int32_t)std::max<int64_t>(r.pbase, 0),
+                              kPrefillCols});
+        for (size_t lo = 0; lo < fr.size(); lo += kMaxRows) {
+            FinalArgs f{};
+            f.out = out;
+            f.ws_acc = ws_acc;
+            f.ws_ml = ws_ml;
+            f.batch = c->batch;
+            f.T = T;
+            f.hq = q_heads;
+            f.hkv = c->kv_heads;
+            f.group = p.group;
+            f.head_dim = c->head_dim;
+            f.records = p.records;
+            const size_t hi = std::min(fr.size(), lo + kMaxRows);
+            f.rows.n_rows = (int32_t)(hi - lo);
+            for (size_t i = lo; i < hi; ++i) {
+                const int j = (int)(i - lo);
+                f.rows.b[j] = fr[i][0];
+                f.rows.nnew[j] = fr[i][1];
+                f.rows.nsplit[j] = fr[i][2];
+                f.rows.pbase[j] = fr[i][3];
+                f.rows.cols[j] = fr[i][4];
+            }
+            hipError_t e = launch_finalize((int)c->dtype, c->head_dim, f, st);
+            if (e != hipSuccess) return device_fail(e, "gqa_attention (finalize kernel)");
+        }
+    }
+    return ok();
+}
+
+kv_status kv_truncate(kv_cache *c, const int32_t *new_lens, void *stream) {
+    if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
+    if (c->batch > 0 && new_lens == nullptr) return fail(KV_ERR_INVALID_ARG, "new_lens is null");
+    // [CH16] "Layout and validity": 0 <= n <= current length
+    for (int b = 0; b < c->batch; ++b)
+        if (new_lens[b] < 0 || new_lens[b] > c->lens[b]) return fail(KV_ERR_INVALID_ARG, "Invalid truncation length");
+    if (c->lens_dev != nullptr) {
+        std::vector<int> rows;
+        for (int b = 0; b < c->batch; ++b)
+            if (new_lens[b] != c->lens[b]) rows.push_back(b);
+        for (size_t lo = 0; lo < rows.size(); lo += kMaxRows) {
+            LensTable t{};
+            const size_t hi = std::min(rows.size(), lo + kMaxRows);
+            t.n_rows = (int32_t)(hi - lo);
+            for (size_t i = lo; i < hi; ++i) {
+                t.b[i - lo] = rows[i];
+                t.len[i - lo] = new_lens[rows[i]];
+            }
+            hipError_t e = launch_set_lens(c->lens_dev, t, (hipStream_t)stream);
+            if (e != hipSuccess) return device_fail(e, "kv_truncate");
+        }
+    }
+    for (int b = 0; b < c->batch; ++b) c->lens[b] = new_lens[b];
+    return ok();
+}
+
+kv_status kv_get_lens(const kv_cache *c, int32_t *lens_host) {
+    if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
+    if (c->batch > 0 && lens_host == nullptr) return fail(KV_ERR_INVALID_ARG, "lens_host is null");
+    std::copy(c->lens.begin(), c->lens.end(), lens_host);
+    return ok();
+}
+
+uint64_t kv_cache_bytes(const kv_cache *c) {
+    if (c == nullptr) return 0;
+    return 2ull * (uint64_t)c->batch * c->kv_heads * c->max_len * c->head_dim * c->elem_bytes;
+}
+
+uint64_t kv_live_bytes(const kv_cache *c) {
+    if (c == nullptr) return 0;
+    uint64_t tokens = 0;
+    for (int32_t l : c->lens) tokens += (uint64_t)l;
+    return 2ull * tokens * c->kv_heads * c->head_dim * c->elem_bytes;
+}
+
+const char *kv_last_error(void) { return g_err.c_str(); }
+
+kv_status kv_cache_set_policy(kv_cache *c, int32_t path, int32_t keys_per_split) {
+    if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
+    if (path < 0 || path > 2) return fail(KV_ERR_INVALID_ARG, "path %d not in 0..2", path);
+    if (keys_per_split < 0) return fail(KV_ERR_INVALID_ARG, "keys_per_split %d < 0", keys_per_split);
+    c->path_policy = path;
+    c->keys_per_split = keys_per_split;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Work-item indexing shared by the attention kernels (device) and the host-side
+// launch simulator used by the tests (host): one definition of how a block id
+// becomes (row, kv head, query tile, key split), which key range it reads and
+// which partial records it writes.
+#pragma once
+
+#include <stdint.h>
+
+#include "internal.h"
+
+#if defined(__HIP__)
+#define GQAKV_HD __host__ __device__
+#else
+#define GQAKV_HD
+#endif
+
+namespace gqakv {
+
+GQAKV_HD inline int imin(int a, int b) { return a < b ? a : b; }
+
+// Largest r in [0, n_rows) with item0[r] <= item (item0 is nondecreasing).
+GQAKV_HD inline int find_row(const int32_t *item0, int n_rows, int item) {
+    int lo = 0, hi = n_rows - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (item0[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// One work item of an attention launch (see AttnRows for the numbering).
+struct Item {
+    int b, kvh, qtile, split, nq, nsplit;
+    int base;             // absolute position of the row's query 0 = len - n_new
+    int t0, t_end;        // queries [t0, t_end) of this tile
+    int k_begin, k_end;   // keys of this split that some query of the tile may see
+    int rec0;             // first partial record of the item, or -1: direct write
+};
+
+GQAKV_HD inline Item decode_item(const AttnRows &R, int item, int hkv, int group, int cols) {
+    Item it;
+    const int r = find_row(R.item0, R.n_rows, item);
+    const int n = R.nnew[r];
+    const int tq = cols / group;                  // queries per tile
+    it.nq = (n + tq - 1) / tq;
+    it.nsplit = R.nsplit[r];
+    const int local = item - R.item0[r];
+    it.kvh = local % hkv;
+    const int rest = local / hkv;
+    it.split = rest % it.nsplit;
+    it.qtile = it.nq - 1 - rest / it.nsplit;      // longest key range first
+    it.b = R.b[r];
+    it.base = R.len[r] - n;
+    it.t0 = it.qtile * tq;
+    it.t_end = imin(it.t0 + tq, n);
+    // bottom-right rule: the tile's last query sits at base + t_end - 1 and sees
+    // keys up to that position, never past the row's length
+    const int keys_hi = it.base + it.t_end;
+    it.k_begin = it.split * R.lsplit[r];
+    it.k_end = imin(it.k_begin + R.lsplit[r], keys_hi);
+    it.rec0 = R.pbase[r] < 0 ? -1
+            : R.pbase[r] + ((it.kvh * it.nq + it.qtile) * it.nsplit + it.split) * cols;
+    return it;
+}
+
+// Absolute position of the query in column `col` of the item, or -1 for a
+// padding column (no key visible). Column col holds query t0 + col / G of
+// query head kvh * G + col % G.
+GQAKV_HD inline int column_position(const Item &it, int col, int group, int cols) {
+    const int tq = cols / group;
+    const int t = it.t0 + col / group;
+    return (col < tq * group && t < it.t_end) ? it.base + t : -1;
+}
+
+GQAKV_HD inline int column_t(const Item &it, int col, int group) { return it.t0 + col / group; }
+GQAKV_HD inline int column_head(const Item &it, int col, int group) { return it.kvh * group + col % group; }
+
+// Partial record read by the finalize pass for output (row r, head h, query t), split s = 0.
+GQAKV_HD inline int64_t final_record(const FinalRows &F, int r, int h, int t, int group) {
+    const int cols = F.cols[r];
+    const int tq = cols / group;
+    const int nq = (F.nnew[r] + tq - 1) / tq;
+    const int kvh = h / group, g = h % group;
+    const int qtile = t / tq;
+    const int col = (t % tq) * group + g;
+    return F.pbase[r] + (int64_t)((kvh * nq + qtile) * F.nsplit[r]) * cols + col;
+}
+
+}  // namespace gqakv

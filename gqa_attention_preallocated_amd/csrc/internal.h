@@ -1,0 +1,102 @@
+// Launch tables shared by the host planner (abi.cpp) and the kernels
+// (kernels.hip). Per-row metadata travels in the kernel arguments: the host
+// already holds every row's length, so no host-to-device copy is ever needed
+// and every launch is self-contained (graph-capturable). Rows beyond
+// kMaxRows are split over several launches.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace gqakv {
+
+constexpr int kMaxRows = 64;
+
+// ---------------------------------------------------------------- append
+struct AppendTable {
+    int32_t n_rows;
+    int32_t b[kMaxRows];       // batch row
+    int32_t start[kMaxRows];   // row length before the append (first slot written)
+    int32_t n[kMaxRows];       // tokens written
+    int32_t nchunk[kMaxRows];  // 4 KiB copy chunks per (row, kv head)
+    int32_t block0[kMaxRows + 1];
+};
+
+struct AppendArgs {
+    void *k;                   // cache K [B, Hkv, max_len, d]
+    void *v;
+    const void *k_new;         // [B, Hkv, T, d]
+    const void *v_new;
+    int32_t *lens_dev;         // optional
+    int64_t row_bytes;         // d * element size
+    int32_t batch, hkv, max_len, T;
+    AppendTable t;
+};
+
+struct LensTable {
+    int32_t n_rows;
+    int32_t b[kMaxRows];
+    int32_t len[kMaxRows];
+};
+
+// ------------------------------------------------------------- attention
+// Work item = (row, kv head, query tile, key split). Items of one row are
+// numbered with the kv head fastest, then the split, then the query tile from
+// the last (longest key range) to the first.
+struct AttnRows {
+    int32_t n_rows;
+    int32_t total_items;
+    int32_t b[kMaxRows];
+    int32_t len[kMaxRows];     // keys valid after the append
+    int32_t nnew[kMaxRows];    // real queries of the row
+    int32_t nsplit[kMaxRows];  // key splits per (kv head, query tile)
+    int32_t lsplit[kMaxRows];  // keys per split (multiple of the key tile)
+    int32_t pbase[kMaxRows];   // first partial record of the row; -1: write out directly
+    int32_t item0[kMaxRows + 1];
+};
+
+struct AttnArgs {
+    const void *q;             // [B, Hq, T, d]
+    void *out;                 // [B, Hq, T, d]
+    const void *k;             // cache [B, Hkv, max_len, d]
+    const void *v;
+    float *ws_acc;             // partial records: unnormalised acc [rec][d]
+    float *ws_ml;              // partial records: (running max in log2 units, sum) [rec][2]
+    int32_t batch, T, hq, hkv, group, max_len, head_dim;
+    int64_t records;           // partial records available in the workspace
+    float scale_log2;          // log2(e) / sqrt(d)
+    AttnRows rows;
+};
+
+struct FinalRows {
+    int32_t n_rows;
+    int32_t b[kMaxRows];
+    int32_t nnew[kMaxRows];
+    int32_t nsplit[kMaxRows];  // 0: nothing to combine (written directly, or no queries)
+    int32_t pbase[kMaxRows];
+    int32_t cols[kMaxRows];    // columns per query tile of the kernel that wrote the partials
+};
+
+struct FinalArgs {
+    void *out;
+    const float *ws_acc;
+    const float *ws_ml;
+    int32_t batch, T, hq, hkv, group, head_dim;
+    int64_t records;
+    FinalRows rows;
+};
+
+// element type codes match kv_dtype
+hipError_t launch_append(const AppendArgs &a, int n_blocks, hipStream_t s);
+hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t s);
+// nsub: 16-column subtiles per decode work item (1, 2 or 4)
+hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t s);
+hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t s);
+hipError_t launch_finalize(int dtype, int head_dim, const FinalArgs &a, hipStream_t s);
+
+constexpr int kDecodeKeyTile = 32;
+constexpr int kPrefillKeyTile = 64;
+constexpr int kPrefillCols = 128;
+constexpr int kAppendChunk = 4096;
+
+}  // namespace gqakv

@@ -1,0 +1,701 @@
+// HIP kernels for grouped-query attention over a preallocated KV cache, gfx950.
+//
+// Pages cited (titles; sections named where used):
+//   [GQA]  "Implement grouped-query attention over a preallocated KV cache, with
+//          no torch.cat, for both prefill chunks and decode"
+//   [MASK] "Write the causal mask for a decode step with a KV cache, where the
+//          query is shorter than the keys"
+//   [CH16] "16. Prefill, decode and the KV cache"
+//
+// Matrix-core formulation. Both attention kernels compute, for one KV head,
+//   S^T[key][col] = K[key][:] . Q[col][:]          (MFMA, m = key, n = col)
+//   O^T[d][col]  += V^T[d][key] . P^T[key][col]    (MFMA, m = d,   n = col)
+// where a "column" is one (query, group member) pair: the G query heads that
+// share KV head kvh sit side by side, so every K/V element loaded feeds all G
+// heads and no repeated KV exists ([GQA] "A strong answer", decision 1).
+// With v_mfma_f32_16x16x32_bf16 a lane l holds, for A, row (l%16) and k-slots
+// 8*(l/16)..+7; for B, column (l%16) and the same k-slots; for C, rows
+// 4*(l/16)+i and column (l%16). Putting the key on S^T's m axis leaves each
+// lane with 4 scores of one column; two 16-key blocks give 8 scores, exactly
+// the 8 k-slots the lane needs as B operand of the O^T product, so the
+// probabilities never move between lanes. Only V needs a transpose (k-slots
+// must run along keys), done through LDS.
+//
+// Float32 caches use v_mfma_f32_16x16x4_f32 with the same operand layout
+// (8 values per lane, issued as 8 instructions), so they never round to bf16.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "indexing.h"
+#include "internal.h"
+
+namespace gqakv {
+
+typedef __bf16 bf16_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// ---------------------------------------------------------------------------
+// element traits: 8-element MFMA operands and the 16x16 product
+// ---------------------------------------------------------------------------
+template <typename E> struct Op;
+
+template <> struct Op<bf16_t> {
+    using vec = bf16x8;
+    static constexpr int kBytes = 2;
+    __device__ static inline vec zero() { return __builtin_bit_cast(vec, make_uint4(0, 0, 0, 0)); }
+    __device__ static inline vec gload(const bf16_t *p) {
+        return __builtin_bit_cast(vec, *reinterpret_cast<const uint4 *>(p));
+    }
+    __device__ static inline vec lds_load(const unsigned char *p) {
+        return __builtin_bit_cast(vec, *reinterpret_cast<const uint4 *>(p));
+    }
+    __device__ static inline f32x4 mma(const vec &a, const vec &b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline vec from_f32(const f32x8 &x) { return __builtin_convertvector(x, vec); }
+    // gather 8 elements at byte offsets off[j] from LDS
+    __device__ static inline vec lds_gather(const unsigned char *base, const int *off) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t lo = *reinterpret_cast<const uint16_t *>(base + off[2 * j]);
+            uint32_t hi = *reinterpret_cast<const uint16_t *>(base + off[2 * j + 1]);
+            w[j] = lo | (hi << 16);
+        }
+        return __builtin_bit_cast(vec, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+    __device__ static inline void store4(bf16_t *p, f32x4 v) {
+        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+        bf16x4 b = __builtin_convertvector(v, bf16x4);
+        *reinterpret_cast<uint2 *>(p) = __builtin_bit_cast(uint2, b);
+    }
+};
+
+template <> struct Op<float> {
+    using vec = f32x8;
+    static constexpr int kBytes = 4;
+    __device__ static inline vec zero() { return vec{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}; }
+    __device__ static inline vec gload(const float *p) {
+        float4 a = reinterpret_cast<const float4 *>(p)[0];
+        float4 b = reinterpret_cast<const float4 *>(p)[1];
+        return vec{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    }
+    __device__ static inline vec lds_load(const unsigned char *p) {
+        float4 a = reinterpret_cast<const float4 *>(p)[0];
+        float4 b = reinterpret_cast<const float4 *>(p)[1];
+        return vec{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    }
+    __device__ static inline f32x4 mma(const vec &a, const vec &b, f32x4 c) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+        return c;
+    }
+    __device__ static inline vec from_f32(const f32x8 &x) { return x; }
+    __device__ static inline vec lds_gather(const unsigned char *base, const int *off) {
+        vec r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = *reinterpret_cast<const float *>(base + off[j]);
+        return r;
+    }
+    __device__ static inline void store4(float *p, f32x4 v) {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+__device__ inline float wave_max_across_groups(float v) {
+    // lanes l, l^16, l^32, l^48 hold the same column
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ inline float wave_sum_across_groups(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// append: bit copy of the new tokens into their slots ([GQA] "A strong answer":
+// written in place at the row's current length; nothing else moves)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+    const int r = find_row(a.t.block0, a.t.n_rows, blockIdx.x);
+    const int local = blockIdx.x - a.t.block0[r];
+    const int nch = a.t.nchunk[r];
+    const int kvh = local / nch;
+    const int chunk = local % nch;
+    const int b = a.t.b[r];
+    const int64_t span = (int64_t)a.t.n[r] * a.row_bytes;
+    const int64_t off = (int64_t)chunk * kAppendChunk + threadIdx.x * 16;
+    const int64_t head = (int64_t)b * a.hkv + kvh;
+    if (off < span) {
+        const int64_t src = head * a.T * a.row_bytes + off;
+        const int64_t dst = (head * a.max_len + a.t.start[r]) * a.row_bytes + off;
+        const uint4 kx = *reinterpret_cast<const uint4 *>((const char *)a.k_new + src);
+        const uint4 vx = *reinterpret_cast<const uint4 *>((const char *)a.v_new + src);
+        *reinterpret_cast<uint4 *>((char *)a.k + dst) = kx;
+        *reinterpret_cast<uint4 *>((char *)a.v + dst) = vx;
+    }
+    // the row's new length becomes visible to later kernels in stream order
+    if (a.lens_dev != nullptr && local == 0 && threadIdx.x == 0) a.lens_dev[b] = a.t.start[r] + a.t.n[r];
+}
+
+__global__ __launch_bounds__(64) void set_lens_kernel(int32_t *lens_dev, LensTable t) {
+    const int i = threadIdx.x;
+    if (i < t.n_rows) lens_dev[t.b[i]] = t.len[i];
+}
+
+// ---------------------------------------------------------------------------
+// shared pieces of the two attention kernels
+// ---------------------------------------------------------------------------
+
+// q row of a column (only read when the column is real)
+template <typename E>
+__device__ inline const E *column_q(const AttnArgs &a, const Item &it, int col, int D) {
+    const int t = column_t(it, col, a.group), h = column_head(it, col, a.group);
+    return reinterpret_cast<const E *>(a.q) + (((int64_t)it.b * a.hq + h) * a.T + t) * D;
+}
+
+template <typename E>
+__device__ inline E *column_out(const AttnArgs &a, const Item &it, int col, int D) {
+    const int t = column_t(it, col, a.group), h = column_head(it, col, a.group);
+    return reinterpret_cast<E *>(a.out) + (((int64_t)it.b * a.hq + h) * a.T + t) * D;
+}
+
+// One online-softmax step for the 8 scores a lane holds for its column
+// (two 16-key blocks: s0 = keys 4g..4g+3, s1 = keys 16+4g..16+4g+3 of a
+// 32-key chunk, g = lane/16). Scores arrive unscaled; `pos` is the column's
+// absolute position; `kfirst` the key index of s0[0]'s block row 0. Keys past
+// pos (or past k_end) get probability 0. Returns the rescale factor for the
+// accumulator and writes the probabilities back into s0/s1.
+struct ColState {
+    float m;   // running max, log2 units (-inf until a key is visible)
+    float l;   // this lane's share of the running denominator
+};
+
+// ---------------------------------------------------------------------------
+// split-K decode / verify kernel: one wave per work item, 16*NSUB columns,
+// 32-key tiles streamed from HBM with the next tile in flight
+// ---------------------------------------------------------------------------
+template <typename E, int D, int NSUB>
+__global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
+    using O = Op<E>;
+    using vec = typename O::vec;
+    constexpr int KT = kDecodeKeyTile;            // 32 keys per tile
+    constexpr int KC = D >= 32 ? D / 32 : 1;      // 32-wide chunks of d
+    constexpr int NB = D / 16;                    // 16-row blocks of O^T
+    constexpr int C = 16 * NSUB;
+    constexpr int ROWB = D * O::kBytes;
+    constexpr int RS = ROWB + 16;                 // padded LDS row: conflict-free transposed reads
+    constexpr int CPK = ROWB / 16;                // 16-byte chunks per key row
+    constexpr int VCH = (KT * CPK + 63) / 64;     // V chunks per lane per tile
+    __shared__ __attribute__((aligned(16))) unsigned char lds[KT * RS];
+
+    const int lane = threadIdx.x;
+    const int lr = lane & 15, lg = lane >> 4;
+    const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, C);
+
+    // ---- columns: absolute positions and Q operands (B of S^T)
+    int pos[NSUB];
+    vec qop[NSUB][KC];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+        const int col = s * 16 + lr;
+        pos[s] = column_position(it, col, a.group, C);
+        const E *qp = pos[s] >= 0 ? column_q<E>(a, it, col, D) : nullptr;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            const int d0 = kc * 32 + lg * 8;
+            qop[s][kc] = (qp != nullptr && d0 < D) ? O::gload(qp + d0) : O::zero();
+        }
+    }
+
+    const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
+    const E *kbase = reinterpret_cast<const E *>(a.k) + head * a.max_len * D;
+    const E *vbase = reinterpret_cast<const E *>(a.v) + head * a.max_len * D;
+
+    f32x4 acc[NSUB][NB];
+    ColState st[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+        st[s].m = -INFINITY;
+        st[s].l = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // transposed-read offsets of V inside the LDS tile: k-slot j of this lane
+    int voff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int key = (j < 4) ? lg * 4 + j : 16 + lg * 4 + (j - 4);
+        voff[j] = key * RS + lr * O::kBytes;
+    }
+
+    // ---- prefetch registers
+    vec kop[2][KC];
+    uint4 vreg[VCH];
+    auto load_tile = [&](int tile) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int key = tile + ks * 16 + lr;
+            const bool ok = key < it.k_end;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const int d0 = kc * 32 + lg * 8;
+                kop[ks][kc] = (ok && d0 < D) ? O::gload(kbase + (int64_t)key * D + d0) : O::zero();
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int c = lane + 64 * i;
+            const int key = c / CPK, part = c % CPK;
+            const bool ok = (c < KT * CPK) && (tile + key < it.k_end);
+            vreg[i] = ok ? *reinterpret_cast<const uint4 *>(
+                               reinterpret_cast<const unsigned char *>(vbase + (int64_t)(tile + key) * D) + part * 16)
+                         : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    if (it.k_begin < it.k_end) load_tile(it.k_begin);
+    // smallest position among this item's real columns: tiles ending at or
+    // before it need no mask ([MASK] "A strong answer", tile cases)
+    const int pos_min = it.base + it.t0;
+
+    for (int tile = it.k_begin; tile < it.k_end; tile += KT) {
+        vec kcur[2][KC];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) kcur[ks][kc] = kop[ks][kc];
+        // V tile into LDS (row-major, padded)
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int c = lane + 64 * i;
+            if (c < KT * CPK) {
+                const int key = c / CPK, part = c % CPK;
+                *reinterpret_cast<uint4 *>(lds + key * RS + part * 16) = vreg[i];
+            }
+        }
+        if (tile + KT < it.k_end) load_tile(tile + KT);
+
+        // ---- S^T = K Q^T for the 32 keys
+        f32x4 sc[NSUB][2];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) c = O::mma(kcur[ks][kc], qop[s][kc], c);
+                sc[s][ks] = c;
+            }
+
+        // ---- mask (only tiles that straddle the diagonal or the split end),
+        //      online softmax in log2 units
+        const bool need_mask = (tile + KT > it.k_end) || (tile + KT - 1 > pos_min);
+        f32x8 p[NSUB];
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int ks = j >> 2, i = j & 3;
+                v[j] = sc[s][ks][i] * a.scale_log2;
+                if (need_mask) {
+                    const int key = tile + ks * 16 + lg * 4 + i;
+                    if (key >= it.k_end || key > pos[s]) v[j] = -INFINITY;
+                }
+            }
+            float tmax = v[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, v[j]);
+            tmax = wave_max_across_groups(tmax);
+            const float m_new = fmaxf(st[s].m, tmax);
+            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // fully masked so far: p = 0
+            const float alpha = exp2f(st[s].m - m_use);
+            float lsum = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float e = exp2f(v[j] - m_use);
+                p[s][j] = e;
+                lsum += e;
+            }
+            st[s].l = st[s].l * alpha + lsum;
+            st[s].m = m_new;
+            if (alpha != 1.f) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[s][nb] *= alpha;
+            }
+        }
+
+        __syncthreads();   // V tile visible in LDS
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            int off[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) off[j] = voff[j] + nb * 16 * O::kBytes;
+            const vec vt = O::lds_gather(lds, off);
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) acc[s][nb] = O::mma(vt, O::from_f32(p[s]), acc[s][nb]);
+        }
+        __syncthreads();   // LDS free for the next tile
+    }
+
+    // ---- write: direct (normalised, cast) or partial record
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+        const float l = wave_sum_across_groups(st[s].l);
+        const int col = s * 16 + lr;
+        if (pos[s] < 0) continue;
+        if (it.rec0 < 0) {
+            E *op = column_out<E>(a, it, col, D);
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) O::store4(op + nb * 16 + lg * 4, acc[s][nb] * inv);
+        } else {
+            const int64_t rec = it.rec0 + col;
+            float *ap = a.ws_acc + rec * D;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                *reinterpret_cast<float4 *>(ap + nb * 16 + lg * 4) =
+                    make_float4(acc[s][nb][0], acc[s][nb][1], acc[s][nb][2], acc[s][nb][3]);
+            if (lg == 0) *reinterpret_cast<float2 *>(a.ws_ml + rec * 2) = make_float2(st[s].m, l);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// chunked-prefill kernel: 4 waves x 32 columns = 128 columns per work item,
+// 64-key tiles of K and V shared by the 4 waves through double-buffered LDS.
+// Key tiles past the last query's position are never loaded; tiles wholly at
+// or below the first query's position are not masked; only tiles straddling
+// the diagonal compare indices ([MASK] "A strong answer", tiled-kernel rule).
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
+    using O = Op<E>;
+    using vec = typename O::vec;
+    constexpr int KT = kPrefillKeyTile;           // 64 keys per tile
+    constexpr int KC = D >= 32 ? D / 32 : 1;
+    constexpr int NB = D / 16;
+    constexpr int C = kPrefillCols;               // 128 columns per item
+    constexpr int NS = 2;                         // 16-column subtiles per wave
+    constexpr int ROWB = D * O::kBytes;
+    constexpr int RS = ROWB + 16;
+    constexpr int CPK = ROWB / 16;
+    constexpr int TILE_BYTES = KT * RS;
+    constexpr int PCH = (KT * CPK + 255) / 256;   // 16-byte chunks per thread per tensor
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][TILE_BYTES];   // [buf][K|V]
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, C);
+
+    int pos[NS];
+    vec qop[NS][KC];
+    int wave_pos_max = -1, wave_pos_min = 0x7fffffff;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int col = wave * 32 + s * 16 + lr;
+        pos[s] = column_position(it, col, a.group, C);
+        const E *qp = pos[s] >= 0 ? column_q<E>(a, it, col, D) : nullptr;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            const int d0 = kc * 32 + lg * 8;
+            qop[s][kc] = (qp != nullptr && d0 < D) ? O::gload(qp + d0) : O::zero();
+        }
+    }
+    {
+        // range of real positions among the wave's 32 columns (uniform over the wave)
+        const int tq = C / a.group;
+        const int c_lo = wave * 32, c_hi = min(wave * 32 + 31, tq * a.group - 1);
+        if (c_lo <= c_hi) {
+            const int t_lo = it.t0 + c_lo / a.group;
+            const int t_hi = min(it.t0 + c_hi / a.group, it.t_end - 1);
+            if (t_lo <= t_hi) {
+                wave_pos_min = it.base + t_lo;
+                wave_pos_max = it.base + t_hi;
+            }
+        }
+    }
+
+    const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
+    const unsigned char *kbase = reinterpret_cast<const unsigned char *>(
+        reinterpret_cast<const E *>(a.k) + head * a.max_len * D);
+    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(
+        reinterpret_cast<const E *>(a.v) + head * a.max_len * D);
+
+    f32x4 acc[NS][NB];
+    ColState st[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        st[s].m = -INFINITY;
+        st[s].l = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    int voff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int key = (j < 4) ? lg * 4 + j : 16 + lg * 4 + (j - 4);
+        voff[j] = key * RS + lr * O::kBytes;
+    }
+
+    uint4 kreg[PCH], vreg[PCH];
+    auto load_tile = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < PCH; ++i) {
+            const int c = tid + 256 * i;
+            const int key = c / CPK, part = c % CPK;
+            const bool ok = (c < KT * CPK) && (tile + key < it.k_end);
+            const int64_t goff = (int64_t)(tile + key) * ROWB + part * 16;
+            kreg[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + goff) : make_uint4(0, 0, 0, 0);
+            vreg[i] = ok ? *reinterpret_cast<const uint4 *>(vbase + goff) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < PCH; ++i) {
+            const int c = tid + 256 * i;
+            if (c < KT * CPK) {
+                const int key = c / CPK, part = c % CPK;
+                *reinterpret_cast<uint4 *>(&lds[buf][0][key * RS + part * 16]) = kreg[i];
+                *reinterpret_cast<uint4 *>(&lds[buf][1][key * RS + part * 16]) = vreg[i];
+            }
+        }
+    };
+
+    if (it.k_begin < it.k_end) load_tile(it.k_begin);
+    int buf = 0;
+    for (int tile = it.k_begin; tile < it.k_end; tile += KT) {
+        store_tile(buf);
+        __syncthreads();
+        if (tile + KT < it.k_end) load_tile(tile + KT);
+
+        if (tile <= wave_pos_max) {
+            const unsigned char *kl = lds[buf][0];
+            const unsigned char *vl = lds[buf][1];
+            const bool need_mask = (tile + KT > it.k_end) || (tile + KT - 1 > wave_pos_min);
+            // two 32-key chunks; each chunk's scores feed the chunk's O^T update
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                f32x4 sc[NS][2];
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    sc[s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    sc[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int krow = ch * 32 + ks * 16 + lr;
+#pragma unroll
+                    for (int kc = 0; kc < KC; ++kc) {
+                        const int d0 = kc * 32 + lg * 8;
+                        const vec kv = (d0 < D) ? O::lds_load(kl + krow * RS + d0 * O::kBytes) : O::zero();
+#pragma unroll
+                        for (int s = 0; s < NS; ++s) sc[s][ks] = O::mma(kv, qop[s][kc], sc[s][ks]);
+                    }
+                }
+                f32x8 p[NS];
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    float v[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int ks = j >> 2, i = j & 3;
+                        v[j] = sc[s][ks][i] * a.scale_log2;
+                        if (need_mask) {
+                            const int key = tile + ch * 32 + ks * 16 + lg * 4 + i;
+                            if (key >= it.k_end || key > pos[s]) v[j] = -INFINITY;
+                        }
+                    }
+                    float tmax = v[0];
+#pragma unroll
+                    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, v[j]);
+                    tmax = wave_max_across_groups(tmax);
+                    const float m_new = fmaxf(st[s].m, tmax);
+                    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                    const float alpha = exp2f(st[s].m - m_use);
+                    float lsum = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float e = exp2f(v[j] - m_use);
+                        p[s][j] = e;
+                        lsum += e;
+                    }
+                    st[s].l = st[s].l * alpha + lsum;
+                    st[s].m = m_new;
+                    if (alpha != 1.f) {
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) acc[s][nb] *= alpha;
+                    }
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    int off[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) off[j] = voff[j] + ch * 32 * RS + nb * 16 * O::kBytes;
+                    const vec vt = O::lds_gather(vl, off);
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt, O::from_f32(p[s]), acc[s][nb]);
+                }
+            }
+        }
+        buf ^= 1;
+    }
+
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const float l = wave_sum_across_groups(st[s].l);
+        const int col = wave * 32 + s * 16 + lr;
+        if (pos[s] < 0) continue;
+        if (it.rec0 < 0) {
+            E *op = column_out<E>(a, it, col, D);
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) O::store4(op + nb * 16 + lg * 4, acc[s][nb] * inv);
+        } else {
+            const int64_t rec = it.rec0 + col;
+            float *ap = a.ws_acc + rec * D;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                *reinterpret_cast<float4 *>(ap + nb * 16 + lg * 4) =
+                    make_float4(acc[s][nb][0], acc[s][nb][1], acc[s][nb][2], acc[s][nb][3]);
+            if (lg == 0) *reinterpret_cast<float2 *>(a.ws_ml + rec * 2) = make_float2(st[s].m, l);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// finalize: merge split partials by log-sum-exp in a fixed order, normalise,
+// cast; write +0.0 into every padded slot (t >= n_new) and every slot of a
+// row with no new tokens ([GQA] "A strong answer": zeros, never NaN)
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+__global__ __launch_bounds__(256) void finalize_kernel(FinalArgs a) {
+    using O = Op<E>;
+    constexpr int TPR = D / 4;              // threads per output row (4 elements each)
+    constexpr int RPP = 256 / TPR;          // rows per pass
+    const int r = blockIdx.x / a.hq;
+    const int h = blockIdx.x % a.hq;
+    const int b = a.rows.b[r];
+    const int n = a.rows.nnew[r];
+    const int nsplit = a.rows.nsplit[r];
+    const int cols = a.rows.cols[r];
+    const int d = (threadIdx.x % TPR) * 4;
+    E *out = reinterpret_cast<E *>(a.out) + ((int64_t)b * a.hq + h) * a.T * D;
+    for (int t = threadIdx.x / TPR; t < a.T; t += RPP) {
+        E *op = out + (int64_t)t * D + d;
+        if (t >= n) {
+            O::store4(op, f32x4{0.f, 0.f, 0.f, 0.f});
+            continue;
+        }
+        if (nsplit == 0) continue;    // written by the attention kernel
+        const int64_t rec = final_record(a.rows, r, h, t, a.group);
+        float mmax = -INFINITY;
+        for (int s = 0; s < nsplit; ++s) mmax = fmaxf(mmax, a.ws_ml[(rec + (int64_t)s * cols) * 2]);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        float l = 0.f;
+        if (mmax != -INFINITY) {
+            for (int s = 0; s < nsplit; ++s) {
+                const int64_t rs = rec + (int64_t)s * cols;
+                const float2 ml = *reinterpret_cast<const float2 *>(a.ws_ml + rs * 2);
+                const float w = exp2f(ml.x - mmax);     // a split with no visible key has m = -inf: w = 0
+                const float4 x = *reinterpret_cast<const float4 *>(a.ws_acc + rs * D + d);
+                acc[0] += w * x.x; acc[1] += w * x.y; acc[2] += w * x.z; acc[3] += w * x.w;
+                l += w * ml.y;
+            }
+        }
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        O::store4(op, acc * inv);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_append(const AppendArgs &a, int n_blocks, hipStream_t s) {
+    if (n_blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(append_kernel, dim3(n_blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t s) {
+    if (t.n_rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(set_lens_kernel, dim3(1), dim3(64), 0, s, lens_dev, t);
+    return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t decode_d(int nsub, const AttnArgs &a, hipStream_t s) {
+    const dim3 grid(a.rows.total_items), block(64);
+    switch (nsub) {
+        case 1: hipLaunchKernelGGL((decode_kernel<E, D, 1>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<E, D, 2>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<E, D, 4>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename E>
+static hipError_t decode_e(int head_dim, int nsub, const AttnArgs &a, hipStream_t s) {
+    switch (head_dim) {
+        case 16: return decode_d<E, 16>(nsub, a, s);
+        case 32: return decode_d<E, 32>(nsub, a, s);
+        case 64: return decode_d<E, 64>(nsub, a, s);
+        case 128: return decode_d<E, 128>(nsub, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t s) {
+    if (a.rows.total_items <= 0) return hipSuccess;
+    return dtype == 0 ? decode_e<float>(head_dim, nsub, a, s) : decode_e<bf16_t>(head_dim, nsub, a, s);
+}
+
+template <typename E>
+static hipError_t prefill_e(int head_dim, const AttnArgs &a, hipStream_t s) {
+    const dim3 grid(a.rows.total_items), block(256);
+    switch (head_dim) {
+        case 16: hipLaunchKernelGGL((prefill_kernel<E, 16>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((prefill_kernel<E, 32>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((prefill_kernel<E, 64>), grid, block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((prefill_kernel<E, 128>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t s) {
+    if (a.rows.total_items <= 0) return hipSuccess;
+    return dtype == 0 ? prefill_e<float>(head_dim, a, s) : prefill_e<bf16_t>(head_dim, a, s);
+}
+
+template <typename E>
+static hipError_t finalize_e(int head_dim, const FinalArgs &a, hipStream_t s) {
+    const dim3 grid(a.rows.n_rows * a.hq), block(256);
+    switch (head_dim) {
+        case 16: hipLaunchKernelGGL((finalize_kernel<E, 16>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((finalize_kernel<E, 32>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((finalize_kernel<E, 64>), grid, block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((finalize_kernel<E, 128>), grid, block, 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(int dtype, int head_dim, const FinalArgs &a, hipStream_t s) {
+    if (a.rows.n_rows <= 0 || a.hq <= 0) return hipSuccess;
+    return dtype == 0 ? finalize_e<float>(head_dim, a, s) : finalize_e<bf16_t>(head_dim, a, s);
+}
+
+}  // namespace gqakv

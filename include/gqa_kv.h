@@ -1,0 +1,173 @@
+/*
+ * gqa_kv.h -- grouped-query attention over a contiguous, preallocated KV cache
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow three pages:
+ *   [GQA]  "Implement grouped-query attention over a preallocated KV cache, with
+ *          no torch.cat, for both prefill chunks and decode" (inferenceinterviews.com)
+ *   [MASK] "Write the causal mask for a decode step with a KV cache, where the
+ *          query is shorter than the keys" (inferenceinterviews.com)
+ *   [CH16] "16. Prefill, decode and the KV cache" (inference.shantanugoel.com)
+ *
+ * Ownership. The caller owns every device buffer (K, V, the optional device
+ * copy of the lengths, q, out, k_new, v_new, the workspace) and every stream.
+ * The library owns only the opaque handle and its host copy of the per-row
+ * lengths; it never allocates device memory.
+ *
+ * Layout. All device arrays are dense and row-major:
+ *   K, V            [B, Hkv, max_len, d]   ([GQA] "A strong answer")
+ *   k_new, v_new    [B, Hkv, T, d]         (slots t >= n_new[b] are padding)
+ *   q, out          [B, Hq,  T, d]
+ * q, out, k_new, v_new and the cache share one element type. Every device
+ * pointer must be 16-byte aligned. Supported d: 16, 32, 64, 128. Hq must be a
+ * positive multiple of Hkv, with group size G = Hq / Hkv <= 128.
+ *
+ * Ordering. Calls are enqueued on the given HIP stream (NULL = the null
+ * stream) and return without waiting for the device. The host copy of the
+ * lengths is updated when a call is enqueued, so host-side validation of the
+ * next call sees it at once. All calls on one handle must be issued from one
+ * host thread at a time and kept in stream order by the caller.
+ *
+ * Errors. Every call validates all of its arguments on the host before it
+ * enqueues anything. A status other than KV_OK means nothing was enqueued and
+ * no state changed: not the host lengths, not the device lengths, not a byte
+ * of K or V. kv_last_error() returns the message of the last failing call on
+ * the calling thread.
+ */
+#ifndef GQA_KV_H
+#define GQA_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kv_cache kv_cache;
+
+typedef enum kv_status {
+    KV_OK = 0,
+    KV_ERR_INVALID_ARG = 1,   /* bad pointer, shape, n_new or truncation length */
+    KV_ERR_CAPACITY = 2,      /* an append would pass max_len                    */
+    KV_ERR_UNSUPPORTED = 3,   /* head_dim, dtype or group size not built         */
+    KV_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required      */
+    KV_ERR_DEVICE = 5         /* a HIP call failed                               */
+} kv_status;
+
+typedef enum kv_dtype {
+    KV_DTYPE_F32 = 0,         /* IEEE float32 storage and float32 arithmetic     */
+    KV_DTYPE_BF16 = 1         /* bfloat16 storage, float32 accumulation          */
+} kv_dtype;
+
+/*
+ * Wrap caller-allocated cache buffers in a handle.
+ * [GQA] "A strong answer" (the cache is allocated once as [B, Hkv, max_len, d]
+ * plus a length per row); [CH16] "Layout and validity" (capacity vs length).
+ *   k_buf, v_buf  device, B*Hkv*max_len*d elements each. Their contents are
+ *                 never read outside a row's valid prefix; the caller should
+ *                 zero-fill them if it wants bit-defined tails.
+ *   lens_dev      optional device int32[B] that the library keeps equal to the
+ *                 per-row lengths in stream order (append, truncate). May be NULL.
+ *                 When given, it is set to zero on `stream` here.
+ *   out           receives the handle.
+ * All rows start empty. Returns KV_ERR_UNSUPPORTED for a head_dim outside
+ * {16,32,64,128} or an unknown dtype, KV_ERR_INVALID_ARG for non-positive
+ * kv_heads/max_len, negative batch or NULL/misaligned buffers.
+ */
+kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim,
+                          kv_dtype dtype, void *k_buf, void *v_buf, int32_t *lens_dev,
+                          void *stream, kv_cache **out);
+
+/* Release the handle (never the caller's buffers). NULL is ignored. */
+void kv_cache_destroy(kv_cache *c);
+
+/*
+ * Append in place: for each row b, write k_new[b,:,0:n_new[b]] and
+ * v_new[b,:,0:n_new[b]] into K and V at positions lens[b] .. lens[b]+n_new[b]-1,
+ * then advance lens[b] by n_new[b]. History is never moved and nothing is
+ * concatenated. [GQA] "A strong answer" (in-place write at the row's length),
+ * [CH16] "Layout and validity" (capacity checked before the copy).
+ *   k_new, v_new  device [B, Hkv, T, d]; padded slots are never read.
+ *   T             slots per row in k_new (>= 0).
+ *   n_new         HOST int32[B], 0 <= n_new[b] <= T.
+ * Every row is checked before anything is written: if lens[b] + n_new[b] >
+ * max_len for any b the call returns KV_ERR_CAPACITY with the message
+ * "row {b}: {lens[b]+n_new[b]} tokens > max_len {max_len}" and changes nothing.
+ * The bytes are copied bit for bit.
+ */
+kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T,
+                    const int32_t *n_new, void *stream);
+
+/*
+ * Workspace that gqa_attention needs for this call (split-K partial results),
+ * in bytes, written to *bytes. Depends on the current lengths and n_new.
+ * Zero means no workspace is needed.
+ */
+kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32_t T,
+                                       const int32_t *n_new, size_t *bytes);
+
+/*
+ * Grouped-query attention for the n_new[b] tokens each row just appended
+ * (call it after kv_append of the same step).
+ * [GQA] "A strong answer" and TL;DR: query head h reads KV head h / G with no
+ * repeated KV; query t of row b sits at absolute position
+ * lens[b] - n_new[b] + t and sees key j iff j <= lens[b] - n_new[b] + t and
+ * j < lens[b] ([MASK] TL;DR: the bottom-right-aligned rule j <= i + (S - T),
+ * evaluated as index arithmetic, never as a mask tensor). Scores are scaled by
+ * 1/sqrt(d). Slots t >= n_new[b], rows with n_new[b] == 0, B == 0 and T == 0
+ * give +0.0 (never NaN).
+ *   q             device [B, q_heads, T, d]; out device [B, q_heads, T, d].
+ *   n_new         HOST int32[B] with 0 <= n_new[b] <= min(T, lens[b]).
+ *   workspace     device scratch of at least gqa_attention_workspace_size()
+ *                 bytes (may be NULL when that size is 0).
+ * Returns KV_ERR_INVALID_ARG for a bad shape, a q_heads that is not a positive
+ * multiple of kv_heads, or a bad n_new; KV_ERR_UNSUPPORTED when G > 128;
+ * KV_ERR_WORKSPACE when the workspace is too small.
+ */
+kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
+                        const int32_t *n_new, void *out, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
+ * Roll back: set lens[b] = new_lens[b] for every row, copying and clearing
+ * nothing. [CH16] "Layout and validity" (truncate for speculative rollback;
+ * stale slots stay and are never read). new_lens is a HOST int32[B] with
+ * 0 <= new_lens[b] <= lens[b]; otherwise KV_ERR_INVALID_ARG with the message
+ * "Invalid truncation length". Truncating every row to 0 is a reset.
+ */
+kv_status kv_truncate(kv_cache *c, const int32_t *new_lens, void *stream);
+
+/* Copy the host lengths (as of the last enqueued call) into lens_host[B]. */
+kv_status kv_get_lens(const kv_cache *c, int32_t *lens_host);
+
+/*
+ * Bytes of the reservation, 2 * B * Hkv * max_len * d * element size
+ * ([CH16] "Layout and validity", the bytes property).
+ */
+uint64_t kv_cache_bytes(const kv_cache *c);
+
+/*
+ * Bytes of valid K and V, 2 * sum(lens) * Hkv * d * element size
+ * ([CH16] "How big is the cache?" with tokens = the current lengths).
+ */
+uint64_t kv_live_bytes(const kv_cache *c);
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char *kv_last_error(void);
+
+/*
+ * Kernel selection, for tests and tuning. path: 0 = automatic (rows with
+ * G * n_new[b] <= 64 use the split-K decode kernel, the others the tiled
+ * chunked-prefill kernel), 1 = every row through the split-K decode kernel,
+ * 2 = every row through the chunked-prefill kernel. keys_per_split: 0 =
+ * automatic, otherwise the key range of one split (rounded up to the key
+ * tile). The result is the same attention up to float32 rounding order.
+ */
+kv_status kv_cache_set_policy(kv_cache *c, int32_t path, int32_t keys_per_split);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_KV_H */

@@ -1,0 +1,251 @@
+// Host-side stand-in for the kernel launchers of libgqakv (test infrastructure).
+//
+// Linked with the library's real host code (abi.cpp) instead of kernels.hip,
+// it replays every launch the planner issues, block by block and column by
+// column, using the same indexing functions the kernels use (indexing.h), and
+// checks on the CPU that
+//   * every K/V/q/out/workspace/lens access lies inside a registered buffer,
+//   * append writes only the slots [lens, lens + n_new) of each row, once,
+//   * each attention call writes every output row (b, h, t) exactly once,
+//   * each split partial is written once before the combine reads it.
+// Buffers are fake addresses registered by the test; nothing is dereferenced.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "indexing.h"
+#include "internal.h"
+
+namespace {
+
+struct Region {
+    uintptr_t base;
+    size_t size;
+    std::string name;
+};
+
+std::vector<Region> g_regions;
+std::vector<std::string> g_errors;
+std::map<uintptr_t, int> g_out_rows;   // start address of an output row -> writes
+std::map<int64_t, int> g_records;      // partial record -> writes
+std::map<uintptr_t, int> g_appended;   // 16-byte chunk of K -> writes
+std::vector<int32_t> g_lens_dev;
+int64_t g_launches = 0;
+
+void err(const std::string &m) {
+    if (g_errors.size() < 64) g_errors.push_back(m);
+}
+
+void access(const void *p, size_t bytes, const char *want, const char *what) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    for (const Region &r : g_regions) {
+        if (a >= r.base && a + bytes <= r.base + r.size) {
+            if (r.name != want)
+                err(std::string(what) + ": hits buffer " + r.name + ", expected " + want);
+            return;
+        }
+    }
+    char buf[160];
+    snprintf(buf, sizeof buf, "%s: %zu bytes at %#lx outside every buffer (want %s)", what, bytes,
+             (unsigned long)a, want);
+    err(buf);
+}
+
+}  // namespace
+
+extern "C" {
+
+void hostcheck_reset() {
+    g_regions.clear();
+    g_errors.clear();
+    g_out_rows.clear();
+    g_records.clear();
+    g_appended.clear();
+    g_lens_dev.clear();
+    g_launches = 0;
+}
+
+void hostcheck_region(uintptr_t base, size_t size, const char *name) { g_regions.push_back({base, size, name}); }
+
+// Start a new attention call: forget output-row and record counts.
+void hostcheck_begin_call() {
+    g_out_rows.clear();
+    g_records.clear();
+}
+
+int hostcheck_error_count() { return (int)g_errors.size(); }
+
+const char *hostcheck_error(int i) { return (i >= 0 && i < (int)g_errors.size()) ? g_errors[i].c_str() : ""; }
+
+int64_t hostcheck_launches() { return g_launches; }
+
+// Writes recorded for output row i of an [rows, row_bytes] array at base.
+int hostcheck_out_row_writes(uintptr_t base, int64_t i, int64_t row_bytes) {
+    auto it = g_out_rows.find(base + (uintptr_t)(i * row_bytes));
+    return it == g_out_rows.end() ? 0 : it->second;
+}
+
+int64_t hostcheck_out_rows_total() {
+    int64_t n = 0;
+    for (auto &kv : g_out_rows) n += kv.second;
+    return n;
+}
+
+// 16-byte chunks of K written by appends so far, and how many were written twice
+int64_t hostcheck_appended_chunks() { return (int64_t)g_appended.size(); }
+int64_t hostcheck_appended_dupes() {
+    int64_t n = 0;
+    for (auto &kv : g_appended) n += kv.second > 1;
+    return n;
+}
+
+int32_t hostcheck_lens_dev(int b) { return (b >= 0 && b < (int)g_lens_dev.size()) ? g_lens_dev[b] : -1; }
+
+}  // extern "C"
+
+namespace gqakv {
+
+hipError_t launch_append(const AppendArgs &a, int n_blocks, hipStream_t) {
+    ++g_launches;
+    if ((int)g_lens_dev.size() < a.batch) g_lens_dev.resize(a.batch, 0);
+    for (int blk = 0; blk < n_blocks; ++blk) {
+        const int r = find_row(a.t.block0, a.t.n_rows, blk);
+        const int local = blk - a.t.block0[r];
+        const int nch = a.t.nchunk[r];
+        const int kvh = local / nch, chunk = local % nch;
+        const int b = a.t.b[r];
+        if (b < 0 || b >= a.batch || kvh < 0 || kvh >= a.hkv) err("append: block maps outside the cache");
+        const int64_t span = (int64_t)a.t.n[r] * a.row_bytes;
+        const int64_t head = (int64_t)b * a.hkv + kvh;
+        for (int tid = 0; tid < 256; ++tid) {
+            const int64_t off = (int64_t)chunk * kAppendChunk + tid * 16;
+            if (off >= span) continue;
+            const int64_t src = head * a.T * a.row_bytes + off;
+            const int64_t dst = (head * a.max_len + a.t.start[r]) * a.row_bytes + off;
+            access((const char *)a.k_new + src, 16, "k_new", "append read k_new");
+            access((const char *)a.v_new + src, 16, "v_new", "append read v_new");
+            access((const char *)a.k + dst, 16, "k", "append write K");
+            access((const char *)a.v + dst, 16, "v", "append write V");
+            const int64_t slot = dst / a.row_bytes - head * a.max_len;
+            if (slot < a.t.start[r] || slot >= a.t.start[r] + a.t.n[r] || slot >= a.max_len)
+                err("append: write outside the row's new slots");
+            g_appended[(uintptr_t)a.k + dst]++;
+        }
+        if (a.lens_dev != nullptr && local == 0) {
+            access(a.lens_dev + b, 4, "lens", "append lens_dev");
+            g_lens_dev[b] = a.t.start[r] + a.t.n[r];
+        }
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t) {
+    ++g_launches;
+    for (int i = 0; i < t.n_rows; ++i) {
+        access(lens_dev + t.b[i], 4, "lens", "set_lens");
+        if ((int)g_lens_dev.size() <= t.b[i]) g_lens_dev.resize(t.b[i] + 1, 0);
+        g_lens_dev[t.b[i]] = t.len[i];
+    }
+    return hipSuccess;
+}
+
+static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem) {
+    ++g_launches;
+    const AttnRows &R = a.rows;
+    const int D = a.head_dim;
+    const int64_t row_bytes = (int64_t)D * elem;
+    if (R.item0[R.n_rows] != R.total_items) err("item0 does not end at total_items");
+    for (int r = 0; r < R.n_rows; ++r) {
+        if (R.len[r] > a.max_len || R.nnew[r] > R.len[r] || R.nnew[r] <= 0 || R.nnew[r] > a.T)
+            err("attention: bad row table entry");
+        if (R.lsplit[r] % key_tile != 0 || R.nsplit[r] <= 0) err("attention: bad split");
+        if ((int64_t)R.nsplit[r] * R.lsplit[r] < R.len[r]) err("attention: splits do not cover the row");
+    }
+    for (int item = 0; item < R.total_items; ++item) {
+        const Item it = decode_item(R, item, a.hkv, a.group, cols);
+        const int r = find_row(R.item0, R.n_rows, item);
+        if (it.b < 0 || it.b >= a.batch || it.kvh < 0 || it.kvh >= a.hkv || it.qtile < 0 || it.qtile >= it.nq ||
+            it.split < 0 || it.split >= it.nsplit)
+            err("attention: item decodes outside the launch");
+        if (it.k_begin < 0 || it.k_end > R.len[r]) err("attention: key range outside the row");
+        const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
+        // keys read: [k_begin, k_end), loaded tile by tile with loads past k_end predicated off
+        if (it.k_begin < it.k_end) {
+            for (int key : {it.k_begin, it.k_end - 1}) {
+                access((const char *)a.k + (head * a.max_len + key) * row_bytes, row_bytes, "k", "attention K");
+                access((const char *)a.v + (head * a.max_len + key) * row_bytes, row_bytes, "v", "attention V");
+            }
+        }
+        for (int col = 0; col < cols; ++col) {
+            const int pos = column_position(it, col, a.group, cols);
+            if (pos < 0) continue;
+            const int t = column_t(it, col, a.group), h = column_head(it, col, a.group);
+            if (t < 0 || t >= a.T || t >= R.nnew[r] || h < 0 || h >= a.hq) err("attention: column outside q");
+            if (pos != R.len[r] - R.nnew[r] + t) err("attention: wrong absolute position");
+            const int64_t qrow = ((int64_t)it.b * a.hq + h) * a.T + t;
+            access((const char *)a.q + qrow * row_bytes, row_bytes, "q", "attention q");
+            if (it.rec0 < 0) {
+                const char *o = (const char *)a.out + qrow * row_bytes;
+                access(o, row_bytes, "out", "attention out");
+                g_out_rows[(uintptr_t)o]++;
+            } else {
+                const int64_t rec = (int64_t)it.rec0 + col;
+                if (rec < 0 || rec >= a.records) err("attention: partial record out of range");
+                access(a.ws_acc + rec * D, D * 4, "ws", "attention partial acc");
+                access(a.ws_ml + rec * 2, 8, "ws", "attention partial m,l");
+                g_records[rec]++;
+            }
+        }
+    }
+}
+
+hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t) {
+    if (head_dim != a.head_dim) err("decode: head_dim mismatch");
+    sim_attention(a, 16 * nsub, kDecodeKeyTile, dtype == 0 ? 4 : 2);
+    return hipSuccess;
+}
+
+hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t) {
+    if (head_dim != a.head_dim) err("prefill: head_dim mismatch");
+    sim_attention(a, kPrefillCols, kPrefillKeyTile, dtype == 0 ? 4 : 2);
+    return hipSuccess;
+}
+
+hipError_t launch_finalize(int dtype, int head_dim, const FinalArgs &a, hipStream_t) {
+    ++g_launches;
+    const int elem = dtype == 0 ? 4 : 2;
+    const int64_t row_bytes = (int64_t)head_dim * elem;
+    for (int r = 0; r < a.rows.n_rows; ++r) {
+        for (int h = 0; h < a.hq; ++h) {
+            const int b = a.rows.b[r];
+            for (int t = 0; t < a.T; ++t) {
+                const char *o = (const char *)a.out + (((int64_t)b * a.hq + h) * a.T + t) * row_bytes;
+                if (t >= a.rows.nnew[r]) {
+                    access(o, row_bytes, "out", "finalize zero fill");
+                    g_out_rows[(uintptr_t)o]++;
+                    continue;
+                }
+                if (a.rows.nsplit[r] == 0) continue;
+                const int64_t rec = final_record(a.rows, r, h, t, a.group);
+                for (int s = 0; s < a.rows.nsplit[r]; ++s) {
+                    const int64_t rs = rec + (int64_t)s * a.rows.cols[r];
+                    if (rs < 0 || rs >= a.records) err("finalize: record out of range");
+                    auto w = g_records.find(rs);
+                    if (w == g_records.end() || w->second != 1) err("finalize: record not written exactly once");
+                    access(a.ws_acc + rs * head_dim, head_dim * 4, "ws", "finalize acc");
+                    access(a.ws_ml + rs * 2, 8, "ws", "finalize m,l");
+                }
+                access(o, row_bytes, "out", "finalize out");
+                g_out_rows[(uintptr_t)o]++;
+            }
+        }
+    }
+    return hipSuccess;
+}
+
+}  // namespace gqakv

@@ -1,0 +1,160 @@
+"""GPU parity at the full Llama-3.1-8B-shaped workloads (one layer, Hq=32, Hkv=8,
+d=128, bfloat16), in the launch configuration the benchmark times.
+
+The oracle recomputes sampled outputs one by one from the same seeded bits
+(each row's history is regenerated on the host); properties that hold at any
+size are checked on the whole output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import direct
+import workloads as W
+from gpu_util import assert_close, from_dev, out_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return KVCache, gqa_attention
+
+
+def fill_rows(cache, shape, seed, lens, chunk=2048):
+    """Append each row's seeded history (prefix_kv) until row b holds lens[b] tokens."""
+    lens = np.asarray(lens)
+    B, hk, d = shape.batch, shape.kv_heads, shape.head_dim
+    start = 0
+    while start < lens.max():
+        n = np.clip(lens - start, 0, chunk)
+        T = int(n.max())
+        k = np.zeros((B, hk, T, d), W.storage_np_dtype(shape.dtype))
+        v = np.zeros_like(k)
+        for b in range(B):
+            if n[b] > 0:
+                k[b, :, :n[b]], v[b, :, :n[b]] = W.prefix_kv(shape, seed, b, start, int(n[b]))
+        cache.append(to_dev(k, shape.dtype), to_dev(v, shape.dtype), n.tolist())
+        start += chunk
+
+
+def row_history(shape, seed, b, length, extra_k=None, extra_v=None):
+    k, v = W.prefix_kv(shape, seed, b, 0, length)
+    if extra_k is not None:
+        k = np.concatenate([k, extra_k], axis=1)
+        v = np.concatenate([v, extra_v], axis=1)
+    return k, v
+
+
+def test_zero_output_fails_the_gate():
+    """Negative control: at these magnitudes max-abs 2e-2 alone would pass zeros."""
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal((4, 128)) * 1.4e-3
+    with pytest.raises(AssertionError):
+        assert_close(np.zeros_like(ref), ref, "bf16", "zeros")
+
+
+def test_llama_decode_b32_s4096():
+    KVCache, gqa_attention = _lib()
+    sh, seed = W.LLAMA8B_DECODE, 1
+    cache = KVCache(sh.batch, sh.kv_heads, sh.max_len, sh.head_dim)
+    fill_rows(cache, sh, seed, [4096] * sh.batch)
+    n = [1] * sh.batch
+    q, k, v = W.step_inputs(sh, seed, 10_000, 1, n, pad="nan")
+    cache.append(to_dev(k, "bf16"), to_dev(v, "bf16"), n)
+    out = gqa_attention(to_dev(q, "bf16"), cache, n)
+    got = out_f64(out, "bf16")
+    assert np.isfinite(got).all()
+    for b in [0, 13, 31]:
+        kr, vr = row_history(sh, seed, b, 4096, k[b, :, :1], v[b, :, :1])
+        ref = direct.attention_row(kr, vr, 4097, 1, q[b], "bf16", [(h, 0) for h in range(sh.q_heads)])
+        assert_close(got[b], ref, "bf16", f"decode row {b}")
+    # any size: each output is a convex combination of V rows of its KV head
+    vmax = float(np.abs(W.bf16_bits_to_f32(v)).max())
+    assert np.abs(got).max() <= max(vmax, 1.0)
+    # roll back and repeat: identical bits (stale token overwritten in place)
+    cache.truncate([4096] * sh.batch)
+    cache.append(to_dev(k, "bf16"), to_dev(v, "bf16"), n)
+    out2 = gqa_attention(to_dev(q, "bf16"), cache, n)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_llama_verify_b16_t4():
+    KVCache, gqa_attention = _lib()
+    sh, seed = W.LLAMA8B_VERIFY, 2
+    cache = KVCache(sh.batch, sh.kv_heads, sh.max_len, sh.head_dim)
+    fill_rows(cache, sh, seed, [4092] * sh.batch)
+    n = [4] * sh.batch
+    q, k, v = W.step_inputs(sh, seed, 10_000, 4, n, pad="nan")
+    cache.append(to_dev(k, "bf16"), to_dev(v, "bf16"), n)
+    got = out_f64(gqa_attention(to_dev(q, "bf16"), cache, n), "bf16")
+    for b in [0, 9, 15]:
+        kr, vr = row_history(sh, seed, b, 4092, k[b], v[b])
+        ref = direct.attention_row(kr, vr, 4096, 4, q[b], "bf16",
+                                   [(h, t) for h in range(sh.q_heads) for t in range(4)])
+        assert_close(got[b], ref, "bf16", f"verify row {b}")
+
+
+def test_llama_chunked_prefill_10240x512():
+    KVCache, gqa_attention = _lib()
+    sh, seed = W.LLAMA8B_CHUNKED_PREFILL, 3
+    cache = KVCache(sh.batch, sh.kv_heads, sh.max_len, sh.head_dim)
+    n = [512] * sh.batch
+    hist_k, hist_v = [], []
+    check = {0: None, 1: None, 10: None, 19: None}
+    rng = np.random.default_rng(5)
+    for c in range(20):
+        q, k, v = W.step_inputs(sh, seed, c, 512, n, pad="normal")
+        hist_k.append(k)
+        hist_v.append(v)
+        cache.append(to_dev(k, "bf16"), to_dev(v, "bf16"), n)
+        out = gqa_attention(to_dev(q, "bf16"), cache, n)
+        if c in check:
+            got = out_f64(out, "bf16")
+            assert np.isfinite(got).all()
+            L = 512 * (c + 1)
+            ts = sorted({0, 1, 63, 64, 255, 511, *rng.integers(0, 512, 4).tolist()})
+            for b in [0, 3]:
+                kr = np.concatenate([hk[b] for hk in hist_k], axis=1)
+                vr = np.concatenate([hv[b] for hv in hist_v], axis=1)
+                pairs = [(h, t) for h in (0, 5, 17, 31) for t in ts]
+                ref = direct.attention_row(kr, vr, L, 512, q[b], "bf16", pairs)
+                for h, t in pairs:
+                    assert_close(got[b, h, t], ref[h, t], "bf16", f"chunk {c} row {b} head {h} t {t}")
+    assert cache.lens == [10240] * sh.batch
+
+
+@pytest.mark.parametrize("seed", [4])
+def test_llama_ragged_b64(seed):
+    KVCache, gqa_attention = _lib()
+    sh = W.LLAMA8B_RAGGED
+    lens, n_new = W.ragged_rows(seed)
+    cache = KVCache(sh.batch, sh.kv_heads, sh.max_len, sh.head_dim)
+    fill_rows(cache, sh, seed, lens)
+    q, k, v = W.step_inputs(sh, seed, 10_000, 256, n_new, pad="nan")
+    cache.append(to_dev(k, "bf16"), to_dev(v, "bf16"), n_new.tolist())
+    out = gqa_attention(to_dev(q, "bf16"), cache, n_new.tolist())
+    raw = from_dev(out, "bf16")
+    got = out_f64(out, "bf16")
+    assert np.isfinite(got).all()
+    for b in range(sh.batch):
+        assert not raw[b, :, n_new[b]:].view(np.uint8).any(), f"row {b}: padding not +0.0"
+    # one row of each class, plus the longest row
+    picks = []
+    for cls in (1, 4, 256):
+        idx = np.flatnonzero(n_new == cls)
+        if idx.size:
+            picks.append(int(idx[np.argmax(lens[idx])]))
+    picks.append(int(np.argmax(lens + (n_new > 0) * 10**6)))
+    rng = np.random.default_rng(6)
+    for b in sorted(set(picks)):
+        nb = int(n_new[b])
+        L = int(lens[b]) + nb
+        kr, vr = row_history(sh, seed, b, int(lens[b]), k[b, :, :nb], v[b, :, :nb])
+        ts = sorted({0, nb - 1, *rng.integers(0, nb, 3).tolist()})
+        pairs = [(h, t) for h in (0, 3, 30) for t in ts]
+        ref = direct.attention_row(kr, vr, L, nb, q[b], "bf16", pairs)
+        for h, t in pairs:
+            assert_close(got[b, h, t], ref[h, t], "bf16", f"ragged row {b} (len {L}, n_new {nb}) head {h} t {t}")

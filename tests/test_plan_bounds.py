@@ -1,0 +1,237 @@
+"""CPU replay of every launch the library plans, checked for bounds and coverage.
+
+The library's real host code (validation, lengths, work planning) is linked
+against a simulator of the kernel launchers (tests/hostcheck/launch_sim.cpp)
+that walks every block and column with the kernels' own indexing functions.
+Each workload below is run through append + attention on fake addresses, and
+the simulator must report no access outside a buffer, every output row written
+exactly once per call, every appended slot written once, and the device lengths
+equal to the host lengths.
+"""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gqa_attention_preallocated_amd", "csrc")
+
+
+@pytest.fixture(scope="session")
+def sim(tmp_path_factory):
+    out = tmp_path_factory.mktemp("hostcheck") / "libhostcheck.so"
+    cmd = ["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "abi.cpp"), os.path.join(ROOT, "tests", "hostcheck", "launch_sim.cpp"),
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    lib = ctypes.CDLL(str(out))
+    P, I32 = ctypes.c_void_p, ctypes.c_int32
+    I32P = ctypes.POINTER(ctypes.c_int32)
+    lib.kv_cache_create.argtypes = [I32, I32, I32, I32, ctypes.c_int, P, P, P, P, ctypes.POINTER(P)]
+    lib.kv_append.argtypes = [P, P, P, I32, I32P, P]
+    lib.gqa_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gqa_attention.argtypes = [P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
+    lib.kv_truncate.argtypes = [P, I32P, P]
+    lib.kv_cache_set_policy.argtypes = [P, I32, I32]
+    lib.kv_cache_destroy.argtypes = [P]
+    lib.kv_last_error.restype = ctypes.c_char_p
+    lib.hostcheck_region.argtypes = [ctypes.c_uint64, ctypes.c_size_t, ctypes.c_char_p]
+    lib.hostcheck_error.restype = ctypes.c_char_p
+    lib.hostcheck_out_row_writes.argtypes = [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int64]
+    lib.hostcheck_out_rows_total.restype = ctypes.c_int64
+    lib.hostcheck_appended_chunks.restype = ctypes.c_int64
+    lib.hostcheck_appended_dupes.restype = ctypes.c_int64
+    lib.hostcheck_launches.restype = ctypes.c_int64
+    return lib
+
+
+def _i32(vals):
+    vals = [int(x) for x in vals]
+    return (ctypes.c_int32 * max(1, len(vals)))(*vals)
+
+
+class SimCache:
+    """A cache on fake, non-overlapping addresses inside the simulator."""
+
+    GAP = 1 << 44
+
+    def __init__(self, lib, B, hk, max_len, d, dtype, hq, t_max):
+        self.lib, self.B, self.hk, self.max_len, self.d, self.hq = lib, B, hk, max_len, d, hq
+        self.elem = 4 if dtype == "f32" else 2
+        lib.hostcheck_reset()
+        self.addr = {}
+        sizes = {
+            "k": B * hk * max_len * d * self.elem, "v": B * hk * max_len * d * self.elem,
+            "lens": 4 * max(B, 1),
+            "k_new": B * hk * t_max * d * self.elem, "v_new": B * hk * t_max * d * self.elem,
+            "q": B * hq * t_max * d * self.elem, "out": B * hq * t_max * d * self.elem,
+            "ws": 1 << 34,
+        }
+        for i, (name, size) in enumerate(sizes.items()):
+            base = (i + 1) * self.GAP
+            self.addr[name] = base
+            lib.hostcheck_region(base, max(size, 1), name.encode())
+        h = ctypes.c_void_p()
+        st = lib.kv_cache_create(B, hk, max_len, d, 0 if dtype == "f32" else 1, ctypes.c_void_p(self.addr["k"]),
+                                 ctypes.c_void_p(self.addr["v"]), ctypes.c_void_p(self.addr["lens"]), None,
+                                 ctypes.byref(h))
+        assert st == 0, lib.kv_last_error()
+        self.h = h
+        self.lens = np.zeros(B, np.int64)
+        self.appended = 0
+        self.rewrote = False     # set after a rollback: slots get written again
+
+    def append(self, T, n_new):
+        st = self.lib.kv_append(self.h, ctypes.c_void_p(self.addr["k_new"]), ctypes.c_void_p(self.addr["v_new"]),
+                                T, _i32(n_new), None)
+        assert st == 0, self.lib.kv_last_error()
+        self.lens += np.asarray(n_new)
+        self.appended += int(np.sum(n_new)) * self.hk * self.d * self.elem // 16
+
+    def attention(self, T, n_new):
+        size = ctypes.c_size_t()
+        assert self.lib.gqa_attention_workspace_size(self.h, self.hq, T, _i32(n_new), ctypes.byref(size)) == 0
+        assert size.value < (1 << 34)
+        self.lib.hostcheck_begin_call()
+        st = self.lib.gqa_attention(self.h, ctypes.c_void_p(self.addr["q"]), self.hq, T, _i32(n_new),
+                                    ctypes.c_void_p(self.addr["out"]), ctypes.c_void_p(self.addr["ws"]),
+                                    size.value, None)
+        assert st == 0, self.lib.kv_last_error()
+        return size.value
+
+    def check(self, T=None):
+        lib = self.lib
+        errs = [lib.hostcheck_error(i).decode() for i in range(lib.hostcheck_error_count())]
+        assert not errs, errs[:5]
+        if not self.rewrote:
+            assert lib.hostcheck_appended_dupes() == 0
+            assert lib.hostcheck_appended_chunks() == self.appended
+        for b in range(self.B):
+            assert lib.hostcheck_lens_dev(b) == self.lens[b]
+        if T is not None and self.B > 0 and T > 0:
+            rows = self.B * self.hq * T
+            row_bytes = self.d * self.elem
+            assert lib.hostcheck_out_rows_total() == rows
+            for i in range(rows):
+                assert lib.hostcheck_out_row_writes(self.addr["out"], i, row_bytes) == 1, i
+
+
+def _run(sim, B, hk, G, d, max_len, dtype, calls, policy=(0, 0)):
+    t_max = max([c["T"] for c in calls] + [1])
+    c = SimCache(sim, B, hk, max_len, d, dtype, hk * G, t_max)
+    sim.kv_cache_set_policy(c.h, policy[0], policy[1])
+    for call in calls:
+        c.append(call["T"], call["n_new"])
+        c.attention(call["T"], call["n_new"])
+        c.check(call["T"])
+    return c
+
+
+@pytest.mark.parametrize("policy", [(0, 0), (1, 0), (2, 0), (1, 32), (2, 64)])
+def test_tiny_schedule(sim, policy):
+    sh = W.TINY_FP32
+    _run(sim, sh.batch, sh.kv_heads, sh.group, sh.head_dim, sh.max_len, "f32", W.tiny_schedule(0), policy)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_trials(sim, seed):
+    shape, calls = W.trial_spec(seed, head_dims=(16, 32, 64, 128))
+    for policy in [(0, 0), (1, 32), (2, 64)]:
+        _run(sim, shape.batch, shape.kv_heads, shape.group, shape.head_dim, shape.max_len,
+             "bf16" if seed % 2 else "f32", calls, policy)
+
+
+def _prefix_calls(lens, chunk=4096):
+    """Appends that bring every row to lens[b] (chunks of at most `chunk`)."""
+    lens = np.asarray(lens)
+    done = np.zeros_like(lens)
+    calls = []
+    while (done < lens).any():
+        n = np.minimum(lens - done, chunk)
+        calls.append({"T": int(n.max()), "n_new": n.tolist()})
+        done += n
+    return calls
+
+
+def _setup(sim, shape, lens, t_max):
+    c = SimCache(sim, shape.batch, shape.kv_heads, shape.max_len, shape.head_dim, shape.dtype,
+                 shape.q_heads, max(t_max, 4096))
+    for call in _prefix_calls(lens):
+        c.append(call["T"], call["n_new"])
+    return c
+
+
+def test_llama_decode(sim):
+    sh = W.LLAMA8B_DECODE
+    c = _setup(sim, sh, [4096] * sh.batch, 1)
+    for _ in range(2):
+        c.append(1, [1] * sh.batch)
+        ws = c.attention(1, [1] * sh.batch)
+        c.check(1)
+        sim.kv_truncate(c.h, _i32([4096] * sh.batch), None)
+        c.lens[:] = 4096
+        c.rewrote = True
+        c.check()
+    assert ws > 0
+
+
+def test_llama_verify(sim):
+    sh = W.LLAMA8B_VERIFY
+    c = _setup(sim, sh, [4092] * sh.batch, 4)
+    c.append(4, [4] * sh.batch)
+    c.attention(4, [4] * sh.batch)
+    c.check(4)
+
+
+def test_llama_chunked_prefill(sim):
+    sh = W.LLAMA8B_CHUNKED_PREFILL
+    c = SimCache(sim, sh.batch, sh.kv_heads, sh.max_len, sh.head_dim, "bf16", sh.q_heads, 512)
+    for chunk in range(20):
+        c.append(512, [512] * sh.batch)
+        c.attention(512, [512] * sh.batch)
+        c.check(512)
+    assert c.lens.tolist() == [10240] * sh.batch
+
+
+@pytest.mark.parametrize("seed", [4, 5, 6])
+def test_llama_ragged(sim, seed):
+    sh = W.LLAMA8B_RAGGED
+    lens, n_new = W.ragged_rows(seed)
+    c = _setup(sim, sh, lens, 256)
+    c.append(256, n_new)
+    c.attention(256, n_new)
+    c.check(256)
+
+
+def test_more_rows_than_one_launch_table(sim):
+    B = 150
+    rng = np.random.default_rng(0)
+    lens = rng.integers(1, 300, B)
+    c = SimCache(sim, B, 2, 512, 64, "bf16", 8, 300)
+    for call in _prefix_calls(lens, 128):
+        c.append(call["T"], call["n_new"])
+    n_new = rng.choice([0, 1, 3, 40], B)
+    n_new = np.minimum(n_new, c.lens)
+    c.attention(40, n_new)
+    c.check(40)
+    sim.kv_truncate(c.h, _i32(c.lens // 2), None)
+    c.lens = c.lens // 2
+    c.rewrote = True
+    c.check()
+
+
+def test_mqa_and_mha_shapes(sim):
+    for hk, G in [(1, 32), (1, 64), (1, 128), (8, 1), (2, 3)]:
+        c = SimCache(sim, 2, hk, 256, 128, "bf16", hk * G, 64)
+        c.append(64, [64, 30])
+        c.attention(64, [64, 30])
+        c.check(64)
+        c.append(3, [1, 3])
+        c.attention(3, [1, 3])
+        c.check(3)
