@@ -53,10 +53,12 @@ class KVCache:
 
     ``k`` and ``v`` are the preallocated buffers themselves (their data
     pointers never change); ``lens`` is the host copy of the per-row lengths and
-    ``lens_dev`` the device copy the library keeps in stream order.
+    ``lens_dev`` the device copy the library keeps in stream order (None with
+    ``device_lens=False``: then a rollback is host-only bookkeeping).
     """
 
-    def __init__(self, batch, kv_heads, max_len, head_dim, dtype=torch.bfloat16, device="cuda"):
+    def __init__(self, batch, kv_heads, max_len, head_dim, dtype=torch.bfloat16, device="cuda",
+                 device_lens=True):
         if dtype not in _DTYPES:
             raise ValueError(f"dtype {dtype} not supported (float32 or bfloat16)")
         self._lib = _lib.load()
@@ -66,7 +68,7 @@ class KVCache:
         shape = (batch, kv_heads, max_len, head_dim)
         self.k = torch.zeros(shape, dtype=dtype, device=device)
         self.v = torch.zeros(shape, dtype=dtype, device=device)
-        self.lens_dev = torch.zeros(max(batch, 1), dtype=torch.int32, device=device)
+        self.lens_dev = torch.zeros(max(batch, 1), dtype=torch.int32, device=device) if device_lens else None
         self.dtype = dtype
         self.batch, self.kv_heads, self.max_len, self.head_dim = shape
         self._ws = None
@@ -75,7 +77,7 @@ class KVCache:
             st = self._lib.kv_cache_create(batch, kv_heads, max_len, head_dim, _DTYPES[dtype],
                                            ctypes.c_void_p(self.k.data_ptr()),
                                            ctypes.c_void_p(self.v.data_ptr()),
-                                           ctypes.c_void_p(self.lens_dev.data_ptr()),
+                                           ctypes.c_void_p(self.lens_dev.data_ptr() if device_lens else 0),
                                            _stream_ptr(), ctypes.byref(h))
         _lib.check(st, self._lib)
         self._h = h
@@ -154,7 +156,8 @@ class KVCache:
         if nbytes == 0:
             return None
         if self._ws is None or self._ws.numel() < nbytes:
-            self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            # zero-filled once: the split-combine counters then start from a known state
+            self._ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
         return self._ws
 
 

@@ -80,12 +80,12 @@ struct Plan {
     std::vector<RowPlan> dec, pre;     // rows per kernel
     std::vector<int32_t> zero_rows;    // rows with no new tokens (all slots zero)
     int64_t records = 0;               // partial records (d + 2 floats each)
-    bool need_final = false;
+    std::vector<int32_t> pad_rows;     // rows with padded slots (n_new < T), zero-filled
 };
 
-// Target number of decode work items (one wave each) for a full chip: enough
-// to keep several waves per SIMD streaming K/V.
-constexpr int64_t kDecodeWaveTarget = 4096;
+// Decode work groups (kDecodeWaves waves each) the chip runs at once: one per
+// CU. Rows are split across work groups only as far as needed to fill them.
+constexpr int64_t kDecodeSlots = 256;
 // Prefill work-group slots on the chip (256 CUs x 2 resident work groups).
 constexpr int64_t kPrefillSlots = 512;
 
@@ -116,15 +116,16 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
     p.nsub = need <= 16 ? 1 : (need <= 32 ? 2 : 4);
     p.dec_cols = 16 * p.nsub;
 
-    // ---- decode rows: split keys so the launch has about kDecodeWaveTarget waves
+    // ---- decode rows: a work group streams at least kDecodeWaves tiles per
+    //      split; keep splitting the longest rows while the chip is not full
     {
         const int tq = p.dec_cols / G;
-        int64_t units = 0;
-        for (int b : dec_rows) {
-            const int nq = (int)ceil_div(n_new[b], tq);
-            units += (int64_t)c->kv_heads * nq * ceil_div(c->lens[b], kDecodeKeyTile);
-        }
-        int64_t tps = std::max<int64_t>(4, ceil_div(units, kDecodeWaveTarget));   // tiles per split
+        int64_t total = 0;
+        for (int b : dec_rows)
+            total += (int64_t)c->kv_heads * ceil_div(n_new[b], tq) * ceil_div(c->lens[b], kDecodeKeyTile);
+        // tiles per work group: the whole job spread over the slots, never
+        // fewer than one tile per wave
+        const int64_t tpw = std::max<int64_t>(kDecodeWaves, ceil_div(total, kDecodeSlots));
         for (int b : dec_rows) {
             RowPlan r{};
             r.b = b;
@@ -136,7 +137,7 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
                 r.lsplit = (int)(ceil_div(c->keys_per_split, kDecodeKeyTile) * kDecodeKeyTile);
                 r.nsplit = (int)ceil_div(r.len, r.lsplit);
             } else {
-                r.nsplit = (int)ceil_div(tiles, tps);
+                r.nsplit = (int)ceil_div(tiles, tpw);
                 r.lsplit = (int)(ceil_div(tiles, r.nsplit) * kDecodeKeyTile);
             }
             r.work = tiles * r.nq;
@@ -181,36 +182,39 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
     std::stable_sort(p.dec.begin(), p.dec.end(), heavier);
     std::stable_sort(p.pre.begin(), p.pre.end(), heavier);
 
-    // ---- partial records for split rows
+    // ---- partial records for rows split across work groups
     p.records = 0;
-    for (auto &r : p.dec) {
+    auto assign = [&](RowPlan &r, int cols) {
         if (r.nsplit > 1) {
             r.pbase = p.records;
-            p.records += (int64_t)c->kv_heads * r.nq * r.nsplit * p.dec_cols;
+            p.records += (int64_t)c->kv_heads * r.nq * r.nsplit * cols;
         } else {
             r.pbase = -1;
         }
-    }
-    for (auto &r : p.pre) {
-        if (r.nsplit > 1) {
-            r.pbase = p.records;
-            p.records += (int64_t)c->kv_heads * r.nq * r.nsplit * kPrefillCols;
-        } else {
-            r.pbase = -1;
-        }
-    }
-    p.need_final = !p.zero_rows.empty();
-    for (auto &r : p.dec) p.need_final |= (r.nsplit > 1) || (r.nnew < T);
-    for (auto &r : p.pre) p.need_final |= (r.nsplit > 1) || (r.nnew < T);
+    };
+    for (auto &r : p.dec) assign(r, p.dec_cols);
+    for (auto &r : p.pre) assign(r, kPrefillCols);
+    for (int b = 0; b < c->batch; ++b)
+        if (n_new[b] < T) p.pad_rows.push_back(b);
 }
 
-size_t workspace_bytes_for(const kv_cache *c, const Plan &p) {
-    if (p.records == 0) return 0;
-    // acc region then (m, l) region, each 256-byte aligned
-    size_t acc = (size_t)p.records * c->head_dim * sizeof(float);
-    acc = (acc + 255) & ~(size_t)255;
-    return acc + (size_t)p.records * 2 * sizeof(float);
+// workspace: [partial acc: records x d floats][partial (m, l): records x 2 floats],
+// the second region 256-byte aligned
+struct WsLayout {
+    size_t acc = 0, ml = 0, total = 0;
+};
+
+WsLayout ws_layout(const kv_cache *c, const Plan &p) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    WsLayout w;
+    if (p.records == 0) return w;
+    w.acc = 0;
+    w.ml = up((size_t)p.records * c->head_dim * sizeof(float));
+    w.total = w.ml + (size_t)p.records * 2 * sizeof(float);
+    return w;
 }
+
+size_t workspace_bytes_for(const kv_cache *c, const Plan &p) { return ws_layout(c, p).total; }
 
 kv_status check_attention_args(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new) {
     if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
@@ -390,20 +394,39 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
     const size_t need = workspace_bytes_for(c, p);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
-    if (p.records > INT32_MAX / 2) return fail(KV_ERR_UNSUPPORTED, "too many split partials");
+    if (p.records > INT32_MAX / 2)
+        return fail(KV_ERR_UNSUPPORTED, "too many split partials");
 
     hipStream_t st = (hipStream_t)stream;
-    float *ws_acc = (float *)workspace;
-    size_t acc_bytes = ((size_t)p.records * c->head_dim * sizeof(float) + 255) & ~(size_t)255;
-    float *ws_ml = need > 0 ? (float *)((char *)workspace + acc_bytes) : nullptr;
+    const WsLayout w = ws_layout(c, p);
+    char *ws = (char *)workspace;
+
+    // padded slots first: independent of the attention kernels
+    for (size_t lo = 0; lo < p.pad_rows.size(); lo += kMaxRows) {
+        ZeroArgs z{};
+        z.out = out;
+        z.batch = c->batch;
+        z.T = T;
+        z.hq = q_heads;
+        z.head_dim = c->head_dim;
+        z.row_bytes = (int64_t)c->head_dim * c->elem_bytes;
+        const size_t hi = std::min(p.pad_rows.size(), lo + kMaxRows);
+        z.rows.n_rows = (int32_t)(hi - lo);
+        for (size_t i = lo; i < hi; ++i) {
+            z.rows.b[i - lo] = p.pad_rows[i];
+            z.rows.nnew[i - lo] = n_new[p.pad_rows[i]];
+        }
+        hipError_t e = launch_zero_fill(z, st);
+        if (e != hipSuccess) return device_fail(e, "gqa_attention (zero fill)");
+    }
 
     AttnArgs a{};
     a.q = q;
     a.out = out;
     a.k = c->k;
     a.v = c->v;
-    a.ws_acc = ws_acc;
-    a.ws_ml = ws_ml;
+    a.ws_acc = w.total ? (float *)(ws + w.acc) : nullptr;
+    a.ws_ml = w.total ? (float *)(ws + w.ml) : nullptr;
     a.batch = c->batch;
     a.T = T;
     a.hq = q_heads;
@@ -424,43 +447,42 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
         hipError_t e = launch_decode((int)c->dtype, c->head_dim, p.nsub, a, st);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (decode kernel)");
     }
-    if (p.need_final) {
-        // rows needing a combine or zero slots
-        std::vector<std::array<int32_t, 5>> fr;   // b, nnew, nsplit, pbase, cols
-        for (int b : p.zero_rows) fr.push_back({b, 0, 0, 0, 0});
-        for (auto &r : p.dec)
-            if (r.nsplit > 1 || r.nnew < T)
-                fr.push_back({r.b, r.nnew, r.nsplit > 1 ? r.nsplit : 0, (int32_t)std::max<int64_t>(r.pbase, 0),
-                              p.dec_cols});
-        for (auto &r : p.pre)
-            if (r.nsplit > 1 || r.nnew < T)
-                fr.push_back({r.b, r.nnew, r.nsplit > 1 ? r.nsplit : 0, (int32_t)std::max<int64_t>(r.pbase, 0),
-                              kPrefillCols});
-        for (size_t lo = 0; lo < fr.size(); lo += kMaxRows) {
-            FinalArgs f{};
-            f.out = out;
-            f.ws_acc = ws_acc;
-            f.ws_ml = ws_ml;
-            f.batch = c->batch;
-            f.T = T;
-            f.hq = q_heads;
-            f.hkv = c->kv_heads;
-            f.group = p.group;
-            f.head_dim = c->head_dim;
-            f.records = p.records;
-            const size_t hi = std::min(fr.size(), lo + kMaxRows);
-            f.rows.n_rows = (int32_t)(hi - lo);
-            for (size_t i = lo; i < hi; ++i) {
-                const int j = (int)(i - lo);
-                f.rows.b[j] = fr[i][0];
-                f.rows.nnew[j] = fr[i][1];
-                f.rows.nsplit[j] = fr[i][2];
-                f.rows.pbase[j] = fr[i][3];
-                f.rows.cols[j] = fr[i][4];
-            }
-            hipError_t e = launch_finalize((int)c->dtype, c->head_dim, f, st);
-            if (e != hipSuccess) return device_fail(e, "gqa_attention (finalize kernel)");
+    // rows split across work groups: merge their partials
+    std::vector<std::pair<const RowPlan *, int>> split_rows;
+    for (auto &r : p.pre)
+        if (r.nsplit > 1) split_rows.push_back({&r, kPrefillCols});
+    for (auto &r : p.dec)
+        if (r.nsplit > 1) split_rows.push_back({&r, p.dec_cols});
+    for (size_t lo = 0; lo < split_rows.size(); lo += kMaxRows) {
+        CombineArgs m{};
+        m.out = out;
+        m.ws_acc = a.ws_acc;
+        m.ws_ml = a.ws_ml;
+        m.batch = c->batch;
+        m.T = T;
+        m.hq = q_heads;
+        m.hkv = c->kv_heads;
+        m.group = p.group;
+        m.head_dim = c->head_dim;
+        m.records = p.records;
+        const size_t hi = std::min(split_rows.size(), lo + kMaxRows);
+        m.rows.n_rows = (int32_t)(hi - lo);
+        int32_t blocks = 0;
+        for (size_t i = lo; i < hi; ++i) {
+            const RowPlan &r = *split_rows[i].first;
+            const int j = (int)(i - lo);
+            m.rows.b[j] = r.b;
+            m.rows.nnew[j] = r.nnew;
+            m.rows.nsplit[j] = r.nsplit;
+            m.rows.pbase[j] = (int32_t)r.pbase;
+            m.rows.cols[j] = split_rows[i].second;
+            m.rows.blk0[j] = blocks;
+            blocks += c->kv_heads * r.nq;
         }
+        m.rows.blk0[m.rows.n_rows] = blocks;
+        m.rows.total_blocks = blocks;
+        hipError_t e = launch_combine((int)c->dtype, c->head_dim, m, st);
+        if (e != hipSuccess) return device_fail(e, "gqa_attention (combine kernel)");
     }
     return ok();
 }

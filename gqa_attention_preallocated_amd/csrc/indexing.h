@@ -75,15 +75,4 @@ GQAKV_HD inline int column_position(const Item &it, int col, int group, int cols
 GQAKV_HD inline int column_t(const Item &it, int col, int group) { return it.t0 + col / group; }
 GQAKV_HD inline int column_head(const Item &it, int col, int group) { return it.kvh * group + col % group; }
 
-// Partial record read by the finalize pass for output (row r, head h, query t), split s = 0.
-GQAKV_HD inline int64_t final_record(const FinalRows &F, int r, int h, int t, int group) {
-    const int cols = F.cols[r];
-    const int tq = cols / group;
-    const int nq = (F.nnew[r] + tq - 1) / tq;
-    const int kvh = h / group, g = h % group;
-    const int qtile = t / tq;
-    const int col = (t % tq) * group + g;
-    return F.pbase[r] + (int64_t)((kvh * nq + qtile) * F.nsplit[r]) * cols + col;
-}
-
 }  // namespace gqakv

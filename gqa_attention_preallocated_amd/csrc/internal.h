@@ -68,22 +68,39 @@ struct AttnArgs {
     AttnRows rows;
 };
 
-struct FinalRows {
+// Combine of rows split across work groups: one block per (row, kv head, query tile).
+struct CombineRows {
     int32_t n_rows;
+    int32_t total_blocks;
     int32_t b[kMaxRows];
     int32_t nnew[kMaxRows];
-    int32_t nsplit[kMaxRows];  // 0: nothing to combine (written directly, or no queries)
+    int32_t nsplit[kMaxRows];
     int32_t pbase[kMaxRows];
     int32_t cols[kMaxRows];    // columns per query tile of the kernel that wrote the partials
+    int32_t blk0[kMaxRows + 1];
 };
 
-struct FinalArgs {
+struct CombineArgs {
     void *out;
     const float *ws_acc;
     const float *ws_ml;
     int32_t batch, T, hq, hkv, group, head_dim;
     int64_t records;
-    FinalRows rows;
+    CombineRows rows;
+};
+
+// Zero fill of padded query slots: rows r get out[b, :, nnew[r]:T, :] = +0.0.
+struct ZeroRows {
+    int32_t n_rows;
+    int32_t b[kMaxRows];
+    int32_t nnew[kMaxRows];
+};
+
+struct ZeroArgs {
+    void *out;
+    int32_t batch, T, hq, head_dim;
+    int64_t row_bytes;         // d * element size
+    ZeroRows rows;
 };
 
 // element type codes match kv_dtype
@@ -92,9 +109,11 @@ hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t s)
 // nsub: 16-column subtiles per decode work item (1, 2 or 4)
 hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t s);
 hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t s);
-hipError_t launch_finalize(int dtype, int head_dim, const FinalArgs &a, hipStream_t s);
+hipError_t launch_combine(int dtype, int head_dim, const CombineArgs &a, hipStream_t s);
+hipError_t launch_zero_fill(const ZeroArgs &a, hipStream_t s);
 
 constexpr int kDecodeKeyTile = 32;
+constexpr int kDecodeWaves = 8;       // waves per decode work group (they split the keys)
 constexpr int kPrefillKeyTile = 64;
 constexpr int kPrefillCols = 128;
 constexpr int kAppendChunk = 4096;

@@ -36,6 +36,14 @@ typedef __bf16 bf16_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+// K and V are read once per call: non-temporal loads keep them from displacing
+// other lines and measured faster for streaming reads on MI355X
+__device__ inline uint4 load_stream(const void *p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 // ---------------------------------------------------------------------------
 // element traits: 8-element MFMA operands and the 16x16 product
@@ -49,6 +57,7 @@ template <> struct Op<bf16_t> {
     __device__ static inline vec gload(const bf16_t *p) {
         return __builtin_bit_cast(vec, *reinterpret_cast<const uint4 *>(p));
     }
+    __device__ static inline vec gload_stream(const bf16_t *p) { return __builtin_bit_cast(vec, load_stream(p)); }
     __device__ static inline vec lds_load(const unsigned char *p) {
         return __builtin_bit_cast(vec, *reinterpret_cast<const uint4 *>(p));
     }
@@ -81,6 +90,11 @@ template <> struct Op<float> {
     __device__ static inline vec gload(const float *p) {
         float4 a = reinterpret_cast<const float4 *>(p)[0];
         float4 b = reinterpret_cast<const float4 *>(p)[1];
+        return vec{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    }
+    __device__ static inline vec gload_stream(const float *p) {
+        const float4 a = __builtin_bit_cast(float4, load_stream(p));
+        const float4 b = __builtin_bit_cast(float4, load_stream(p + 4));
         return vec{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     }
     __device__ static inline vec lds_load(const unsigned char *p) {
@@ -177,12 +191,17 @@ struct ColState {
     float l;   // this lane's share of the running denominator
 };
 
+
 // ---------------------------------------------------------------------------
-// split-K decode / verify kernel: one wave per work item, 16*NSUB columns,
-// 32-key tiles streamed from HBM with the next tile in flight
+// split-K decode / verify kernel. One work group of W waves per work item
+// (row, kv head, query tile, key split) with 16*NSUB columns. The item's key
+// range is cut into W contiguous pieces, one per wave; each wave streams its
+// 32-key tiles from HBM (the next tile in flight while the current one is
+// computed), then the waves merge their partial results through LDS (reusing
+// the V staging space), so a split-free row needs no second pass.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int NSUB>
-__global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
+template <typename E, int D, int NSUB, int W>
+__global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     using O = Op<E>;
     using vec = typename O::vec;
     constexpr int KT = kDecodeKeyTile;            // 32 keys per tile
@@ -193,11 +212,23 @@ __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
     constexpr int RS = ROWB + 16;                 // padded LDS row: conflict-free transposed reads
     constexpr int CPK = ROWB / 16;                // 16-byte chunks per key row
     constexpr int VCH = (KT * CPK + 63) / 64;     // V chunks per lane per tile
-    __shared__ __attribute__((aligned(16))) unsigned char lds[KT * RS];
+    constexpr int STAGE = KT * RS;                // per-wave V staging bytes
+    constexpr int PSTR = D + 4;                   // floats per column in the merge area
+    constexpr int MERGE = W * 16 * PSTR * 4 + W * 16 * 2 * 4;
+    constexpr int LDS_BYTES = (W * STAGE > MERGE) ? W * STAGE : MERGE;
+    __shared__ __attribute__((aligned(16))) unsigned char lds_all[LDS_BYTES];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
+    unsigned char *lds = lds_all + wave * STAGE;
     const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, C);
+
+    // this wave's share of the item's keys (whole tiles)
+    const int tiles = (it.k_end - it.k_begin + KT - 1) / KT;
+    const int per_wave = (tiles + W - 1) / W;
+    const int w_begin = it.k_begin + wave * per_wave * KT;
+    const int w_end = imin(w_begin + per_wave * KT, it.k_end);
 
     // ---- columns: absolute positions and Q operands (B of S^T)
     int pos[NSUB];
@@ -243,36 +274,36 @@ __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int key = tile + ks * 16 + lr;
-            const bool ok = key < it.k_end;
+            const bool ok = key < w_end;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const int d0 = kc * 32 + lg * 8;
-                kop[ks][kc] = (ok && d0 < D) ? O::gload(kbase + (int64_t)key * D + d0) : O::zero();
+                kop[ks][kc] = (ok && d0 < D) ? O::gload_stream(kbase + (int64_t)key * D + d0) : O::zero();
             }
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int c = lane + 64 * i;
             const int key = c / CPK, part = c % CPK;
-            const bool ok = (c < KT * CPK) && (tile + key < it.k_end);
-            vreg[i] = ok ? *reinterpret_cast<const uint4 *>(
-                               reinterpret_cast<const unsigned char *>(vbase + (int64_t)(tile + key) * D) + part * 16)
+            const bool ok = (c < KT * CPK) && (tile + key < w_end);
+            vreg[i] = ok ? load_stream(reinterpret_cast<const unsigned char *>(vbase + (int64_t)(tile + key) * D) +
+                                       part * 16)
                          : make_uint4(0, 0, 0, 0);
         }
     };
 
-    if (it.k_begin < it.k_end) load_tile(it.k_begin);
+    if (w_begin < w_end) load_tile(w_begin);
     // smallest position among this item's real columns: tiles ending at or
     // before it need no mask ([MASK] "A strong answer", tile cases)
     const int pos_min = it.base + it.t0;
 
-    for (int tile = it.k_begin; tile < it.k_end; tile += KT) {
+    for (int tile = w_begin; tile < w_end; tile += KT) {
         vec kcur[2][KC];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) kcur[ks][kc] = kop[ks][kc];
-        // V tile into LDS (row-major, padded)
+        // V tile into this wave's LDS stage (row-major, padded)
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int c = lane + 64 * i;
@@ -281,7 +312,7 @@ __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
                 *reinterpret_cast<uint4 *>(lds + key * RS + part * 16) = vreg[i];
             }
         }
-        if (tile + KT < it.k_end) load_tile(tile + KT);
+        if (tile + KT < w_end) load_tile(tile + KT);
 
         // ---- S^T = K Q^T for the 32 keys
         f32x4 sc[NSUB][2];
@@ -295,9 +326,9 @@ __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
                 sc[s][ks] = c;
             }
 
-        // ---- mask (only tiles that straddle the diagonal or the split end),
+        // ---- mask (only tiles that straddle the diagonal or the range end),
         //      online softmax in log2 units
-        const bool need_mask = (tile + KT > it.k_end) || (tile + KT - 1 > pos_min);
+        const bool need_mask = (tile + KT > w_end) || (tile + KT - 1 > pos_min);
         f32x8 p[NSUB];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
@@ -308,7 +339,7 @@ __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
                 v[j] = sc[s][ks][i] * a.scale_log2;
                 if (need_mask) {
                     const int key = tile + ks * 16 + lg * 4 + i;
-                    if (key >= it.k_end || key > pos[s]) v[j] = -INFINITY;
+                    if (key >= w_end || key > pos[s]) v[j] = -INFINITY;
                 }
             }
             float tmax = v[0];
@@ -333,7 +364,8 @@ __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
             }
         }
 
-        __syncthreads();   // V tile visible in LDS
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's V stores have landed
+        __builtin_amdgcn_wave_barrier();
 
         // ---- O^T += V^T P^T
 #pragma unroll
@@ -345,28 +377,50 @@ __global__ __launch_bounds__(64) void decode_kernel(AttnArgs a) {
 #pragma unroll
             for (int s = 0; s < NSUB; ++s) acc[s][nb] = O::mma(vt, O::from_f32(p[s]), acc[s][nb]);
         }
-        __syncthreads();   // LDS free for the next tile
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // V^T reads done before the stage is overwritten
+        __builtin_amdgcn_wave_barrier();
     }
 
-    // ---- write: direct (normalised, cast) or partial record
+    // ---- merge the W waves' partials in LDS, one 16-column subtile at a time
+    float *part = reinterpret_cast<float *>(lds_all);                 // [W][16][PSTR]
+    float *pml = part + W * 16 * PSTR;                                // [W][16][2]
+    constexpr int DC = D / 4;
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
         const float l = wave_sum_across_groups(st[s].l);
-        const int col = s * 16 + lr;
-        if (pos[s] < 0) continue;
-        if (it.rec0 < 0) {
-            E *op = column_out<E>(a, it, col, D);
-            const float inv = l > 0.f ? 1.f / l : 0.f;
+        __syncthreads();                       // stages (or the previous subtile) no longer read
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) O::store4(op + nb * 16 + lg * 4, acc[s][nb] * inv);
-        } else {
-            const int64_t rec = it.rec0 + col;
-            float *ap = a.ws_acc + rec * D;
+        for (int nb = 0; nb < NB; ++nb)
+            *reinterpret_cast<float4 *>(part + (wave * 16 + lr) * PSTR + nb * 16 + lg * 4) =
+                make_float4(acc[s][nb][0], acc[s][nb][1], acc[s][nb][2], acc[s][nb][3]);
+        if (lg == 0) *reinterpret_cast<float2 *>(pml + (wave * 16 + lr) * 2) = make_float2(st[s].m, l);
+        __syncthreads();
+        for (int task = tid; task < 16 * DC; task += 64 * W) {
+            const int c16 = task / DC, d = (task % DC) * 4;
+            const int col = s * 16 + c16;
+            if (column_position(it, col, a.group, C) < 0) continue;
+            float M = -INFINITY;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                *reinterpret_cast<float4 *>(ap + nb * 16 + lg * 4) =
-                    make_float4(acc[s][nb][0], acc[s][nb][1], acc[s][nb][2], acc[s][nb][3]);
-            if (lg == 0) *reinterpret_cast<float2 *>(a.ws_ml + rec * 2) = make_float2(st[s].m, l);
+            for (int w = 0; w < W; ++w) M = fmaxf(M, pml[(w * 16 + c16) * 2]);
+            const float m_use = (M == -INFINITY) ? 0.f : M;
+            f32x4 o = {0.f, 0.f, 0.f, 0.f};
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const float2 ml = *reinterpret_cast<const float2 *>(pml + (w * 16 + c16) * 2);
+                const float wt = exp2f(ml.x - m_use);      // a wave that saw no key: weight 0
+                const float4 x = *reinterpret_cast<const float4 *>(part + (w * 16 + c16) * PSTR + d);
+                o[0] += wt * x.x; o[1] += wt * x.y; o[2] += wt * x.z; o[3] += wt * x.w;
+                L += wt * ml.y;
+            }
+            if (it.rec0 < 0) {
+                E *op = column_out<E>(a, it, col, D) + d;
+                O::store4(op, o * (L > 0.f ? 1.f / L : 0.f));
+            } else {
+                const int64_t rec = it.rec0 + col;
+                *reinterpret_cast<float4 *>(a.ws_acc + rec * D + d) = make_float4(o[0], o[1], o[2], o[3]);
+                if (d == 0) *reinterpret_cast<float2 *>(a.ws_ml + rec * 2) = make_float2(M, L);
+            }
         }
     }
 }
@@ -457,8 +511,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
             const int key = c / CPK, part = c % CPK;
             const bool ok = (c < KT * CPK) && (tile + key < it.k_end);
             const int64_t goff = (int64_t)(tile + key) * ROWB + part * 16;
-            kreg[i] = ok ? *reinterpret_cast<const uint4 *>(kbase + goff) : make_uint4(0, 0, 0, 0);
-            vreg[i] = ok ? *reinterpret_cast<const uint4 *>(vbase + goff) : make_uint4(0, 0, 0, 0);
+            kreg[i] = ok ? load_stream(kbase + goff) : make_uint4(0, 0, 0, 0);
+            vreg[i] = ok ? load_stream(vbase + goff) : make_uint4(0, 0, 0, 0);
         }
     };
     auto store_tile = [&](int buf) {
@@ -575,47 +629,79 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// finalize: merge split partials by log-sum-exp in a fixed order, normalise,
-// cast; write +0.0 into every padded slot (t >= n_new) and every slot of a
-// row with no new tokens ([GQA] "A strong answer": zeros, never NaN)
+// zero fill: +0.0 into every padded slot t >= n_new[b] (and every slot of a
+// row with no new tokens). [GQA] "A strong answer": such rows give zeros,
+// never NaN. One block per (row, query head); 16-byte stores.
 // ---------------------------------------------------------------------------
-template <typename E, int D>
-__global__ __launch_bounds__(256) void finalize_kernel(FinalArgs a) {
-    using O = Op<E>;
-    constexpr int TPR = D / 4;              // threads per output row (4 elements each)
-    constexpr int RPP = 256 / TPR;          // rows per pass
+__global__ __launch_bounds__(256) void zero_fill_kernel(ZeroArgs a) {
     const int r = blockIdx.x / a.hq;
     const int h = blockIdx.x % a.hq;
     const int b = a.rows.b[r];
     const int n = a.rows.nnew[r];
-    const int nsplit = a.rows.nsplit[r];
-    const int cols = a.rows.cols[r];
-    const int d = (threadIdx.x % TPR) * 4;
-    E *out = reinterpret_cast<E *>(a.out) + ((int64_t)b * a.hq + h) * a.T * D;
-    for (int t = threadIdx.x / TPR; t < a.T; t += RPP) {
-        E *op = out + (int64_t)t * D + d;
-        if (t >= n) {
-            O::store4(op, f32x4{0.f, 0.f, 0.f, 0.f});
-            continue;
-        }
-        if (nsplit == 0) continue;    // written by the attention kernel
-        const int64_t rec = final_record(a.rows, r, h, t, a.group);
-        float mmax = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) mmax = fmaxf(mmax, a.ws_ml[(rec + (int64_t)s * cols) * 2]);
+    const int64_t head_off = ((int64_t)b * a.hq + h) * a.T * a.row_bytes;
+    const int64_t begin = head_off + (int64_t)n * a.row_bytes;
+    const int64_t end = head_off + (int64_t)a.T * a.row_bytes;
+    char *out = reinterpret_cast<char *>(a.out);
+    for (int64_t off = begin + threadIdx.x * 16; off < end; off += 256 * 16)
+        *reinterpret_cast<uint4 *>(out + off) = make_uint4(0, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// combine: for rows split across work groups, merge the nsplit partials of
+// every column by log-sum-exp in split order, normalise and cast. One block per
+// (row, kv head, query tile); loads of 8 splits are issued together.
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+    using O = Op<E>;
+    constexpr int DC = D / 4;
+    const int r = find_row(a.rows.blk0, a.rows.n_rows, blockIdx.x);
+    const int local = blockIdx.x - a.rows.blk0[r];
+    const int cols = a.rows.cols[r], nsplit = a.rows.nsplit[r], n = a.rows.nnew[r];
+    const int tq = cols / a.group;
+    const int nq = (n + tq - 1) / tq;
+    const int kvh = local / nq, qtile = local % nq;
+    const int b = a.rows.b[r];
+    const int64_t rec_first = a.rows.pbase[r] + (int64_t)((kvh * nq + qtile) * nsplit) * cols;
+    for (int task = threadIdx.x; task < cols * DC; task += 256) {
+        const int col = task / DC, d = (task % DC) * 4;
+        const int t = qtile * tq + col / a.group;
+        if (col >= tq * a.group || t >= n) continue;
+        const int h = kvh * a.group + col % a.group;
+        const int64_t rec = rec_first + col;
+        float M = -INFINITY, L = 0.f;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        float l = 0.f;
-        if (mmax != -INFINITY) {
-            for (int s = 0; s < nsplit; ++s) {
-                const int64_t rs = rec + (int64_t)s * cols;
-                const float2 ml = *reinterpret_cast<const float2 *>(a.ws_ml + rs * 2);
-                const float w = exp2f(ml.x - mmax);     // a split with no visible key has m = -inf: w = 0
-                const float4 x = *reinterpret_cast<const float4 *>(a.ws_acc + rs * D + d);
-                acc[0] += w * x.x; acc[1] += w * x.y; acc[2] += w * x.z; acc[3] += w * x.w;
-                l += w * ml.y;
+        for (int s0 = 0; s0 < nsplit; s0 += 8) {
+            float2 ml[8];
+            float4 x[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t rs = rec + (int64_t)(s0 + j) * cols;
+                if (s0 + j < nsplit) {
+                    ml[j] = *reinterpret_cast<const float2 *>(a.ws_ml + rs * 2);
+                    x[j] = *reinterpret_cast<const float4 *>(a.ws_acc + rs * D + d);
+                } else {
+                    ml[j] = make_float2(-INFINITY, 0.f);
+                    x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
             }
+            float bm = M;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bm = fmaxf(bm, ml[j].x);
+            if (bm == -INFINITY) continue;        // no split so far saw a key of this column
+            const float c = exp2f(M - bm);        // M = -inf: c = 0 (acc and L are still 0)
+            acc *= c;
+            L *= c;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float w = exp2f(ml[j].x - bm);   // a split that saw no key: w = 0
+                acc[0] += w * x[j].x; acc[1] += w * x[j].y; acc[2] += w * x[j].z; acc[3] += w * x[j].w;
+                L += w * ml[j].y;
+            }
+            M = bm;
         }
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        O::store4(op, acc * inv);
+        E *op = reinterpret_cast<E *>(a.out) + (((int64_t)b * a.hq + h) * a.T + t) * D + d;
+        O::store4(op, acc * (L > 0.f ? 1.f / L : 0.f));
     }
 }
 
@@ -636,11 +722,12 @@ hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t s)
 
 template <typename E, int D>
 static hipError_t decode_d(int nsub, const AttnArgs &a, hipStream_t s) {
-    const dim3 grid(a.rows.total_items), block(64);
+    constexpr int W = kDecodeWaves;
+    const dim3 grid(a.rows.total_items), block(64 * W);
     switch (nsub) {
-        case 1: hipLaunchKernelGGL((decode_kernel<E, D, 1>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<E, D, 2>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<E, D, 4>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<E, D, 1, W>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<E, D, 2, W>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<E, D, 4, W>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -681,21 +768,27 @@ hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_
 }
 
 template <typename E>
-static hipError_t finalize_e(int head_dim, const FinalArgs &a, hipStream_t s) {
-    const dim3 grid(a.rows.n_rows * a.hq), block(256);
+static hipError_t combine_e(int head_dim, const CombineArgs &a, hipStream_t s) {
+    const dim3 grid(a.rows.total_blocks), block(256);
     switch (head_dim) {
-        case 16: hipLaunchKernelGGL((finalize_kernel<E, 16>), grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((finalize_kernel<E, 32>), grid, block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((finalize_kernel<E, 64>), grid, block, 0, s, a); break;
-        case 128: hipLaunchKernelGGL((finalize_kernel<E, 128>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((combine_kernel<E, 16>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((combine_kernel<E, 32>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((combine_kernel<E, 64>), grid, block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((combine_kernel<E, 128>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(int dtype, int head_dim, const FinalArgs &a, hipStream_t s) {
+hipError_t launch_combine(int dtype, int head_dim, const CombineArgs &a, hipStream_t s) {
+    if (a.rows.total_blocks <= 0) return hipSuccess;
+    return dtype == 0 ? combine_e<float>(head_dim, a, s) : combine_e<bf16_t>(head_dim, a, s);
+}
+
+hipError_t launch_zero_fill(const ZeroArgs &a, hipStream_t s) {
     if (a.rows.n_rows <= 0 || a.hq <= 0) return hipSuccess;
-    return dtype == 0 ? finalize_e<float>(head_dim, a, s) : finalize_e<bf16_t>(head_dim, a, s);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(a.rows.n_rows * a.hq), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace gqakv

@@ -7,7 +7,7 @@
 //   * every K/V/q/out/workspace/lens access lies inside a registered buffer,
 //   * append writes only the slots [lens, lens + n_new) of each row, once,
 //   * each attention call writes every output row (b, h, t) exactly once,
-//   * each split partial is written once before the combine reads it.
+//   * each split partial is written once before the combine kernel reads it.
 // Buffers are fake addresses registered by the test; nothing is dereferenced.
 
 #include <hip/hip_runtime_api.h>
@@ -216,35 +216,48 @@ hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_
     return hipSuccess;
 }
 
-hipError_t launch_finalize(int dtype, int head_dim, const FinalArgs &a, hipStream_t) {
+hipError_t launch_combine(int dtype, int head_dim, const CombineArgs &a, hipStream_t) {
     ++g_launches;
-    const int elem = dtype == 0 ? 4 : 2;
-    const int64_t row_bytes = (int64_t)head_dim * elem;
-    for (int r = 0; r < a.rows.n_rows; ++r) {
-        for (int h = 0; h < a.hq; ++h) {
-            const int b = a.rows.b[r];
-            for (int t = 0; t < a.T; ++t) {
-                const char *o = (const char *)a.out + (((int64_t)b * a.hq + h) * a.T + t) * row_bytes;
-                if (t >= a.rows.nnew[r]) {
-                    access(o, row_bytes, "out", "finalize zero fill");
-                    g_out_rows[(uintptr_t)o]++;
-                    continue;
-                }
-                if (a.rows.nsplit[r] == 0) continue;
-                const int64_t rec = final_record(a.rows, r, h, t, a.group);
-                for (int s = 0; s < a.rows.nsplit[r]; ++s) {
-                    const int64_t rs = rec + (int64_t)s * a.rows.cols[r];
-                    if (rs < 0 || rs >= a.records) err("finalize: record out of range");
-                    auto w = g_records.find(rs);
-                    if (w == g_records.end() || w->second != 1) err("finalize: record not written exactly once");
-                    access(a.ws_acc + rs * head_dim, head_dim * 4, "ws", "finalize acc");
-                    access(a.ws_ml + rs * 2, 8, "ws", "finalize m,l");
-                }
-                access(o, row_bytes, "out", "finalize out");
-                g_out_rows[(uintptr_t)o]++;
+    const int64_t row_bytes = (int64_t)head_dim * (dtype == 0 ? 4 : 2);
+    if (a.rows.blk0[a.rows.n_rows] != a.rows.total_blocks) err("combine: blk0 does not end at total_blocks");
+    for (int blk = 0; blk < a.rows.total_blocks; ++blk) {
+        const int r = find_row(a.rows.blk0, a.rows.n_rows, blk);
+        const int local = blk - a.rows.blk0[r];
+        const int cols = a.rows.cols[r], nsplit = a.rows.nsplit[r], n = a.rows.nnew[r];
+        const int tq = cols / a.group;
+        const int nq = (n + tq - 1) / tq;
+        const int kvh = local / nq, qtile = local % nq;
+        if (kvh >= a.hkv || nsplit < 2) err("combine: block maps outside the row");
+        const int64_t rec_first = a.rows.pbase[r] + (int64_t)((kvh * nq + qtile) * nsplit) * cols;
+        for (int col = 0; col < cols; ++col) {
+            const int t = qtile * tq + col / a.group;
+            if (col >= tq * a.group || t >= n) continue;
+            const int h = kvh * a.group + col % a.group;
+            for (int s = 0; s < nsplit; ++s) {
+                const int64_t rs = rec_first + col + (int64_t)s * cols;
+                if (rs < 0 || rs >= a.records) err("combine: record out of range");
+                auto w = g_records.find(rs);
+                if (w == g_records.end() || w->second != 1) err("combine: partial not written exactly once");
+                access(a.ws_acc + rs * head_dim, head_dim * 4, "ws", "combine acc");
+                access(a.ws_ml + rs * 2, 8, "ws", "combine m,l");
             }
+            const char *o = (const char *)a.out + (((int64_t)a.rows.b[r] * a.hq + h) * a.T + t) * row_bytes;
+            access(o, row_bytes, "out", "combine out");
+            g_out_rows[(uintptr_t)o]++;
         }
     }
+    return hipSuccess;
+}
+
+hipError_t launch_zero_fill(const ZeroArgs &a, hipStream_t) {
+    ++g_launches;
+    for (int r = 0; r < a.rows.n_rows; ++r)
+        for (int h = 0; h < a.hq; ++h)
+            for (int t = a.rows.nnew[r]; t < a.T; ++t) {
+                const char *o = (const char *)a.out + (((int64_t)a.rows.b[r] * a.hq + h) * a.T + t) * a.row_bytes;
+                access(o, a.row_bytes, "out", "zero fill");
+                g_out_rows[(uintptr_t)o]++;
+            }
     return hipSuccess;
 }
 

@@ -178,7 +178,7 @@ def test_llama_decode(sim):
         c.lens[:] = 4096
         c.rewrote = True
         c.check()
-    assert ws > 0
+    assert ws == 0            # 256 (row, kv head) items fill the chip: no cross-group split
 
 
 def test_llama_verify(sim):
