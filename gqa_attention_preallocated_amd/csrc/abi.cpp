@@ -157,6 +157,8 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
             }
             longest = std::max<int64_t>(longest, ceil_div(c->lens[b], kPrefillKeyTile));
         }
+        // a row is split only when its longest item would run more than twice
+        // as long as the per-slot share of the whole launch
         const int64_t cap = std::max<int64_t>(32, ceil_div(total, kPrefillSlots));   // tiles per item
         for (int b : pre_rows) {
             RowPlan r{};
@@ -169,7 +171,7 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
                 r.lsplit = (int)(ceil_div(c->keys_per_split, kPrefillKeyTile) * kPrefillKeyTile);
                 r.nsplit = (int)ceil_div(r.len, r.lsplit);
             } else {
-                r.nsplit = (int)ceil_div(tiles, cap);
+                r.nsplit = tiles > 2 * cap ? (int)ceil_div(tiles, cap) : 1;
                 r.lsplit = (int)(ceil_div(tiles, r.nsplit) * kPrefillKeyTile);
             }
             r.work = tiles * r.nq;

@@ -65,16 +65,25 @@ template <> struct Op<bf16_t> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
     __device__ static inline vec from_f32(const f32x8 &x) { return __builtin_convertvector(x, vec); }
-    // gather 8 elements at byte offsets off[j] from LDS
-    __device__ static inline vec lds_gather(const unsigned char *base, const int *off) {
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t lo = *reinterpret_cast<const uint16_t *>(base + off[2 * j]);
-            uint32_t hi = *reinterpret_cast<const uint16_t *>(base + off[2 * j + 1]);
-            w[j] = lo | (hi << 16);
-        }
-        return __builtin_bit_cast(vec, make_uint4(w[0], w[1], w[2], w[3]));
+    // LDS row stride for a K/V tile: 32 bytes of padding put the rows that one
+    // transposed read touches on disjoint banks
+    static constexpr int kPad = 32;
+    // A operand of O^T += V^T P^T for output rows d0..d0+15 and the 32 keys
+    // key0.. of a row-major LDS tile: lane (i, g) needs V[key][d0 + i] for the
+    // keys k-slot j of group g stands for (4g + j, then 16 + 4g + j). The
+    // gfx950 transpose read gives lane i of a 16-lane group element i%4 of the
+    // 8-byte segments read by lanes i/4 + 4j, so lane a + 4j reads
+    // V[key_j][d0 + 4a .. +3].
+    __device__ static inline vec vt_operand(const unsigned char *tile, int rs, int key0, int d0, int lane) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const int src = lane & 15, g = lane >> 4;
+        const unsigned char *p = tile + (key0 + g * 4 + (src >> 2)) * rs + (d0 + 4 * (src & 3)) * 2;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s *)(p));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s *)(p + 16 * rs));
+        const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+        return __builtin_bit_cast(vec, make_uint4(a.x, a.y, b.x, b.y));
     }
     __device__ static inline void store4(bf16_t *p, f32x4 v) {
         typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
@@ -108,10 +117,16 @@ template <> struct Op<float> {
         return c;
     }
     __device__ static inline vec from_f32(const f32x8 &x) { return x; }
-    __device__ static inline vec lds_gather(const unsigned char *base, const int *off) {
+    static constexpr int kPad = 16;
+    // A operand of O^T += V^T P^T (see the bf16 version): 8 single-element reads
+    __device__ static inline vec vt_operand(const unsigned char *tile, int rs, int key0, int d0, int lane) {
+        const int lr = lane & 15, lg = lane >> 4;
         vec r;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) r[j] = *reinterpret_cast<const float *>(base + off[j]);
+        for (int j = 0; j < 8; ++j) {
+            const int key = key0 + ((j < 4) ? lg * 4 + j : 16 + lg * 4 + (j - 4));
+            r[j] = *reinterpret_cast<const float *>(tile + key * rs + (d0 + lr) * 4);
+        }
         return r;
     }
     __device__ static inline void store4(float *p, f32x4 v) {
@@ -209,7 +224,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     constexpr int NB = D / 16;                    // 16-row blocks of O^T
     constexpr int C = 16 * NSUB;
     constexpr int ROWB = D * O::kBytes;
-    constexpr int RS = ROWB + 16;                 // padded LDS row: conflict-free transposed reads
+    constexpr int RS = ROWB + O::kPad;            // padded LDS row: conflict-free transposed reads
     constexpr int CPK = ROWB / 16;                // 16-byte chunks per key row
     constexpr int VCH = (KT * CPK + 63) / 64;     // V chunks per lane per tile
     constexpr int STAGE = KT * RS;                // per-wave V staging bytes
@@ -257,14 +272,6 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         st[s].l = 0.f;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // transposed-read offsets of V inside the LDS tile: k-slot j of this lane
-    int voff[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int key = (j < 4) ? lg * 4 + j : 16 + lg * 4 + (j - 4);
-        voff[j] = key * RS + lr * O::kBytes;
     }
 
     // ---- prefetch registers
@@ -370,10 +377,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         // ---- O^T += V^T P^T
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            int off[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) off[j] = voff[j] + nb * 16 * O::kBytes;
-            const vec vt = O::lds_gather(lds, off);
+            const vec vt = O::vt_operand(lds, RS, 0, nb * 16, lane);
 #pragma unroll
             for (int s = 0; s < NSUB; ++s) acc[s][nb] = O::mma(vt, O::from_f32(p[s]), acc[s][nb]);
         }
@@ -433,7 +437,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 // the diagonal compare indices ([MASK] "A strong answer", tiled-kernel rule).
 // ---------------------------------------------------------------------------
 template <typename E, int D>
-__global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(AttnArgs a) {
     using O = Op<E>;
     using vec = typename O::vec;
     constexpr int KT = kPrefillKeyTile;           // 64 keys per tile
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
     constexpr int C = kPrefillCols;               // 128 columns per item
     constexpr int NS = 2;                         // 16-column subtiles per wave
     constexpr int ROWB = D * O::kBytes;
-    constexpr int RS = ROWB + 16;
+    constexpr int RS = ROWB + O::kPad;
     constexpr int CPK = ROWB / 16;
     constexpr int TILE_BYTES = KT * RS;
     constexpr int PCH = (KT * CPK + 255) / 256;   // 16-byte chunks per thread per tensor
@@ -496,13 +500,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    int voff[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int key = (j < 4) ? lg * 4 + j : 16 + lg * 4 + (j - 4);
-        voff[j] = key * RS + lr * O::kBytes;
-    }
-
     uint4 kreg[PCH], vreg[PCH];
     auto load_tile = [&](int tile) {
 #pragma unroll
@@ -594,10 +591,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(AttnArgs a) {
                 }
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    int off[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) off[j] = voff[j] + ch * 32 * RS + nb * 16 * O::kBytes;
-                    const vec vt = O::lds_gather(vl, off);
+                    const vec vt = O::vt_operand(vl, RS, ch * 32, nb * 16, lane);
 #pragma unroll
                     for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt, O::from_f32(p[s]), acc[s][nb]);
                 }
