@@ -210,10 +210,11 @@ struct ColState {
 // ---------------------------------------------------------------------------
 // split-K decode / verify kernel. One work group of W waves per work item
 // (row, kv head, query tile, key split) with 16*NSUB columns. The item's key
-// range is cut into W contiguous pieces, one per wave; each wave streams its
-// 32-key tiles from HBM (the next tile in flight while the current one is
-// computed), then the waves merge their partial results through LDS (reusing
-// the V staging space), so a split-free row needs no second pass.
+// range is cut into W contiguous pieces, one per wave (a fixed assignment, so
+// results are bitwise reproducible); each wave streams its 32-key tiles from
+// HBM with the next tiles in flight while one is computed, then the waves
+// merge their partial results through LDS (reusing the V staging space), so a
+// split-free row needs no second pass.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int NSUB, int W>
 __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
@@ -274,10 +275,12 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- prefetch registers
-    vec kop[2][KC];
-    uint4 vreg[VCH];
-    auto load_tile = [&](int tile) {
+    // ---- prefetch: with two register sets the next two tiles are in flight
+    //      while one is computed (where registers allow), else the next one
+    constexpr int PF = (NSUB == 1 && O::kBytes == 2) ? 2 : 1;
+    vec kA[2][KC], kB[2][KC];
+    uint4 vA[VCH], vB[VCH];
+    auto load_tile = [&](vec (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int key = tile + ks * 16 + lr;
@@ -299,17 +302,12 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         }
     };
 
-    if (w_begin < w_end) load_tile(w_begin);
     // smallest position among this item's real columns: tiles ending at or
     // before it need no mask ([MASK] "A strong answer", tile cases)
     const int pos_min = it.base + it.t0;
 
-    for (int tile = w_begin; tile < w_end; tile += KT) {
-        vec kcur[2][KC];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) kcur[ks][kc] = kop[ks][kc];
+    // compute the tile held in (kop, vreg), refilling the set with the tile PF ahead
+    auto process = [&](vec (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
         // V tile into this wave's LDS stage (row-major, padded)
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
@@ -319,8 +317,6 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
                 *reinterpret_cast<uint4 *>(lds + key * RS + part * 16) = vreg[i];
             }
         }
-        if (tile + KT < w_end) load_tile(tile + KT);
-
         // ---- S^T = K Q^T for the 32 keys
         f32x4 sc[NSUB][2];
 #pragma unroll
@@ -329,9 +325,10 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
             for (int ks = 0; ks < 2; ++ks) {
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) c = O::mma(kcur[ks][kc], qop[s][kc], c);
+                for (int kc = 0; kc < KC; ++kc) c = O::mma(kop[ks][kc], qop[s][kc], c);
                 sc[s][ks] = c;
             }
+        if (tile + PF * KT < w_end) load_tile(kop, vreg, tile + PF * KT);
 
         // ---- mask (only tiles that straddle the diagonal or the range end),
         //      online softmax in log2 units
@@ -383,6 +380,17 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);   // V^T reads done before the stage is overwritten
         __builtin_amdgcn_wave_barrier();
+    };
+
+    if (w_begin < w_end) load_tile(kA, vA, w_begin);
+    if constexpr (PF == 2) {
+        if (w_begin + KT < w_end) load_tile(kB, vB, w_begin + KT);
+        for (int tile = w_begin; tile < w_end; tile += 2 * KT) {
+            process(kA, vA, tile);
+            if (tile + KT < w_end) process(kB, vB, tile + KT);
+        }
+    } else {
+        for (int tile = w_begin; tile < w_end; tile += KT) process(kA, vA, tile);
     }
 
     // ---- merge the W waves' partials in LDS, one 16-column subtile at a time
