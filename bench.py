@@ -263,6 +263,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="time one workload only (for profiling); prints its own JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -284,7 +286,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.only == "prefill":
+        print(json.dumps({"prefill": run_prefill(torch)}), flush=True)
+        return
     res = run_decode(torch, args.steps, args.warmup)
+    if args.only == "decode":
+        args.no_prefill = True
+        args.no_cpu_baseline = True
     step_bytes = res["att_bytes"] + res["append_bytes"]
     value = step_bytes / res["wall_s"] / 1e9
     achieved = res["att_bytes"] / (res["att_ms_avg"] * 1e-3) / 1e9

@@ -134,11 +134,18 @@ template <> struct Op<float> {
     }
 };
 
+// 2^x with the hardware instruction alone. exp2f adds a range fix for
+// results below 2^-126; a probability that small is zero for every purpose here.
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline float wave_max_across_groups(float v) {
-    // lanes l, l^16, l^32, l^48 hold the same column
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    // lanes l, l^16, l^32, l^48 hold the same column. A gfx950 lane-half swap
+    // returns (own, partner) in some order, so the max of the pair is the max
+    // over the two lanes, with no LDS traffic.
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ inline float wave_sum_across_groups(float v) {
@@ -202,9 +209,42 @@ __device__ inline E *column_out(const AttnArgs &a, const Item &it, int col, int 
 // pos (or past k_end) get probability 0. Returns the rescale factor for the
 // accumulator and writes the probabilities back into s0/s1.
 struct ColState {
-    float m;   // running max, log2 units (-inf until a key is visible)
+    float m;   // reference max, log2 units (-inf until a key is visible)
     float l;   // this lane's share of the running denominator
 };
+
+// The accumulator is rescaled only when a column's max grows past the
+// reference by more than this (log2 units): between rescales exp2 arguments
+// stay <= 8, so probabilities stay <= 256, far inside float32 and bfloat16
+// range, and acc / l is unchanged algebraically.
+constexpr float kRescaleLog2 = 8.f;
+
+// One online-softmax step for the 8 raw scores q.k a lane holds for its
+// column (two 16-key blocks: v[0..3] = keys 4g..4g+3, v[4..7] = keys
+// 16+4g..16+4g+3 of a 32-key chunk, g = lane/16); invisible keys are -inf.
+// c = log2(e)/sqrt(d) > 0, so the max of raw scores scaled by c is the max of
+// the scaled scores. Writes p = exp2(v*c - m) and updates the state.
+template <int NB>
+__device__ inline void softmax_step(const float (&v)[8], float c, ColState &st, f32x4 (&acc)[NB], f32x8 &p) {
+    float tmax = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    tmax = wave_max_across_groups(tmax) * c;
+    if (tmax > st.m + kRescaleLog2) {             // st.m = -inf: the first visible key sets it
+        const float alpha = fast_exp2(st.m - tmax);   // 0 when st.m = -inf (acc and l are still 0)
+        st.l *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
+        st.m = tmax;
+    }
+    const float m_use = (st.m == -INFINITY) ? 0.f : st.m;   // no key seen yet: every p is 0
+    float lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float e = fast_exp2(fmaf(v[j], c, -m_use));
+        p[j] = e;
+        lsum += e;
+    }
+    st.l += lsum;
+}
 
 
 // ---------------------------------------------------------------------------
@@ -338,34 +378,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         for (int s = 0; s < NSUB; ++s) {
             float v[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int ks = j >> 2, i = j & 3;
-                v[j] = sc[s][ks][i] * a.scale_log2;
-                if (need_mask) {
-                    const int key = tile + ks * 16 + lg * 4 + i;
-                    if (key >= w_end || key > pos[s]) v[j] = -INFINITY;
-                }
-            }
-            float tmax = v[0];
+            for (int j = 0; j < 8; ++j) v[j] = sc[s][j >> 2][j & 3];
+            if (need_mask) {                      // uniform over the wave
+                // key j is visible iff j <= pos and j < the range end
+                const int lim = imin(pos[s] + 1, w_end) - (tile + lg * 4);
 #pragma unroll
-            for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, v[j]);
-            tmax = wave_max_across_groups(tmax);
-            const float m_new = fmaxf(st[s].m, tmax);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // fully masked so far: p = 0
-            const float alpha = exp2f(st[s].m - m_use);
-            float lsum = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float e = exp2f(v[j] - m_use);
-                p[s][j] = e;
-                lsum += e;
+                for (int j = 0; j < 8; ++j) v[j] = ((j >> 2) * 16 + (j & 3) < lim) ? v[j] : -INFINITY;
             }
-            st[s].l = st[s].l * alpha + lsum;
-            st[s].m = m_new;
-            if (alpha != 1.f) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[s][nb] *= alpha;
-            }
+            softmax_step<NB>(v, a.scale_log2, st[s], acc[s], p[s]);
         }
 
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's V stores have landed
@@ -420,7 +440,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 #pragma unroll
             for (int w = 0; w < W; ++w) {
                 const float2 ml = *reinterpret_cast<const float2 *>(pml + (w * 16 + c16) * 2);
-                const float wt = exp2f(ml.x - m_use);      // a wave that saw no key: weight 0
+                const float wt = fast_exp2(ml.x - m_use);      // a wave that saw no key: weight 0
                 const float4 x = *reinterpret_cast<const float4 *>(part + (w * 16 + c16) * PSTR + d);
                 o[0] += wt * x.x; o[1] += wt * x.y; o[2] += wt * x.z; o[3] += wt * x.w;
                 L += wt * ml.y;
@@ -568,34 +588,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 for (int s = 0; s < NS; ++s) {
                     float v[8];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int ks = j >> 2, i = j & 3;
-                        v[j] = sc[s][ks][i] * a.scale_log2;
-                        if (need_mask) {
-                            const int key = tile + ch * 32 + ks * 16 + lg * 4 + i;
-                            if (key >= it.k_end || key > pos[s]) v[j] = -INFINITY;
-                        }
-                    }
-                    float tmax = v[0];
+                    for (int j = 0; j < 8; ++j) v[j] = sc[s][j >> 2][j & 3];
+                    if (need_mask) {              // uniform over the wave
+                        // key j is visible iff j <= pos and j < the split end
+                        const int lim = imin(pos[s] + 1, it.k_end) - (tile + ch * 32 + lg * 4);
 #pragma unroll
-                    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, v[j]);
-                    tmax = wave_max_across_groups(tmax);
-                    const float m_new = fmaxf(st[s].m, tmax);
-                    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-                    const float alpha = exp2f(st[s].m - m_use);
-                    float lsum = 0.f;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float e = exp2f(v[j] - m_use);
-                        p[s][j] = e;
-                        lsum += e;
+                        for (int j = 0; j < 8; ++j) v[j] = ((j >> 2) * 16 + (j & 3) < lim) ? v[j] : -INFINITY;
                     }
-                    st[s].l = st[s].l * alpha + lsum;
-                    st[s].m = m_new;
-                    if (alpha != 1.f) {
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) acc[s][nb] *= alpha;
-                    }
+                    softmax_step<NB>(v, a.scale_log2, st[s], acc[s], p[s]);
                 }
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
@@ -691,12 +691,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) bm = fmaxf(bm, ml[j].x);
             if (bm == -INFINITY) continue;        // no split so far saw a key of this column
-            const float c = exp2f(M - bm);        // M = -inf: c = 0 (acc and L are still 0)
+            const float c = fast_exp2(M - bm);        // M = -inf: c = 0 (acc and L are still 0)
             acc *= c;
             L *= c;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float w = exp2f(ml[j].x - bm);   // a split that saw no key: w = 0
+                const float w = fast_exp2(ml[j].x - bm);   // a split that saw no key: w = 0
                 acc[0] += w * x[j].x; acc[1] += w * x[j].y; acc[2] += w * x[j].z; acc[3] += w * x[j].w;
                 L += w * ml[j].y;
             }
