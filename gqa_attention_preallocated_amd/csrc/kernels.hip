@@ -246,6 +246,32 @@ __device__ inline void softmax_step(const float (&v)[8], float c, ColState &st, 
     st.l += lsum;
 }
 
+// The same step over the N = 16 scores of two 32-key chunks (v[0..7] chunk
+// 0, v[8..15] chunk 1, each in the layout above): one max, one rescale test.
+template <int NB, int N>
+__device__ inline void softmax_tile(const float (&v)[N], float c, ColState &st, f32x4 (&acc)[NB], f32x8 &p0,
+                                    f32x8 &p1) {
+    float t0 = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    float t1 = fmaxf(fmaxf(fmaxf(v[8], v[9]), fmaxf(v[10], v[11])), fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15])));
+    const float tmax = wave_max_across_groups(fmaxf(t0, t1)) * c;
+    if (tmax > st.m + kRescaleLog2) {
+        const float alpha = fast_exp2(st.m - tmax);
+        st.l *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
+        st.m = tmax;
+    }
+    const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
+    float lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        p0[j] = fast_exp2(fmaf(v[j], c, -m_use));
+        p1[j] = fast_exp2(fmaf(v[8 + j], c, -m_use));
+        lsum += p0[j] + p1[j];
+    }
+    st.l += lsum;
+}
+
 
 // ---------------------------------------------------------------------------
 // split-K decode / verify kernel. One work group of W waves per work item
@@ -563,14 +589,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             const unsigned char *kl = lds[buf][0];
             const unsigned char *vl = lds[buf][1];
             const bool need_mask = (tile + KT > it.k_end) || (tile + KT - 1 > wave_pos_min);
-            // two 32-key chunks; each chunk's scores feed the chunk's O^T update
+            // scores of both 32-key chunks first, so the softmax of one chunk
+            // can issue while the matrix core still works on the next
+            f32x4 sc[2][NS][2];
+            __builtin_amdgcn_s_setprio(1);    // matrix phase first: the other wave on the SIMD takes the VALU
 #pragma unroll
             for (int ch = 0; ch < 2; ++ch) {
-                f32x4 sc[NS][2];
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    sc[s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    sc[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    sc[ch][s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    sc[ch][s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
@@ -580,30 +608,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                         const int d0 = kc * 32 + lg * 8;
                         const vec kv = (d0 < D) ? O::lds_load(kl + krow * RS + d0 * O::kBytes) : O::zero();
 #pragma unroll
-                        for (int s = 0; s < NS; ++s) sc[s][ks] = O::mma(kv, qop[s][kc], sc[s][ks]);
+                        for (int s = 0; s < NS; ++s) sc[ch][s][ks] = O::mma(kv, qop[s][kc], sc[ch][s][ks]);
                     }
                 }
-                f32x8 p[NS];
+            }
+            // one max and one rescale decision per column for the whole tile;
+            // the exponentials and both chunks' O^T products then form one
+            // branch-free block the scheduler can interleave
+            f32x8 p[2][NS];
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    float v[8];
+            for (int s = 0; s < NS; ++s) {
+                float v[16];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) v[j] = sc[s][j >> 2][j & 3];
-                    if (need_mask) {              // uniform over the wave
-                        // key j is visible iff j <= pos and j < the split end
-                        const int lim = imin(pos[s] + 1, it.k_end) - (tile + ch * 32 + lg * 4);
+                for (int j = 0; j < 16; ++j) v[j] = sc[j >> 3][s][(j >> 2) & 1][j & 3];
+                if (need_mask) {                  // uniform over the wave
+                    // key (ch, j) is visible iff it is <= pos and < the split end
+                    const int lim = imin(pos[s] + 1, it.k_end) - (tile + lg * 4);
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) v[j] = ((j >> 2) * 16 + (j & 3) < lim) ? v[j] : -INFINITY;
+                    for (int j = 0; j < 16; ++j) {
+                        const int off = (j >> 3) * 32 + ((j >> 2) & 1) * 16 + (j & 3);
+                        v[j] = (off < lim) ? v[j] : -INFINITY;
                     }
-                    softmax_step<NB>(v, a.scale_log2, st[s], acc[s], p[s]);
                 }
+                softmax_tile<NB, 16>(v, a.scale_log2, st[s], acc[s], p[0][s], p[1][s]);
+            }
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const vec vt = O::vt_operand(vl, RS, ch * 32, nb * 16, lane);
 #pragma unroll
-                    for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt, O::from_f32(p[s]), acc[s][nb]);
+                    for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt, O::from_f32(p[ch][s]), acc[s][nb]);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         buf ^= 1;
     }
