@@ -223,6 +223,83 @@ def run_prefill(torch, reps=3):
     }
 
 
+def _fill_gpu_random(torch, cache, lens, seed, chunk=4096):
+    """Seeded N(0,1) K/V history drawn on the GPU (fast set-up for timing runs)."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    lens = [int(x) for x in lens]
+    done = [0] * len(lens)
+    B, hkv, d = cache.batch, cache.kv_heads, cache.head_dim
+    while any(x < l for x, l in zip(done, lens)):
+        n = [min(chunk, l - x) for x, l in zip(done, lens)]
+        T = max(n)
+        k = torch.randn(B, hkv, T, d, device="cuda", generator=g).to(torch.bfloat16)
+        v = torch.randn(B, hkv, T, d, device="cuda", generator=g).to(torch.bfloat16)
+        cache.append(k, v, n)
+        done = [x + y for x, y in zip(done, n)]
+
+
+def _time_calls(torch, fn, reps):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps * 1e-3
+
+
+def run_verify(torch, reps=30):
+    """Speculative verify: B=16, 4,092 cached + 4 new tokens per row, T=4."""
+    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    import workloads as W
+    sh = W.LLAMA8B_VERIFY
+    B, hq, hkv, d = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim
+    caches = [KVCache(B, hkv, sh.max_len, d, device_lens=False) for _ in range(2)]
+    n = [4] * B
+    for i, c in enumerate(caches):
+        _fill_gpu_random(torch, c, [4096] * B, 20 + i)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    q = torch.randn(B, hq, 4, d, device="cuda", generator=g).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(max(c.workspace_bytes(hq, 4, n) for c in caches), 256), dtype=torch.uint8, device="cuda")
+    t = _time_calls(torch, lambda i: gqa_attention(q, caches[i & 1], n, out=out, workspace=ws), reps)
+    nbytes = attention_bytes([4096] * B, n, hq, hkv, d, 4)
+    return {"metric": "verify attention HBM GB/s", "value": round(nbytes / t / 1e9, 2), "unit": "GB/s",
+            "frac_of_8TBs": round(nbytes / t / 8e12, 4), "ms": round(t * 1e3, 5), "bytes": nbytes,
+            "config": {"workload": sh.name, "batch": B, "T": 4, "keys": 4096}}
+
+
+def run_ragged(torch, seed=4, reps=20):
+    """Ragged batch: 64 rows, log-uniform lengths in [1, 32000], n_new in {0, 1, 4, 256}, T=256."""
+    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    import workloads as W
+    sh = W.LLAMA8B_RAGGED
+    B, hq, hkv, d, T = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim, 256
+    lens, n_new = W.ragged_rows(seed)
+    cache = KVCache(B, hkv, sh.max_len, d, device_lens=False)
+    _fill_gpu_random(torch, cache, lens, 30)
+    g = torch.Generator(device="cuda").manual_seed(8)
+    kn = torch.randn(B, hkv, T, d, device="cuda", generator=g).to(torch.bfloat16)
+    q = torch.randn(B, hq, T, d, device="cuda", generator=g).to(torch.bfloat16)
+    n = [int(x) for x in n_new]
+    cache.append(kn, kn, n)
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(cache.workspace_bytes(hq, T, n), 256), dtype=torch.uint8, device="cuda")
+    t = _time_calls(torch, lambda i: gqa_attention(q, cache, n, out=out, workspace=ws), reps)
+    after = [int(l) + x for l, x in zip(lens, n)]
+    nbytes = attention_bytes(after, n, hq, hkv, d, T)
+    flops = attention_flops(after, n, hq, d)
+    t_bw, t_mm = nbytes / 8e12, flops / 2.5e15
+    return {"metric": "ragged batch attention, lower bound / time", "value": round(max(t_bw, t_mm) / t, 4),
+            "unit": "fraction", "ms": round(t * 1e3, 5), "bytes": nbytes, "flops": flops,
+            "hbm_frac": round(t_bw / t, 4), "mfma_frac": round(t_mm / t, 4),
+            "rows_by_n_new": {str(k): int((n_new == k).sum()) for k in (0, 1, 4, 256)},
+            "config": {"workload": sh.name, "seed": seed, "batch": B, "T": T, "sum_lens": int(sum(after))}}
+
+
 def cpu_baseline(res, max_rows=32, budget_s=20.0):
     """The float64 oracle on the host, one decode step over as many rows as fit the budget."""
     try:
@@ -263,7 +340,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged"], default=None,
                     help="time one workload only (for profiling); prints its own JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one plain 256 MiB device copy (counter calibration)")
@@ -286,8 +363,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if args.only == "prefill":
-        print(json.dumps({"prefill": run_prefill(torch)}), flush=True)
+    if args.only in ("prefill", "verify", "ragged"):
+        fn = {"prefill": run_prefill, "verify": run_verify, "ragged": run_ragged}[args.only]
+        print(json.dumps({args.only: fn(torch)}), flush=True)
         return
     res = run_decode(torch, args.steps, args.warmup)
     if args.only == "decode":

@@ -156,8 +156,7 @@ class KVCache:
         if nbytes == 0:
             return None
         if self._ws is None or self._ws.numel() < nbytes:
-            # zero-filled once: the split-combine counters then start from a known state
-            self._ws = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+            self._ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         return self._ws
 
 

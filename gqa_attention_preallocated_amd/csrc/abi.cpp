@@ -34,6 +34,7 @@ struct kv_cache {
     std::vector<int32_t> lens;   // host copy, authoritative, updated at enqueue
     int32_t path_policy = 0;     // 0 auto, 1 split-K decode kernel, 2 prefill kernel
     int32_t keys_per_split = 0;  // 0 auto
+    SideStream side;             // created on the first mixed decode + prefill call
 };
 
 namespace {
@@ -157,9 +158,10 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
             }
             longest = std::max<int64_t>(longest, ceil_div(c->lens[b], kPrefillKeyTile));
         }
-        // a row is split only when its longest item would run more than twice
-        // as long as the per-slot share of the whole launch
-        const int64_t cap = std::max<int64_t>(32, ceil_div(total, kPrefillSlots));   // tiles per item
+        // a row is split only when its longest item would run well past the
+        // per-slot share of the whole launch (the launch lasts as long as its
+        // longest item)
+        const int64_t cap = std::max<int64_t>(8, ceil_div(total, kPrefillSlots));    // tiles per item
         for (int b : pre_rows) {
             RowPlan r{};
             r.b = b;
@@ -171,7 +173,7 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
                 r.lsplit = (int)(ceil_div(c->keys_per_split, kPrefillKeyTile) * kPrefillKeyTile);
                 r.nsplit = (int)ceil_div(r.len, r.lsplit);
             } else {
-                r.nsplit = tiles > 2 * cap ? (int)ceil_div(tiles, cap) : 1;
+                r.nsplit = 2 * tiles > 3 * cap ? (int)ceil_div(tiles, cap) : 1;
                 r.lsplit = (int)(ceil_div(tiles, r.nsplit) * kPrefillKeyTile);
             }
             r.work = tiles * r.nq;
@@ -310,7 +312,11 @@ kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int3
     return ok();
 }
 
-void kv_cache_destroy(kv_cache *c) { delete c; }
+void kv_cache_destroy(kv_cache *c) {
+    if (c == nullptr) return;
+    side_stream_destroy(c->side);
+    delete c;
+}
 
 kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T, const int32_t *n_new,
                     void *stream) {
@@ -403,7 +409,20 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
     const WsLayout w = ws_layout(c, p);
     char *ws = (char *)workspace;
 
-    // padded slots first: independent of the attention kernels
+    // A batch with both decode and prefill rows runs the decode kernel on a
+    // side stream forked from (and later joined back to) the caller's stream,
+    // beside the zero fill and the prefill kernel, so no kernel's ramp and
+    // tail idles the chip. The three write disjoint output slots.
+    const bool mixed = !p.pre.empty() && !p.dec.empty();
+    hipStream_t dec_stream = st;
+    if (mixed) {
+        hipError_t e = side_stream_init(c->side);
+        if (e == hipSuccess) e = side_stream_fork(c->side, st);
+        if (e != hipSuccess) return device_fail(e, "gqa_attention (side stream)");
+        dec_stream = c->side.side;
+    }
+
+    // padded slots: independent of the attention kernels
     for (size_t lo = 0; lo < p.pad_rows.size(); lo += kMaxRows) {
         ZeroArgs z{};
         z.out = out;
@@ -412,6 +431,7 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
         z.hq = q_heads;
         z.head_dim = c->head_dim;
         z.row_bytes = (int64_t)c->head_dim * c->elem_bytes;
+        z.slices = (int32_t)ceil_div((int64_t)T * z.row_bytes, kZeroSlice);
         const size_t hi = std::min(p.pad_rows.size(), lo + kMaxRows);
         z.rows.n_rows = (int32_t)(hi - lo);
         for (size_t i = lo; i < hi; ++i) {
@@ -439,15 +459,19 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
     a.records = p.records;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c->head_dim));
 
+    for (size_t lo = 0; lo < p.dec.size(); lo += kMaxRows) {
+        fill_attn_rows(p.dec, lo, std::min(p.dec.size(), lo + kMaxRows), c->kv_heads, a.rows);
+        hipError_t e = launch_decode((int)c->dtype, c->head_dim, p.nsub, a, dec_stream);
+        if (e != hipSuccess) return device_fail(e, "gqa_attention (decode kernel)");
+    }
     for (size_t lo = 0; lo < p.pre.size(); lo += kMaxRows) {
         fill_attn_rows(p.pre, lo, std::min(p.pre.size(), lo + kMaxRows), c->kv_heads, a.rows);
         hipError_t e = launch_prefill((int)c->dtype, c->head_dim, a, st);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (prefill kernel)");
     }
-    for (size_t lo = 0; lo < p.dec.size(); lo += kMaxRows) {
-        fill_attn_rows(p.dec, lo, std::min(p.dec.size(), lo + kMaxRows), c->kv_heads, a.rows);
-        hipError_t e = launch_decode((int)c->dtype, c->head_dim, p.nsub, a, st);
-        if (e != hipSuccess) return device_fail(e, "gqa_attention (decode kernel)");
+    if (mixed) {
+        hipError_t e = side_stream_join(c->side, st);
+        if (e != hipSuccess) return device_fail(e, "gqa_attention (side stream)");
     }
     // rows split across work groups: merge their partials
     std::vector<std::pair<const RowPlan *, int>> split_rows;
@@ -479,7 +503,8 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
             m.rows.pbase[j] = (int32_t)r.pbase;
             m.rows.cols[j] = split_rows[i].second;
             m.rows.blk0[j] = blocks;
-            blocks += c->kv_heads * r.nq;
+            const int per_group = (int)ceil_div((int64_t)split_rows[i].second * (c->head_dim / 4), 256);
+            blocks += c->kv_heads * r.nq * per_group;
         }
         m.rows.blk0[m.rows.n_rows] = blocks;
         m.rows.total_blocks = blocks;

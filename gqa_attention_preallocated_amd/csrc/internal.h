@@ -99,6 +99,7 @@ struct ZeroRows {
 struct ZeroArgs {
     void *out;
     int32_t batch, T, hq, head_dim;
+    int32_t slices;            // kZeroSlice-byte slices per (row, query head): ceil(T * row_bytes / kZeroSlice)
     int64_t row_bytes;         // d * element size
     ZeroRows rows;
 };
@@ -110,12 +111,26 @@ hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t s)
 hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t s);
 hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t s);
 hipError_t launch_combine(int dtype, int head_dim, const CombineArgs &a, hipStream_t s);
+
+// Side stream for running the decode kernel beside the prefill kernel of a
+// mixed batch. `fork` makes `side` wait for all work enqueued on `main` so far;
+// `join` makes `main` wait for all work enqueued on `side`. The stream and
+// events are created once (default priority) and owned by the caller.
+struct SideStream {
+    hipStream_t side = nullptr;
+    hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+};
+hipError_t side_stream_init(SideStream &s);
+void side_stream_destroy(SideStream &s);
+hipError_t side_stream_fork(SideStream &s, hipStream_t main);
+hipError_t side_stream_join(SideStream &s, hipStream_t main);
 hipError_t launch_zero_fill(const ZeroArgs &a, hipStream_t s);
 
 constexpr int kDecodeKeyTile = 32;
 constexpr int kDecodeWaves = 8;       // waves per decode work group (they split the keys)
 constexpr int kPrefillKeyTile = 64;
 constexpr int kPrefillCols = 128;
+constexpr int kZeroSlice = 16384;   // bytes of output one zero-fill block clears
 constexpr int kAppendChunk = 4096;
 
 }  // namespace gqakv

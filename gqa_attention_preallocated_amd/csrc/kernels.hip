@@ -673,25 +673,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 // ---------------------------------------------------------------------------
 // zero fill: +0.0 into every padded slot t >= n_new[b] (and every slot of a
 // row with no new tokens). [GQA] "A strong answer": such rows give zeros,
-// never NaN. One block per (row, query head); 16-byte stores.
+// never NaN. Each block clears one 16 KiB slice of a (row, query head) region
+// [0, T) x d, clipped to the padded part; 16-byte stores, 4 per thread.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void zero_fill_kernel(ZeroArgs a) {
-    const int r = blockIdx.x / a.hq;
-    const int h = blockIdx.x % a.hq;
+    const int slice = blockIdx.x % a.slices;
+    const int rh = blockIdx.x / a.slices;
+    const int r = rh / a.hq;
+    const int h = rh % a.hq;
     const int b = a.rows.b[r];
     const int n = a.rows.nnew[r];
     const int64_t head_off = ((int64_t)b * a.hq + h) * a.T * a.row_bytes;
-    const int64_t begin = head_off + (int64_t)n * a.row_bytes;
-    const int64_t end = head_off + (int64_t)a.T * a.row_bytes;
+    const int64_t lo = (int64_t)slice * kZeroSlice;
+    const int64_t begin = head_off + (lo > (int64_t)n * a.row_bytes ? lo : (int64_t)n * a.row_bytes);
+    const int64_t hi = lo + kZeroSlice;
+    const int64_t end = head_off + (hi < (int64_t)a.T * a.row_bytes ? hi : (int64_t)a.T * a.row_bytes);
     char *out = reinterpret_cast<char *>(a.out);
-    for (int64_t off = begin + threadIdx.x * 16; off < end; off += 256 * 16)
-        *reinterpret_cast<uint4 *>(out + off) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kZeroSlice / (256 * 16); ++j) {
+        const int64_t off = head_off + lo + (j * 256 + threadIdx.x) * 16;
+        if (off >= begin && off < end) *reinterpret_cast<uint4 *>(out + off) = make_uint4(0, 0, 0, 0);
+    }
 }
 
 // ---------------------------------------------------------------------------
 // combine: for rows split across work groups, merge the nsplit partials of
-// every column by log-sum-exp in split order, normalise and cast. One block per
-// (row, kv head, query tile); loads of 8 splits are issued together.
+// every column by log-sum-exp in split order, normalise and cast. One thread
+// per (column, 4 outputs) of a (row, kv head, query tile); loads of 8 splits
+// are issued together.
 // ---------------------------------------------------------------------------
 template <typename E, int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
@@ -702,49 +711,51 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int cols = a.rows.cols[r], nsplit = a.rows.nsplit[r], n = a.rows.nnew[r];
     const int tq = cols / a.group;
     const int nq = (n + tq - 1) / tq;
-    const int kvh = local / nq, qtile = local % nq;
+    const int per_group = (cols * DC + 255) / 256;   // blocks per (kv head, query tile)
+    const int grp = local / per_group, part = local % per_group;
+    const int kvh = grp / nq, qtile = grp % nq;
     const int b = a.rows.b[r];
     const int64_t rec_first = a.rows.pbase[r] + (int64_t)((kvh * nq + qtile) * nsplit) * cols;
-    for (int task = threadIdx.x; task < cols * DC; task += 256) {
-        const int col = task / DC, d = (task % DC) * 4;
-        const int t = qtile * tq + col / a.group;
-        if (col >= tq * a.group || t >= n) continue;
-        const int h = kvh * a.group + col % a.group;
-        const int64_t rec = rec_first + col;
-        float M = -INFINITY, L = 0.f;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < nsplit; s0 += 8) {
-            float2 ml[8];
-            float4 x[8];
+    const int task = part * 256 + threadIdx.x;       // one (column, 4 outputs) per thread
+    if (task >= cols * DC) return;
+    const int col = task / DC, d = (task % DC) * 4;
+    const int t = qtile * tq + col / a.group;
+    if (col >= tq * a.group || t >= n) return;
+    const int h = kvh * a.group + col % a.group;
+    const int64_t rec = rec_first + col;
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        float2 ml[8];
+        float4 x[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t rs = rec + (int64_t)(s0 + j) * cols;
-                if (s0 + j < nsplit) {
-                    ml[j] = *reinterpret_cast<const float2 *>(a.ws_ml + rs * 2);
-                    x[j] = *reinterpret_cast<const float4 *>(a.ws_acc + rs * D + d);
-                } else {
-                    ml[j] = make_float2(-INFINITY, 0.f);
-                    x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-                }
+        for (int j = 0; j < 8; ++j) {
+            const int64_t rs = rec + (int64_t)(s0 + j) * cols;
+            if (s0 + j < nsplit) {
+                ml[j] = *reinterpret_cast<const float2 *>(a.ws_ml + rs * 2);
+                x[j] = *reinterpret_cast<const float4 *>(a.ws_acc + rs * D + d);
+            } else {
+                ml[j] = make_float2(-INFINITY, 0.f);
+                x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            float bm = M;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bm = fmaxf(bm, ml[j].x);
-            if (bm == -INFINITY) continue;        // no split so far saw a key of this column
-            const float c = fast_exp2(M - bm);        // M = -inf: c = 0 (acc and L are still 0)
-            acc *= c;
-            L *= c;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float w = fast_exp2(ml[j].x - bm);   // a split that saw no key: w = 0
-                acc[0] += w * x[j].x; acc[1] += w * x[j].y; acc[2] += w * x[j].z; acc[3] += w * x[j].w;
-                L += w * ml[j].y;
-            }
-            M = bm;
         }
-        E *op = reinterpret_cast<E *>(a.out) + (((int64_t)b * a.hq + h) * a.T + t) * D + d;
-        O::store4(op, acc * (L > 0.f ? 1.f / L : 0.f));
+        float bm = M;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bm = fmaxf(bm, ml[j].x);
+        if (bm == -INFINITY) continue;            // no split so far saw a key of this column
+        const float c = fast_exp2(M - bm);        // M = -inf: c = 0 (acc and L are still 0)
+        acc *= c;
+        L *= c;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float w = fast_exp2(ml[j].x - bm);   // a split that saw no key: w = 0
+            acc[0] += w * x[j].x; acc[1] += w * x[j].y; acc[2] += w * x[j].z; acc[3] += w * x[j].w;
+            L += w * ml[j].y;
+        }
+        M = bm;
     }
+    E *op = reinterpret_cast<E *>(a.out) + (((int64_t)b * a.hq + h) * a.T + t) * D + d;
+    O::store4(op, acc * (L > 0.f ? 1.f / L : 0.f));
 }
 
 // ---------------------------------------------------------------------------
@@ -827,9 +838,35 @@ hipError_t launch_combine(int dtype, int head_dim, const CombineArgs &a, hipStre
     return dtype == 0 ? combine_e<float>(head_dim, a, s) : combine_e<bf16_t>(head_dim, a, s);
 }
 
+hipError_t side_stream_init(SideStream &s) {
+    if (s.side != nullptr) return hipSuccess;
+    hipError_t e = hipStreamCreateWithFlags(&s.side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&s.fork_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&s.join_ev, hipEventDisableTiming);
+    if (e != hipSuccess) side_stream_destroy(s);
+    return e;
+}
+
+void side_stream_destroy(SideStream &s) {
+    if (s.fork_ev) (void)hipEventDestroy(s.fork_ev);
+    if (s.join_ev) (void)hipEventDestroy(s.join_ev);
+    if (s.side) (void)hipStreamDestroy(s.side);
+    s = SideStream{};
+}
+
+hipError_t side_stream_fork(SideStream &s, hipStream_t main) {
+    hipError_t e = hipEventRecord(s.fork_ev, main);
+    return e == hipSuccess ? hipStreamWaitEvent(s.side, s.fork_ev, 0) : e;
+}
+
+hipError_t side_stream_join(SideStream &s, hipStream_t main) {
+    hipError_t e = hipEventRecord(s.join_ev, s.side);
+    return e == hipSuccess ? hipStreamWaitEvent(main, s.join_ev, 0) : e;
+}
+
 hipError_t launch_zero_fill(const ZeroArgs &a, hipStream_t s) {
     if (a.rows.n_rows <= 0 || a.hq <= 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_fill_kernel, dim3(a.rows.n_rows * a.hq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(a.rows.n_rows * a.hq * a.slices), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

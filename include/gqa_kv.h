@@ -120,11 +120,16 @@ kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32
  *   q             device [B, q_heads, T, d]; out device [B, q_heads, T, d].
  *   n_new         HOST int32[B] with 0 <= n_new[b] <= min(T, lens[b]).
  *   workspace     device scratch of at least gqa_attention_workspace_size()
- *                 bytes (may be NULL when that size is 0). It holds the split
- *                 partials and the counters by which the last split of each
- *                 (row, kv head, query tile) finds out it must merge them; every
- *                 call tags its counters, so the contents need no initialisation.
- *                 Two calls in flight at once must not share a workspace.
+ *                 bytes (may be NULL when that size is 0). It holds the
+ *                 unnormalised partial outputs and (max, sum) pairs of key
+ *                 ranges split across work groups; every partial is written
+ *                 before it is read in the same call, so the contents need no
+ *                 initialisation. Two calls in flight at once must not share a
+ *                 workspace.
+ * A batch that holds both decode rows and prefill rows runs the decode kernel
+ * on a stream the handle owns, forked from `stream` by an event before any of
+ * the call's work and joined back to it before the call's last kernel, so the
+ * call as a whole stays in `stream` order.
  * Returns KV_ERR_INVALID_ARG for a bad shape, a q_heads that is not a positive
  * multiple of kv_heads, or a bad n_new; KV_ERR_UNSUPPORTED when G > 128;
  * KV_ERR_WORKSPACE when the workspace is too small.

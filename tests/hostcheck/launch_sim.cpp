@@ -220,16 +220,22 @@ hipError_t launch_combine(int dtype, int head_dim, const CombineArgs &a, hipStre
     ++g_launches;
     const int64_t row_bytes = (int64_t)head_dim * (dtype == 0 ? 4 : 2);
     if (a.rows.blk0[a.rows.n_rows] != a.rows.total_blocks) err("combine: blk0 does not end at total_blocks");
+    const int DC = head_dim / 4;
     for (int blk = 0; blk < a.rows.total_blocks; ++blk) {
         const int r = find_row(a.rows.blk0, a.rows.n_rows, blk);
         const int local = blk - a.rows.blk0[r];
         const int cols = a.rows.cols[r], nsplit = a.rows.nsplit[r], n = a.rows.nnew[r];
         const int tq = cols / a.group;
         const int nq = (n + tq - 1) / tq;
-        const int kvh = local / nq, qtile = local % nq;
+        const int per_group = (cols * DC + 255) / 256;
+        const int grp = local / per_group, part = local % per_group;
+        const int kvh = grp / nq, qtile = grp % nq;
         if (kvh >= a.hkv || nsplit < 2) err("combine: block maps outside the row");
         const int64_t rec_first = a.rows.pbase[r] + (int64_t)((kvh * nq + qtile) * nsplit) * cols;
-        for (int col = 0; col < cols; ++col) {
+        for (int tid = 0; tid < 256; ++tid) {
+            const int task = part * 256 + tid;
+            if (task >= cols * DC) continue;
+            const int col = task / DC, d = (task % DC) * 4;
             const int t = qtile * tq + col / a.group;
             if (col >= tq * a.group || t >= n) continue;
             const int h = kvh * a.group + col % a.group;
@@ -238,26 +244,46 @@ hipError_t launch_combine(int dtype, int head_dim, const CombineArgs &a, hipStre
                 if (rs < 0 || rs >= a.records) err("combine: record out of range");
                 auto w = g_records.find(rs);
                 if (w == g_records.end() || w->second != 1) err("combine: partial not written exactly once");
-                access(a.ws_acc + rs * head_dim, head_dim * 4, "ws", "combine acc");
+                access(a.ws_acc + rs * head_dim + d, 16, "ws", "combine acc");
                 access(a.ws_ml + rs * 2, 8, "ws", "combine m,l");
             }
-            const char *o = (const char *)a.out + (((int64_t)a.rows.b[r] * a.hq + h) * a.T + t) * row_bytes;
-            access(o, row_bytes, "out", "combine out");
-            g_out_rows[(uintptr_t)o]++;
+            const char *o = (const char *)a.out + (((int64_t)a.rows.b[r] * a.hq + h) * a.T + t) * row_bytes + d * (dtype == 0 ? 4 : 2);
+            access(o, 4 * (dtype == 0 ? 4 : 2), "out", "combine out");
+            if (d == 0) g_out_rows[(uintptr_t)((const char *)a.out + (((int64_t)a.rows.b[r] * a.hq + h) * a.T + t) * row_bytes)]++;
         }
     }
     return hipSuccess;
 }
 
+// stream fork/join only orders work; the simulator runs launches in call order
+hipError_t side_stream_init(SideStream &s) {
+    s.side = reinterpret_cast<hipStream_t>(0x5);
+    return hipSuccess;
+}
+void side_stream_destroy(SideStream &s) { s = SideStream{}; }
+hipError_t side_stream_fork(SideStream &, hipStream_t) { return hipSuccess; }
+hipError_t side_stream_join(SideStream &, hipStream_t) { return hipSuccess; }
+
 hipError_t launch_zero_fill(const ZeroArgs &a, hipStream_t) {
     ++g_launches;
-    for (int r = 0; r < a.rows.n_rows; ++r)
-        for (int h = 0; h < a.hq; ++h)
-            for (int t = a.rows.nnew[r]; t < a.T; ++t) {
-                const char *o = (const char *)a.out + (((int64_t)a.rows.b[r] * a.hq + h) * a.T + t) * a.row_bytes;
-                access(o, a.row_bytes, "out", "zero fill");
-                g_out_rows[(uintptr_t)o]++;
-            }
+    // block-by-block, as the kernel maps block ids to slices
+    if (a.slices != (a.T * a.row_bytes + kZeroSlice - 1) / kZeroSlice) err("zero fill: slice count");
+    for (int64_t blk = 0; blk < (int64_t)a.rows.n_rows * a.hq * a.slices; ++blk) {
+        const int slice = (int)(blk % a.slices);
+        const int rh = (int)(blk / a.slices);
+        const int r = rh / a.hq, h = rh % a.hq;
+        const int64_t head_off = ((int64_t)a.rows.b[r] * a.hq + h) * a.T * a.row_bytes;
+        const int64_t lo = (int64_t)slice * kZeroSlice;
+        const int64_t begin = head_off + std::max(lo, (int64_t)a.rows.nnew[r] * a.row_bytes);
+        const int64_t end = head_off + std::min(lo + kZeroSlice, (int64_t)a.T * a.row_bytes);
+        for (int j = 0; j < kZeroSlice / 16; ++j) {
+            const int64_t off = head_off + lo + (int64_t)j * 16;
+            if (off < begin || off >= end) continue;
+            const char *o = (const char *)a.out + off;
+            access(o, 16, "out", "zero fill");
+            if ((off - head_off) % a.row_bytes == 0) g_out_rows[(uintptr_t)o]++;
+        }
+    }
     return hipSuccess;
 }
 
