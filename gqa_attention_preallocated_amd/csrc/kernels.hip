@@ -306,11 +306,12 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     unsigned char *lds = lds_all + wave * STAGE;
     const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, C);
 
-    // this wave's share of the item's keys (whole tiles)
-    const int tiles = (it.k_end - it.k_begin + KT - 1) / KT;
-    const int per_wave = (tiles + W - 1) / W;
-    const int w_begin = it.k_begin + wave * per_wave * KT;
-    const int w_end = imin(w_begin + per_wave * KT, it.k_end);
+    // this wave's share of the item's keys: every W-th 32-key tile from its
+    // own, so at any time the work group streams one contiguous run of K and
+    // one of V (fewer concurrent DRAM streams than a contiguous range per wave)
+    const int w_begin = it.k_begin + wave * KT;
+    const int w_end = it.k_end;
+    constexpr int step = W * KT;
 
     // ---- columns: absolute positions and Q operands (B of S^T)
     int pos[NSUB];
@@ -341,11 +342,10 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- prefetch: with two register sets the next two tiles are in flight
-    //      while one is computed (where registers allow), else the next one
-    constexpr int PF = (NSUB == 1 && O::kBytes == 2) ? 2 : 1;
-    vec kA[2][KC], kB[2][KC];
-    uint4 vA[VCH], vB[VCH];
+    // ---- prefetch: the next tile is in flight while one is computed (one
+    //      tile is 64 VGPRs a lane; a second set would halve the waves a CU holds)
+    vec kA[2][KC];
+    uint4 vA[VCH];
     auto load_tile = [&](vec (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     // before it need no mask ([MASK] "A strong answer", tile cases)
     const int pos_min = it.base + it.t0;
 
-    // compute the tile held in (kop, vreg), refilling the set with the tile PF ahead
+    // compute the tile held in (kop, vreg), refilling the set with the next tile
     auto process = [&](vec (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
         // V tile into this wave's LDS stage (row-major, padded)
 #pragma unroll
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
                 for (int kc = 0; kc < KC; ++kc) c = O::mma(kop[ks][kc], qop[s][kc], c);
                 sc[s][ks] = c;
             }
-        if (tile + PF * KT < w_end) load_tile(kop, vreg, tile + PF * KT);
+        if (tile + step < w_end) load_tile(kop, vreg, tile + step);
 
         // ---- mask (only tiles that straddle the diagonal or the range end),
         //      online softmax in log2 units
@@ -429,15 +429,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     };
 
     if (w_begin < w_end) load_tile(kA, vA, w_begin);
-    if constexpr (PF == 2) {
-        if (w_begin + KT < w_end) load_tile(kB, vB, w_begin + KT);
-        for (int tile = w_begin; tile < w_end; tile += 2 * KT) {
-            process(kA, vA, tile);
-            if (tile + KT < w_end) process(kB, vB, tile + KT);
-        }
-    } else {
-        for (int tile = w_begin; tile < w_end; tile += KT) process(kA, vA, tile);
-    }
+    for (int tile = w_begin; tile < w_end; tile += step) process(kA, vA, tile);
 
     // ---- merge the W waves' partials in LDS, one 16-column subtile at a time
     float *part = reinterpret_cast<float *>(lds_all);                 // [W][16][PSTR]
