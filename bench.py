@@ -100,7 +100,7 @@ def run_decode(torch, steps, warmup):
     from gqa_attention_preallocated_amd import KVCache, gqa_attention
     import workloads as W
     sh = W.LLAMA8B_DECODE
-    seed, cached = 1, 4096
+    seed, cached = DECODE_SEED, DECODE_CACHED
     B, hq, hkv, d = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim
     # two caches used in turn: each step streams 537 MB that the previous step
     # did not touch, so the 256 MB last-level cache cannot serve it
@@ -169,7 +169,7 @@ def run_decode(torch, steps, warmup):
     att_b = attention_bytes(lens_after, n, hq, hkv, d, 1)
     app_b = 2 * 2 * sum(n) * hkv * d * 2
     return {
-        "shape": sh, "seed": seed, "hist": hist, "q": q, "k": k, "v": v,
+        "shape": sh, "seed": seed, "q": q, "k": k, "v": v,
         "wall_s": wall, "att_ms_avg": att_avg, "att_ms_p50": att_ms[len(att_ms) // 2],
         "att_ms_p10": att_ms[len(att_ms) // 10], "att_ms_p90": att_ms[(9 * len(att_ms)) // 10],
         "att_bytes": att_b, "append_bytes": app_b, "lens_after": lens_after,
@@ -300,37 +300,96 @@ def run_ragged(torch, seed=4, reps=20):
             "config": {"workload": sh.name, "seed": seed, "batch": B, "T": T, "sum_lens": int(sum(after))}}
 
 
-def cpu_baseline(res, max_rows=32, budget_s=20.0):
-    """The float64 oracle on the host, one decode step over as many rows as fit the budget."""
+DECODE_SEED, DECODE_CACHED = 1, 4096
+
+
+def _oracle_worker(rank, nproc, reps, budget_s, barrier, results):
+    """One host process of the CPU baseline: regenerate this worker's rows of the
+    decode step from the seeded generators, wait for the others, then run the
+    float64 oracle over them `reps` times on one thread, or until budget_s of
+    compute has passed (checked after each row)."""
     try:
         from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
     except ImportError:       # pragma: no cover
-        threadpool_limits = None
+        pass
+    import workloads as W
     from oracle import direct
-    sh = res["shape"]
-    hq, hkv, d = sh.q_heads, sh.kv_heads, sh.head_dim
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    rows_done = 0
+    sh = W.LLAMA8B_DECODE
+    rows = list(range(rank, sh.batch, nproc))
+    n = [1] * sh.batch
+    q, k, v = W.step_inputs(sh, DECODE_SEED, 10_000, 1, n, pad="normal")
+    data = []
+    for b in rows:
+        kh, vh = W.prefix_kv(sh, DECODE_SEED, b, 0, DECODE_CACHED)
+        data.append((b, np.concatenate([kh, k[b, :, :1]], axis=1), np.concatenate([vh, v[b, :, :1]], axis=1)))
+    # one untimed call: the first in a fresh interpreter pays one-off set-up (about 2 s)
+    b0, k0, v0 = data[0]
+    direct.attention_row(k0, v0, k0.shape[1], 1, q[b0], "bf16", [(0, 0)])
+    barrier.wait()
     t0 = time.perf_counter()
-    try:
-        if ctx is not None:
-            ctx.__enter__()
-        for b in range(min(max_rows, sh.batch)):
-            kr = np.concatenate([h[0][b] for h in res["hist"]] + [res["k"][b, :, :1]], axis=1)
-            vr = np.concatenate([h[1][b] for h in res["hist"]] + [res["v"][b, :, :1]], axis=1)
-            direct.attention_row(kr, vr, kr.shape[1], 1, res["q"][b], "bf16", [(h, 0) for h in range(hq)])
-            rows_done += 1
+    done = 0
+    for _ in range(reps):
+        for b, kr, vr in data:
+            direct.attention_row(kr, vr, kr.shape[1], 1, q[b], "bf16", [(h, 0) for h in range(sh.q_heads)])
+            done += 1
             if time.perf_counter() - t0 > budget_s:
                 break
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    dt = time.perf_counter() - t0
-    b_per_row = attention_bytes([res["lens_after"][0]], [1], hq, hkv, d, 1)
-    gbs = rows_done * b_per_row / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows_done} of {sh.batch} rows of one decode step (all {hq} heads), "
-                      f"{dt:.2f} s, float64 numpy, 1 thread"}
+        else:
+            continue
+        break
+    t1 = time.perf_counter()
+    results.put((rank, done, t0, t1))
+
+
+def cpu_baseline(reps=20, budget_s=1.5, max_procs=16):
+    """The float64 oracle on the host: the whole decode step (32 rows x 32 heads)
+    up to `reps` times, rows dealt over one single-threaded process per host core
+    (at most max_procs), each stopping after budget_s of compute. Runs before
+    this process touches the GPU; the workers are fresh interpreters that never
+    do."""
+    import multiprocessing as mp
+    import workloads as W
+    sh = W.LLAMA8B_DECODE
+    nproc = max(1, min(max_procs, len(os.sched_getaffinity(0)), sh.batch))
+    ctx = mp.get_context("spawn")
+    barrier, results = ctx.Barrier(nproc), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(r, nproc, reps, budget_s, barrier, results)) for r in range(nproc)]
+    for pr in procs:
+        pr.start()
+    got = [results.get(timeout=600) for _ in procs]
+    for pr in procs:
+        pr.join()
+    rows = sum(g[1] for g in got)
+    wall = max(g[3] for g in got) - min(g[2] for g in got)
+    cpu_s = sum(g[3] - g[2] for g in got)
+    b_per_row = attention_bytes([DECODE_CACHED + 1], [1], sh.q_heads, sh.kv_heads, sh.head_dim, 1)
+    return {"value": round(rows * b_per_row / wall / 1e9, 4), "unit": "GB/s", "cores": nproc, "kind": "oracle",
+            "sample": f"{rows} row-steps of the decode step (each: one row, all 32 heads, 4,097 keys; "
+                      f"rows dealt round-robin, at most {reps} passes over the 32 rows), "
+                      f"{cpu_s:.1f} s of CPU over {nproc} single-threaded processes, {wall:.2f} s wall, float64 numpy"}
+
+
+def run_append(torch, reps=20):
+    """Append bandwidth: B=32 rows, Llama KV shape, T in {1, 512, 2048, 4096} new tokens per row."""
+    from gqa_attention_preallocated_amd import KVCache
+    B, hkv, d = 32, 8, 128
+    cache = KVCache(B, hkv, 8192, d, device_lens=False)
+    g = torch.Generator(device="cuda").manual_seed(9)
+    out = {}
+    for T in (1, 512, 2048, 4096):
+        k = torch.randn(B, hkv, T, d, device="cuda", generator=g).to(torch.bfloat16)
+        v = torch.randn(B, hkv, T, d, device="cuda", generator=g).to(torch.bfloat16)
+        n = [T] * B
+
+        def call(i):
+            cache.append(k, v, n)
+            cache.truncate(0)
+        t = _time_calls(torch, call, reps)
+        nbytes = 2 * 2 * B * hkv * T * d * 2          # K and V, read once and written once
+        out[str(T)] = {"us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1), "bytes": nbytes}
+    return {"metric": "append HBM GB/s (K+V read + written)", "unit": "GB/s", "by_T": out,
+            "config": {"workload": "llama8b_append_b32", "batch": B, "kv_heads": hkv, "head_dim": d}}
 
 
 def main():
@@ -340,7 +399,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "cpu"], default=None,
                     help="time one workload only (for profiling); prints its own JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one plain 256 MiB device copy (counter calibration)")
@@ -349,6 +408,13 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    if args.only == "cpu":
+        print(json.dumps({"cpu_baseline": cpu_baseline()}), flush=True)
+        return
+    # the CPU baseline runs first, while no GPU context exists in this process
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        cpu = cpu_baseline()
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -363,8 +429,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if args.only in ("prefill", "verify", "ragged"):
-        fn = {"prefill": run_prefill, "verify": run_verify, "ragged": run_ragged}[args.only]
+    if args.only == "ragged":
+        print(json.dumps({"ragged": [run_ragged(torch, seed) for seed in (4, 5, 6)]}), flush=True)
+        return
+    if args.only in ("prefill", "verify", "append"):
+        fn = {"prefill": run_prefill, "verify": run_verify, "append": run_append}[args.only]
         print(json.dumps({args.only: fn(torch)}), flush=True)
         return
     res = run_decode(torch, args.steps, args.warmup)
@@ -400,8 +469,8 @@ def main():
     }
     if not args.no_prefill:
         line["prefill"] = run_prefill(torch)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(res)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
