@@ -45,6 +45,26 @@ __device__ inline uint4 load_stream(const void *p) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// Buffer view of `bytes` bytes from `base`: a load at a byte offset at or past
+// the end returns zeros without touching memory, so a tile that runs past the
+// valid keys needs no per-lane predicate. The last descriptor word is the
+// raw (untyped, unswizzled) buffer setting of CDNA parts.
+// `base` and `bytes` must be the same in every lane of the wave (they are
+// moved to scalar registers).
+__device__ inline __amdgpu_buffer_rsrc_t buffer_view(const void *base, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *p = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// 16 bytes at byte offset `off` of a buffer view, non-temporal (cache policy nt)
+__device__ inline uint4 buffer_load_stream(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // ---------------------------------------------------------------------------
 // element traits: 8-element MFMA operands and the 16x16 product
 // ---------------------------------------------------------------------------
@@ -54,6 +74,9 @@ template <> struct Op<bf16_t> {
     using vec = bf16x8;
     static constexpr int kBytes = 2;
     __device__ static inline vec zero() { return __builtin_bit_cast(vec, make_uint4(0, 0, 0, 0)); }
+    __device__ static inline vec ones() {      // bf16 1.0 = 0x3f80 in every slot
+        return __builtin_bit_cast(vec, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+    }
     __device__ static inline vec gload(const bf16_t *p) {
         return __builtin_bit_cast(vec, *reinterpret_cast<const uint4 *>(p));
     }
@@ -65,6 +88,16 @@ template <> struct Op<bf16_t> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
     __device__ static inline vec from_f32(const f32x8 &x) { return __builtin_convertvector(x, vec); }
+    // elements j, j+1 (j even) of an operand from two floats (one packed convert)
+    __device__ static inline void set_pair(vec &v, int j, float x, float y) {
+        typedef __attribute__((ext_vector_type(2))) float f32x2;
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+        const bf16x2 w = __builtin_convertvector((f32x2){x, y}, bf16x2);
+        uint4 u = __builtin_bit_cast(uint4, v);
+        const uint32_t bits = __builtin_bit_cast(uint32_t, w);
+        if (j == 0) u.x = bits; else if (j == 2) u.y = bits; else if (j == 4) u.z = bits; else u.w = bits;
+        v = __builtin_bit_cast(vec, u);
+    }
     // LDS row stride for a K/V tile: 32 bytes of padding put the rows that one
     // transposed read touches on disjoint banks
     static constexpr int kPad = 32;
@@ -96,6 +129,7 @@ template <> struct Op<float> {
     using vec = f32x8;
     static constexpr int kBytes = 4;
     __device__ static inline vec zero() { return vec{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}; }
+    __device__ static inline vec ones() { return vec{1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f}; }
     __device__ static inline vec gload(const float *p) {
         float4 a = reinterpret_cast<const float4 *>(p)[0];
         float4 b = reinterpret_cast<const float4 *>(p)[1];
@@ -117,6 +151,10 @@ template <> struct Op<float> {
         return c;
     }
     __device__ static inline vec from_f32(const f32x8 &x) { return x; }
+    __device__ static inline void set_pair(vec &v, int j, float x, float y) {
+        v[j] = x;
+        v[j + 1] = y;
+    }
     static constexpr int kPad = 16;
     // A operand of O^T += V^T P^T (see the bf16 version): 8 single-element reads
     __device__ static inline vec vt_operand(const unsigned char *tile, int rs, int key0, int d0, int lane) {
@@ -248,6 +286,8 @@ __device__ inline void softmax_step(const float (&v)[8], float c, ColState &st, 
 
 // The same step over the N = 16 scores of two 32-key chunks (v[0..7] chunk
 // 0, v[8..15] chunk 1, each in the layout above): one max, one rescale test.
+// The running sum is not kept here: the caller accumulates it on the matrix
+// core as an extra output block (acc[NB - 1]), so the rescale covers it too.
 template <int NB, int N>
 __device__ inline void softmax_tile(const float (&v)[N], float c, ColState &st, f32x4 (&acc)[NB], f32x8 &p0,
                                     f32x8 &p1) {
@@ -256,22 +296,17 @@ __device__ inline void softmax_tile(const float (&v)[N], float c, ColState &st, 
     const float tmax = wave_max_across_groups(fmaxf(t0, t1)) * c;
     if (tmax > st.m + kRescaleLog2) {
         const float alpha = fast_exp2(st.m - tmax);
-        st.l *= alpha;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
         st.m = tmax;
     }
     const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
-    float lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         p0[j] = fast_exp2(fmaf(v[j], c, -m_use));
         p1[j] = fast_exp2(fmaf(v[8 + j], c, -m_use));
-        lsum += p0[j] + p1[j];
     }
-    st.l += lsum;
 }
-
 
 // ---------------------------------------------------------------------------
 // split-K decode / verify kernel. One work group of W waves per work item
@@ -496,7 +531,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     constexpr int CPK = ROWB / 16;
     constexpr int TILE_BYTES = KT * RS;
     constexpr int PCH = (KT * CPK + 255) / 256;   // 16-byte chunks per thread per tensor
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][TILE_BYTES];   // [buf][K|V]
+    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][TILE_BYTES];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -537,112 +573,251 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const unsigned char *vbase = reinterpret_cast<const unsigned char *>(
         reinterpret_cast<const E *>(a.v) + head * a.max_len * D);
 
-    f32x4 acc[NS][NB];
+    // acc[s][0..NB-1]: O^T rows; acc[s][NB]: a 16-row block whose A operand is
+    // all ones, so each of its rows is the column's running sum of p (the
+    // same rounded p the output rows use)
+    f32x4 acc[NS][NB + 1];
     ColState st[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         st[s].m = -INFINITY;
         st[s].l = 0.f;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb <= NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const vec ones = O::ones();
     uint4 kreg[PCH], vreg[PCH];
-    auto load_tile = [&](int tile) {
+    // thread chunk c = tid + 256 i is key c / CPK, bytes (c % CPK) * 16.. of the
+    // tile: byte offset c * 16 from the tile's first key. Keys at or past
+    // k_end (and chunks past the tile) fall outside the view and read as zero.
+    auto load = [&](uint4 (&reg)[PCH], const unsigned char *base, int tile) {
+        const __amdgpu_buffer_rsrc_t r = buffer_view(base + (int64_t)tile * ROWB, imin(it.k_end - tile, KT) * ROWB);
+#pragma unroll
+        for (int i = 0; i < PCH; ++i) reg[i] = buffer_load_stream(r, (tid + 256 * i) * 16);
+    };
+    auto store = [&](const uint4 (&reg)[PCH], unsigned char *dst) {
 #pragma unroll
         for (int i = 0; i < PCH; ++i) {
             const int c = tid + 256 * i;
-            const int key = c / CPK, part = c % CPK;
-            const bool ok = (c < KT * CPK) && (tile + key < it.k_end);
-            const int64_t goff = (int64_t)(tile + key) * ROWB + part * 16;
-            kreg[i] = ok ? load_stream(kbase + goff) : make_uint4(0, 0, 0, 0);
-            vreg[i] = ok ? load_stream(vbase + goff) : make_uint4(0, 0, 0, 0);
+            if ((KT * CPK) % 256 == 0 || c < KT * CPK)
+                *reinterpret_cast<uint4 *>(dst + (c / CPK) * RS + (c % CPK) * 16) = reg[i];
         }
     };
-    auto store_tile = [&](int buf) {
+    // S^T of one 64-key tile for the wave's 32 columns (32 MFMAs)
+    auto scores = [&](const unsigned char *kl, f32x4 (&sc)[2][NS][2]) {
 #pragma unroll
-        for (int i = 0; i < PCH; ++i) {
-            const int c = tid + 256 * i;
-            if (c < KT * CPK) {
-                const int key = c / CPK, part = c % CPK;
-                *reinterpret_cast<uint4 *>(&lds[buf][0][key * RS + part * 16]) = kreg[i];
-                *reinterpret_cast<uint4 *>(&lds[buf][1][key * RS + part * 16]) = vreg[i];
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int krow = ch * 32 + ks * 16 + lr;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) sc[ch][s][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const int d0 = kc * 32 + lg * 8;
+                    const vec kv = (d0 < D) ? O::lds_load(kl + krow * RS + d0 * O::kBytes) : O::zero();
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) sc[ch][s][ks] = O::mma(kv, qop[s][kc], sc[ch][s][ks]);
+                }
             }
-        }
     };
 
-    if (it.k_begin < it.k_end) load_tile(it.k_begin);
-    int buf = 0;
-    for (int tile = it.k_begin; tile < it.k_end; tile += KT) {
-        store_tile(buf);
-        __syncthreads();
-        if (tile + KT < it.k_end) load_tile(tile + KT);
-
-        if (tile <= wave_pos_max) {
-            const unsigned char *kl = lds[buf][0];
-            const unsigned char *vl = lds[buf][1];
-            const bool need_mask = (tile + KT > it.k_end) || (tile + KT - 1 > wave_pos_min);
-            // scores of both 32-key chunks first, so the softmax of one chunk
-            // can issue while the matrix core still works on the next
-            f32x4 sc[2][NS][2];
-            __builtin_amdgcn_s_setprio(1);    // matrix phase first: the other wave on the SIMD takes the VALU
+    // O^T += V^T P^T for one staged V tile, and the row sums on the all-ones block
+    auto pv = [&](const unsigned char *vl, const vec (&pb)[2][NS]) {
 #pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
+        for (int ch = 0; ch < 2; ++ch) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const vec vt = O::vt_operand(vl, RS, ch * 32, nb * 16, lane);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt, pb[ch][s], acc[s][nb]);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, pb[ch][s], acc[s][NB]);
+        }
+    };
+    // straddling tiles only: key (ch, ks, j) = tile + ch*32 + ks*16 + 4*lg + j
+    // is visible iff it is <= the column's position and < the split end
+    auto mask = [&](int tile, f32x4 (&sc)[2][NS][2]) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int lim = imin(pos[s] + 1, it.k_end) - (tile + lg * 4);
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        sc[ch][s][ks][j] = (ch * 32 + ks * 16 + j < lim) ? sc[ch][s][ks][j] : -INFINITY;
+        }
+    };
+    // column max of the tile in log2 units
+    auto tile_max = [&](const f32x4 (&sc)[2][NS][2], float (&tmax)[NS]) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float t = -INFINITY;
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    t = fmaxf(t, fmaxf(fmaxf(sc[ch][s][ks][0], sc[ch][s][ks][1]),
+                                       fmaxf(sc[ch][s][ks][2], sc[ch][s][ks][3])));
+            tmax[s] = wave_max_across_groups(t) * a.scale_log2;
+        }
+    };
+    // Software pipeline over the item's key tiles, two matrix phases per tile,
+    // each interleaved by hand with independent VALU work of the same wave so
+    // that the wave issues VALU while its MFMAs occupy the matrix core:
+    //   phase X: O^T += V(i-1)^T P(i-1)^T   beside   the column max of tile i
+    //   phase Y: scores of tile i+1         beside   the probabilities of tile i
+    // Each phase is a fixed sequence of steps (2 MFMAs, their LDS operands
+    // fetched ahead, a few VALU ops) fenced with sched_barrier.
+    // Staging: iteration i writes K(i+1) and V(i-1) to LDS, then one barrier.
+    // Its stores run before that barrier, so a slower wave may still be in
+    // iteration i-1, which reads K(i) and V(i-2); the slots written hold
+    // K(i-1) and V(i-3), last read in iteration i-2. The tile loads for those
+    // stores (K(i+2), V(i)) are issued right after the barrier. V(last) is
+    // staged after the loop behind its own barrier. A wave computes tiles
+    // 0..wave_last only (tiles past its last query are skipped; it still
+    // takes part in staging and barriers).
+    const int ntiles = (it.k_end - it.k_begin + KT - 1) / KT;     // 0 for an empty item
+    const int wave_last = wave_pos_max < it.k_begin ? -1 : imin(ntiles - 1, (wave_pos_max - it.k_begin) / KT);
+    f32x4 sc[2][NS][2];
+    vec pb[2][NS];
+
+    // phase X: 2*NB steps of PV (ch = g / NB, nb = g % NB, both subtiles), then
+    // the two all-ones MFMAs per chunk; VALU: the max tree of tile i as ten
+    // tasks (per subtile: four quarter maxima, then the column max), task t
+    // at step t * NSX / 10 so every task runs after the ones it needs
+    auto phase_x = [&](const unsigned char *vp, float (&tmax)[NS]) {
+        constexpr int NSX = 2 * NB;
+        vec vt[2];
+        vt[0] = O::vt_operand(vp, RS, 0, 0, lane);
+        float part[NS][4];
+#pragma unroll
+        for (int g = 0; g < NSX; ++g) {
+            const int ch = g / NB, nb = g % NB;
+            if (g + 1 < NSX) vt[(g + 1) & 1] = O::vt_operand(vp, RS, ((g + 1) / NB) * 32, ((g + 1) % NB) * 16, lane);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt[g & 1], pb[ch][s], acc[s][nb]);
+#pragma unroll
+            for (int t = 0; t < 10; ++t) {
+                if (t * NSX / 10 != g) continue;
+                if (t < 8) {
+                    const int s = t >> 2, q = t & 3;      // quarter q = (ch, ks) block
+                    const f32x4 x = sc[q >> 1][s][q & 1];
+                    part[s][q] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+                } else {
+                    const int s = t - 8;
+                    const float m4 = fmaxf(fmaxf(part[s][0], part[s][1]), fmaxf(part[s][2], part[s][3]));
+                    tmax[s] = wave_max_across_groups(m4) * a.scale_log2;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, pb[ch][s], acc[s][NB]);
+    };
+    // phase Y: 16 steps of scores for tile i+1 (ch = g / 8, ks = (g / 4) % 2,
+    // kc = g % 4, both subtiles; steps with kc >= KC issue no MFMA); VALU: 2
+    // of the 32 probabilities of tile i per step, packed into the operand
+    auto phase_y = [&](const unsigned char *kn, const float (&m_use)[NS], f32x4 (&scn)[2][NS][2]) {
+        auto kop = [&](int g) {
+            const int krow = (g >> 3) * 32 + ((g >> 2) & 1) * 16 + lr;
+            const int d0 = (g & 3) * 32 + lg * 8;
+            return (d0 < D) ? O::lds_load(kn + krow * RS + d0 * O::kBytes) : O::zero();
+        };
+        vec kv[3];
+        kv[0] = kop(0);
+        kv[1] = kop(1);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            const int ch = g >> 3, ks = (g >> 2) & 1, kc = g & 3;
+            if (g + 2 < 16) kv[(g + 2) % 3] = kop(g + 2);
+            if (kc < KC) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    sc[ch][s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    sc[ch][s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int krow = ch * 32 + ks * 16 + lr;
-#pragma unroll
-                    for (int kc = 0; kc < KC; ++kc) {
-                        const int d0 = kc * 32 + lg * 8;
-                        const vec kv = (d0 < D) ? O::lds_load(kl + krow * RS + d0 * O::kBytes) : O::zero();
-#pragma unroll
-                        for (int s = 0; s < NS; ++s) sc[ch][s][ks] = O::mma(kv, qop[s][kc], sc[ch][s][ks]);
-                    }
+                    const f32x4 c0 = kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : scn[ch][s][ks];
+                    scn[ch][s][ks] = O::mma(kv[g % 3], qop[s][kc], c0);
                 }
             }
-            // one max and one rescale decision per column for the whole tile;
-            // the exponentials and both chunks' O^T products then form one
-            // branch-free block the scheduler can interleave
-            f32x8 p[2][NS];
-            __builtin_amdgcn_s_setprio(0);
+            // probabilities: step g covers (ch', s') = (g / 8, (g / 4) % 2), elements 2 (g % 4) .. +1
+            {
+                const int pc = g >> 3, ps = (g >> 2) & 1, j = (g & 3) * 2;
+                O::set_pair(pb[pc][ps], j, fast_exp2(fmaf(sc[pc][ps][j >> 2][j & 3], a.scale_log2, -m_use[ps])),
+                            fast_exp2(fmaf(sc[pc][ps][(j + 1) >> 2][(j + 1) & 3], a.scale_log2, -m_use[ps])));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto finish_max = [&](const float (&tmax)[NS], float (&m_use)[NS]) {
+        // move the reference max where a column's max outgrew it by more than
+        // kRescaleLog2 (st.m = -inf: the first visible key sets it; alpha is
+        // then 0 and acc is still 0)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (tmax[s] > st[s].m + kRescaleLog2) {
+                const float alpha = fast_exp2(st[s].m - tmax[s]);
+#pragma unroll
+                for (int nb = 0; nb <= NB; ++nb) acc[s][nb] *= alpha;
+                st[s].m = tmax[s];
+            }
+            m_use[s] = (st[s].m == -INFINITY) ? 0.f : st[s].m;    // no key seen yet: every p is 0
+        }
+    };
+
+    if (ntiles > 0) {
+        load(kreg, kbase, it.k_begin);
+        store(kreg, lds_k[0]);
+        __syncthreads();
+        if (ntiles > 1) load(kreg, kbase, it.k_begin + KT);
+        load(vreg, vbase, it.k_begin);
+        if (wave_last >= 0) scores(lds_k[0], sc);
+    }
+    for (int i = 0; i < ntiles; ++i) {
+        const int tile = it.k_begin + i * KT;
+        const bool has_next = i + 1 < ntiles;          // uniform over the work group
+        const unsigned char *kn = lds_k[(i + 1) & 1];  // K(i+1)
+        const unsigned char *vp = lds_v[(i + 1) & 1];  // V(i-1)
+        if (has_next) store(kreg, lds_k[(i + 1) & 1]);
+        if (i > 0) store(vreg, lds_v[(i + 1) & 1]);
+        __syncthreads();
+        if (i + 2 < ntiles) load(kreg, kbase, tile + 2 * KT);
+        if (i > 0) load(vreg, vbase, tile);              // V(0) came with the prologue
+        if (i > wave_last) {
+            if (i == wave_last + 1 && wave_last >= 0) pv(vp, pb);   // the last tile this wave computed
+            continue;
+        }
+        if ((tile + KT > it.k_end) || (tile + KT - 1 > wave_pos_min)) mask(tile, sc);   // uniform over the wave
+
+        float tmax[NS], m_use[NS];
+        __builtin_amdgcn_s_setprio(1);
+        if (i > 0) phase_x(vp, tmax);
+        else tile_max(sc, tmax);
+        finish_max(tmax, m_use);
+        // on the last tile the K slot holds an older tile: those scores are never used
+        f32x4 scn[2][NS][2];
+        phase_y(kn, m_use, scn);
+        __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                float v[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) v[j] = sc[j >> 3][s][(j >> 2) & 1][j & 3];
-                if (need_mask) {                  // uniform over the wave
-                    // key (ch, j) is visible iff it is <= pos and < the split end
-                    const int lim = imin(pos[s] + 1, it.k_end) - (tile + lg * 4);
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int off = (j >> 3) * 32 + ((j >> 2) & 1) * 16 + (j & 3);
-                        v[j] = (off < lim) ? v[j] : -INFINITY;
-                    }
-                }
-                softmax_tile<NB, 16>(v, a.scale_log2, st[s], acc[s], p[0][s], p[1][s]);
+                sc[ch][s][0] = scn[ch][s][0];
+                sc[ch][s][1] = scn[ch][s][1];
             }
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const vec vt = O::vt_operand(vl, RS, ch * 32, nb * 16, lane);
-#pragma unroll
-                    for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt, O::from_f32(p[ch][s]), acc[s][nb]);
-                }
-            }
-            __builtin_amdgcn_s_setprio(0);
-        }
-        buf ^= 1;
+    }
+    if (ntiles > 0) {
+        store(vreg, lds_v[(ntiles - 1) & 1]);            // V(last)
+        __syncthreads();
+        if (wave_last == ntiles - 1) pv(lds_v[(ntiles - 1) & 1], pb);
     }
 
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const float l = wave_sum_across_groups(st[s].l);
+        const float l = acc[s][NB][0];
         const int col = wave * 32 + s * 16 + lr;
         if (pos[s] < 0) continue;
         if (it.rec0 < 0) {

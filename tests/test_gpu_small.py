@@ -106,6 +106,20 @@ def test_split_count_invariance():
         assert np.abs(o - outs[0]).max() <= 1e-5
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_prefill_many_key_tiles(dt, d):
+    """The chunked-prefill kernel over items of many 64-key tiles (its staging
+    ring and the split of work between waves), at every head dim: a long
+    row fed 96 queries at a time beside two short rows that stop growing,
+    with the kernel forced and with one split per row (final lengths 1,968, 131, 71)."""
+    shape = W.Shape("tiles", dt, 3, 16, 2, d, 2048)
+    calls = [{"T": 96, "n_new": [96, 96, 70]}, {"T": 64, "n_new": [64, 34, 0]},
+             {"T": 96, "n_new": [96, 0, 0]}] + [{"T": 96, "n_new": [96, 0, 0]}] * 17 + \
+            [{"T": 96, "n_new": [80, 1, 1]}]
+    _run_schedule(shape, calls, 11, (2, 4096), check_bytes=False)
+
+
 def test_nan_in_padding_and_stale_tail_never_leaks():
     """NaN in padded q/k/v slots and in the cache past each row's length must not
     reach the output (stale slots are never read)."""
