@@ -14,9 +14,11 @@ check it against the pages by eye:
   * ``vectorised`` -- a second, independently written formulation (grouped
                       reshape, an index-arithmetic mask, guarded softmax),
                       used to cross-check ``direct``.
+  * ``window``     -- sliding-window attention over a ring-buffer cache whose
+                      slots store the absolute positions they hold.
 
 Where the pages are silent or disagree, the reading taken is stated in the
 docstring of the function that depends on it.
 """
 
-from . import direct, vectorised  # noqa: F401
+from . import direct, vectorised, window  # noqa: F401
