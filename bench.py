@@ -277,6 +277,35 @@ def run_verify(torch, reps=30):
             "config": {"workload": sh.name, "batch": B, "T": 4, "keys": 4096}}
 
 
+def run_window(torch, reps=30):
+    """Sliding-window decode: B=32 rows, a 4,096-key window over an 8,192-slot ring
+    after 20,000 tokens (the ring has wrapped twice), T=1. Two caches in turn."""
+    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    import workloads as W
+    sh = W.LLAMA8B_WINDOW_DECODE
+    B, hq, hkv, d, C = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim, sh.max_len
+    win, L = sh.notes["window"], sh.notes["cached"]
+    caches = [KVCache(B, hkv, C, d, device_lens=False, window=win) for _ in range(2)]
+    g = torch.Generator(device="cuda").manual_seed(11)
+    for c in caches:
+        done = 0
+        while done < L + 1:
+            n = min(4096, L + 1 - done)
+            x = (torch.randn(B, hkv, n, d, device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+            c.append(x, x, [n] * B)
+            done += n
+    q = (torch.randn(B, hq, 1, d, device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    n = [1] * B
+    ws = torch.zeros(max(max(c.workspace_bytes(hq, 1, n) for c in caches), 256), dtype=torch.uint8, device="cuda")
+    t = _time_calls(torch, lambda i: gqa_attention(q, caches[i & 1], n, out=out, workspace=ws), reps)
+    # live K+V of the window (4,096 keys per row), q and out
+    nbytes = B * win * hkv * d * 2 * 2 + 2 * B * hq * d * 2
+    return {"metric": "sliding-window decode attention HBM GB/s", "value": round(nbytes / t / 1e9, 2), "unit": "GB/s",
+            "frac_of_8TBs": round(nbytes / t / 8e12, 4), "ms": round(t * 1e3, 5), "bytes": nbytes,
+            "config": {"workload": sh.name, "batch": B, "window": win, "ring_slots": C, "position": L, "T": 1}}
+
+
 def run_ragged(torch, seed=4, reps=20):
     """Ragged batch: 64 rows, log-uniform lengths in [1, 32000], n_new in {0, 1, 4, 256}, T=256."""
     from gqa_attention_preallocated_amd import KVCache, gqa_attention
@@ -404,7 +433,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "cpu"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "window", "cpu"],
+                    default=None,
                     help="time one workload only (for profiling); prints its own JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run one plain 256 MiB device copy (counter calibration)")
@@ -437,8 +467,8 @@ def main():
     if args.only == "ragged":
         print(json.dumps({"ragged": [run_ragged(torch, seed) for seed in (4, 5, 6)]}), flush=True)
         return
-    if args.only in ("prefill", "verify", "append"):
-        fn = {"prefill": run_prefill, "verify": run_verify, "append": run_append}[args.only]
+    if args.only in ("prefill", "verify", "append", "window"):
+        fn = {"prefill": run_prefill, "verify": run_verify, "append": run_append, "window": run_window}[args.only]
         print(json.dumps({args.only: fn(torch)}), flush=True)
         return
     res = run_decode(torch, args.steps, args.warmup)

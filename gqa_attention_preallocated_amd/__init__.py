@@ -55,10 +55,15 @@ class KVCache:
     pointers never change); ``lens`` is the host copy of the per-row lengths and
     ``lens_dev`` the device copy the library keeps in stream order (None with
     ``device_lens=False``: then a rollback is host-only bookkeeping).
+
+    With ``window=W`` the cache is a ring of ``max_len`` slots per row (a
+    multiple of 64) that keeps only the latest tokens, and attention sees the
+    last W positions ([MASK] "A strong answer", the reversal); lengths are then
+    absolute positions and may exceed ``max_len``.
     """
 
     def __init__(self, batch, kv_heads, max_len, head_dim, dtype=torch.bfloat16, device="cuda",
-                 device_lens=True):
+                 device_lens=True, window=None):
         if dtype not in _DTYPES:
             raise ValueError(f"dtype {dtype} not supported (float32 or bfloat16)")
         self._lib = _lib.load()
@@ -71,14 +76,18 @@ class KVCache:
         self.lens_dev = torch.zeros(max(batch, 1), dtype=torch.int32, device=device) if device_lens else None
         self.dtype = dtype
         self.batch, self.kv_heads, self.max_len, self.head_dim = shape
+        self.window = window
         self._ws = None
         h = ctypes.c_void_p()
+        bufs = (ctypes.c_void_p(self.k.data_ptr()), ctypes.c_void_p(self.v.data_ptr()),
+                ctypes.c_void_p(self.lens_dev.data_ptr() if device_lens else 0))
         with torch.cuda.device(device):
-            st = self._lib.kv_cache_create(batch, kv_heads, max_len, head_dim, _DTYPES[dtype],
-                                           ctypes.c_void_p(self.k.data_ptr()),
-                                           ctypes.c_void_p(self.v.data_ptr()),
-                                           ctypes.c_void_p(self.lens_dev.data_ptr() if device_lens else 0),
-                                           _stream_ptr(), ctypes.byref(h))
+            if window is None:
+                st = self._lib.kv_cache_create(batch, kv_heads, max_len, head_dim, _DTYPES[dtype], *bufs,
+                                               _stream_ptr(), ctypes.byref(h))
+            else:
+                st = self._lib.kv_cache_create_ring(batch, kv_heads, max_len, head_dim, _DTYPES[dtype],
+                                                    int(window), *bufs, _stream_ptr(), ctypes.byref(h))
         _lib.check(st, self._lib)
         self._h = h
 

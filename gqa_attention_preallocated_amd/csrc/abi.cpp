@@ -21,6 +21,7 @@
 #include <string>
 #include <vector>
 
+#include "indexing.h"
 #include "internal.h"
 
 using namespace gqakv;
@@ -34,6 +35,8 @@ struct kv_cache {
     std::vector<int32_t> lens;   // host copy, authoritative, updated at enqueue
     int32_t path_policy = 0;     // 0 auto, 1 split-K decode kernel, 2 prefill kernel
     int32_t keys_per_split = 0;  // 0 auto
+    bool ring = false;           // token p in slot p mod max_len; lens are absolute positions
+    int32_t window = kNoWindow;  // a query at p sees keys p - window < j <= p
     SideStream side;             // created on the first mixed decode + prefill call
 };
 
@@ -84,6 +87,15 @@ struct Plan {
     std::vector<int32_t> pad_rows;     // rows with padded slots (n_new < T), zero-filled
 };
 
+// Keys of query tile qt of a row (len keys after the append, n new queries,
+// tq queries per tile): from the window's start for the tile's first query
+// (range_start) to the tile's last query. Without a window, base + t_end.
+int64_t tile_span(int32_t len, int32_t n, int tq, int qt, int32_t window) {
+    const int base = len - n, t0 = qt * tq;
+    const int hi = base + std::min(t0 + tq, (int)n);
+    return hi - range_start(base + t0, window);
+}
+
 // Decode work groups (kDecodeWaves waves each) the chip runs at once: one per
 // CU. Rows are split across work groups only as far as needed to fill them.
 constexpr int64_t kDecodeSlots = 256;
@@ -123,7 +135,9 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
         const int tq = p.dec_cols / G;
         int64_t total = 0;
         for (int b : dec_rows)
-            total += (int64_t)c->kv_heads * ceil_div(n_new[b], tq) * ceil_div(c->lens[b], kDecodeKeyTile);
+            for (int qt = 0; qt < ceil_div(n_new[b], tq); ++qt)
+                total += (int64_t)c->kv_heads * ceil_div(tile_span(c->lens[b], n_new[b], tq, qt, c->window),
+                                                         kDecodeKeyTile);
         // tiles per work group: the whole job spread over the slots, never
         // fewer than one tile per wave
         const int64_t tpw = std::max<int64_t>(kDecodeWaves, ceil_div(total, kDecodeSlots));
@@ -133,10 +147,12 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
             r.len = c->lens[b];
             r.nnew = n_new[b];
             r.nq = (int)ceil_div(r.nnew, tq);
-            const int64_t tiles = ceil_div(r.len, kDecodeKeyTile);
+            int64_t span = 0;                      // the longest query tile's key range
+            for (int qt = 0; qt < r.nq; ++qt) span = std::max(span, tile_span(r.len, r.nnew, tq, qt, c->window));
+            const int64_t tiles = ceil_div(span, kDecodeKeyTile);
             if (c->keys_per_split > 0) {
                 r.lsplit = (int)(ceil_div(c->keys_per_split, kDecodeKeyTile) * kDecodeKeyTile);
-                r.nsplit = (int)ceil_div(r.len, r.lsplit);
+                r.nsplit = (int)ceil_div(span, r.lsplit);
             } else {
                 r.nsplit = (int)ceil_div(tiles, tpw);
                 r.lsplit = (int)(ceil_div(tiles, r.nsplit) * kDecodeKeyTile);
@@ -148,16 +164,11 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
     // ---- prefill rows: split only rows whose longest item would dominate
     {
         const int tq = kPrefillCols / G;
-        int64_t total = 0, longest = 0;
-        for (int b : pre_rows) {
-            const int nq = (int)ceil_div(n_new[b], tq);
-            const int base = c->lens[b] - n_new[b];
-            for (int q = 0; q < nq; ++q) {
-                const int keys = base + std::min((q + 1) * tq, n_new[b]);
-                total += (int64_t)c->kv_heads * ceil_div(keys, kPrefillKeyTile);
-            }
-            longest = std::max<int64_t>(longest, ceil_div(c->lens[b], kPrefillKeyTile));
-        }
+        int64_t total = 0;
+        for (int b : pre_rows)
+            for (int qt = 0; qt < ceil_div(n_new[b], tq); ++qt)
+                total += (int64_t)c->kv_heads * ceil_div(tile_span(c->lens[b], n_new[b], tq, qt, c->window),
+                                                         kPrefillKeyTile);
         // a row is split only when its longest item would run well past the
         // per-slot share of the whole launch (the launch lasts as long as its
         // longest item)
@@ -168,10 +179,12 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
             r.len = c->lens[b];
             r.nnew = n_new[b];
             r.nq = (int)ceil_div(r.nnew, tq);
-            const int64_t tiles = ceil_div(r.len, kPrefillKeyTile);
+            int64_t span = 0;
+            for (int qt = 0; qt < r.nq; ++qt) span = std::max(span, tile_span(r.len, r.nnew, tq, qt, c->window));
+            const int64_t tiles = ceil_div(span, kPrefillKeyTile);
             if (c->keys_per_split > 0) {
                 r.lsplit = (int)(ceil_div(c->keys_per_split, kPrefillKeyTile) * kPrefillKeyTile);
-                r.nsplit = (int)ceil_div(r.len, r.lsplit);
+                r.nsplit = (int)ceil_div(span, r.lsplit);
             } else {
                 r.nsplit = 2 * tiles > 3 * cap ? (int)ceil_div(tiles, cap) : 1;
                 r.lsplit = (int)(ceil_div(tiles, r.nsplit) * kPrefillKeyTile);
@@ -179,7 +192,6 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
             r.work = tiles * r.nq;
             p.pre.push_back(r);
         }
-        (void)longest;
     }
     // heaviest rows first so long items start early
     auto heavier = [](const RowPlan &x, const RowPlan &y) { return x.work > y.work; };
@@ -259,6 +271,15 @@ void fill_attn_rows(const std::vector<RowPlan> &rows, size_t lo, size_t hi, int 
     t.total_items = item;
 }
 
+kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim, kv_dtype dtype,
+                       void *k_buf, void *v_buf, int32_t *lens_dev, void *stream, bool ring, int32_t window,
+                       kv_cache **out);
+
+// Ring caches: the lowest position a row of this length still holds, and the
+// lowest key a query at position pos sees ([MASK] "A strong answer", reversal).
+int64_t oldest_kept(const kv_cache *c, int64_t len) { return c->ring ? std::max<int64_t>(0, len - c->max_len) : 0; }
+int64_t lowest_needed(const kv_cache *c, int64_t pos) { return std::max<int64_t>(0, pos - c->window + 1); }
+
 }  // namespace
 
 // ===========================================================================
@@ -267,6 +288,29 @@ extern "C" {
 kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim,
                           kv_dtype dtype, void *k_buf, void *v_buf, int32_t *lens_dev, void *stream,
                           kv_cache **out) {
+    return create_cache(batch, kv_heads, max_len, head_dim, dtype, k_buf, v_buf, lens_dev, stream, false,
+                        kNoWindow, out);
+}
+
+kv_status kv_cache_create_ring(int32_t batch, int32_t kv_heads, int32_t capacity, int32_t head_dim,
+                               kv_dtype dtype, int32_t window, void *k_buf, void *v_buf, int32_t *lens_dev,
+                               void *stream, kv_cache **out) {
+    if (out == nullptr) return fail(KV_ERR_INVALID_ARG, "out is null");
+    *out = nullptr;
+    if (capacity <= 0 || capacity % kRingAlign != 0)
+        return fail(KV_ERR_INVALID_ARG, "ring capacity %d is not a positive multiple of %d", capacity, kRingAlign);
+    if (window < 1 || window > capacity)
+        return fail(KV_ERR_INVALID_ARG, "window %d outside 1..capacity %d", window, capacity);
+    return create_cache(batch, kv_heads, capacity, head_dim, dtype, k_buf, v_buf, lens_dev, stream, true, window,
+                        out);
+}
+
+}  // extern "C"
+
+namespace {
+kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim, kv_dtype dtype,
+                       void *k_buf, void *v_buf, int32_t *lens_dev, void *stream, bool ring, int32_t window,
+                       kv_cache **out) {
     if (out == nullptr) return fail(KV_ERR_INVALID_ARG, "out is null");
     *out = nullptr;
     if (dtype != KV_DTYPE_F32 && dtype != KV_DTYPE_BF16)
@@ -293,6 +337,8 @@ kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int3
     c->v = v_buf;
     c->lens_dev = lens_dev;
     c->lens.assign(batch, 0);
+    c->ring = ring;
+    c->window = window;
     if (lens_dev != nullptr) {
         for (int lo = 0; lo < batch; lo += kMaxRows) {
             LensTable t{};
@@ -311,6 +357,9 @@ kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int3
     *out = c;
     return ok();
 }
+}  // namespace
+
+extern "C" {
 
 void kv_cache_destroy(kv_cache *c) {
     if (c == nullptr) return;
@@ -330,8 +379,14 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
         if (n_new[b] < 0 || n_new[b] > T)
             return fail(KV_ERR_INVALID_ARG, "row %d: n_new %d outside 0..%d", b, n_new[b], T);
         const int64_t s = c->lens[b], n = n_new[b];
-        if (s + n > c->max_len)
+        if (!c->ring && s + n > c->max_len)
             return fail(KV_ERR_CAPACITY, "row %d: %lld tokens > max_len %d", b, (long long)(s + n), c->max_len);
+        // a ring write may not evict a key the first new query still needs
+        if (c->ring && n > 0 && oldest_kept(c, s + n) > lowest_needed(c, s))
+            return fail(KV_ERR_CAPACITY, "row %d: %lld new tokens would evict keys the window still needs "
+                        "(capacity %d, window %d)", b, (long long)n, c->max_len, c->window);
+        if (s + n > INT32_MAX - kRingAlign)
+            return fail(KV_ERR_CAPACITY, "row %d: position %lld out of range", b, (long long)(s + n));
         total += n;
     }
     if (total > 0) {
@@ -351,6 +406,8 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
         a.v_new = v_new;
         a.lens_dev = c->lens_dev;
         a.row_bytes = row_bytes;
+        a.row_shift = 0;
+        while ((int64_t(1) << a.row_shift) < row_bytes) ++a.row_shift;
         a.batch = c->batch;
         a.hkv = c->kv_heads;
         a.max_len = c->max_len;
@@ -362,6 +419,7 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
             const int j = (int)(i - lo), b = rows[i];
             a.t.b[j] = b;
             a.t.start[j] = c->lens[b];
+            a.t.slot0[j] = c->lens[b] % c->max_len;
             a.t.n[j] = n_new[b];
             a.t.nchunk[j] = (int32_t)ceil_div((int64_t)n_new[b] * row_bytes, kAppendChunk);
             a.t.block0[j] = blocks;
@@ -456,6 +514,7 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
     a.group = p.group;
     a.max_len = c->max_len;
     a.head_dim = c->head_dim;
+    a.window = c->window;
     a.records = p.records;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c->head_dim));
 
@@ -517,9 +576,12 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
 kv_status kv_truncate(kv_cache *c, const int32_t *new_lens, void *stream) {
     if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
     if (c->batch > 0 && new_lens == nullptr) return fail(KV_ERR_INVALID_ARG, "new_lens is null");
-    // [CH16] "Layout and validity": 0 <= n <= current length
+    // [CH16] "Layout and validity": 0 <= n <= current length; a ring must
+    // still hold every key the next query (at position n) would see
     for (int b = 0; b < c->batch; ++b)
-        if (new_lens[b] < 0 || new_lens[b] > c->lens[b]) return fail(KV_ERR_INVALID_ARG, "Invalid truncation length");
+        if (new_lens[b] < 0 || new_lens[b] > c->lens[b] ||
+            lowest_needed(c, new_lens[b]) < oldest_kept(c, c->lens[b]))
+            return fail(KV_ERR_INVALID_ARG, "Invalid truncation length");
     if (c->lens_dev != nullptr) {
         std::vector<int> rows;
         for (int b = 0; b < c->batch; ++b)
@@ -554,8 +616,8 @@ uint64_t kv_cache_bytes(const kv_cache *c) {
 
 uint64_t kv_live_bytes(const kv_cache *c) {
     if (c == nullptr) return 0;
-    uint64_t tokens = 0;
-    for (int32_t l : c->lens) tokens += (uint64_t)l;
+    uint64_t tokens = 0;      // a ring holds at most max_len tokens of a row
+    for (int32_t l : c->lens) tokens += (uint64_t)(c->ring ? std::min(l, c->max_len) : l);
     return 2ull * tokens * c->kv_heads * c->head_dim * c->elem_bytes;
 }
 

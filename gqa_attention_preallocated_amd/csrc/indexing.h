@@ -33,11 +33,18 @@ struct Item {
     int b, kvh, qtile, split, nq, nsplit;
     int base;             // absolute position of the row's query 0 = len - n_new
     int t0, t_end;        // queries [t0, t_end) of this tile
-    int k_begin, k_end;   // keys of this split that some query of the tile may see
+    int k_begin, k_end;   // key positions of this split that some query of the tile may see
     int rec0;             // first partial record of the item, or -1: direct write
 };
 
-GQAKV_HD inline Item decode_item(const AttnRows &R, int item, int hkv, int group, int cols) {
+// First key position an item's range starts from: the lowest key its first
+// query sees under the window, rounded down to kRingAlign (0 without a window).
+GQAKV_HD inline int range_start(int first_pos, int window) {
+    const int lo = first_pos - window + 1;
+    return lo <= 0 ? 0 : lo - lo % kRingAlign;
+}
+
+GQAKV_HD inline Item decode_item(const AttnRows &R, int item, int hkv, int group, int cols, int window) {
     Item it;
     const int r = find_row(R.item0, R.n_rows, item);
     const int n = R.nnew[r];
@@ -54,9 +61,10 @@ GQAKV_HD inline Item decode_item(const AttnRows &R, int item, int hkv, int group
     it.t0 = it.qtile * tq;
     it.t_end = imin(it.t0 + tq, n);
     // bottom-right rule: the tile's last query sits at base + t_end - 1 and sees
-    // keys up to that position, never past the row's length
+    // keys up to that position, never past the row's length; with a window the
+    // tile's first query sees nothing below base + t0 - window + 1
     const int keys_hi = it.base + it.t_end;
-    it.k_begin = it.split * R.lsplit[r];
+    it.k_begin = range_start(it.base + it.t0, window) + it.split * R.lsplit[r];
     it.k_end = imin(it.k_begin + R.lsplit[r], keys_hi);
     it.rec0 = R.pbase[r] < 0 ? -1
             : R.pbase[r] + ((it.kvh * it.nq + it.qtile) * it.nsplit + it.split) * cols;

@@ -16,7 +16,8 @@ constexpr int kMaxRows = 64;
 struct AppendTable {
     int32_t n_rows;
     int32_t b[kMaxRows];       // batch row
-    int32_t start[kMaxRows];   // row length before the append (first slot written)
+    int32_t start[kMaxRows];   // row length before the append (position of the first token)
+    int32_t slot0[kMaxRows];   // slot of the first token: start mod max_len (a ring wraps there)
     int32_t n[kMaxRows];       // tokens written
     int32_t nchunk[kMaxRows];  // 4 KiB copy chunks per (row, kv head)
     int32_t block0[kMaxRows + 1];
@@ -28,7 +29,8 @@ struct AppendArgs {
     const void *k_new;         // [B, Hkv, T, d]
     const void *v_new;
     int32_t *lens_dev;         // optional
-    int64_t row_bytes;         // d * element size
+    int64_t row_bytes;         // d * element size (a power of two)
+    int32_t row_shift;         // log2(row_bytes)
     int32_t batch, hkv, max_len, T;
     AppendTable t;
 };
@@ -63,6 +65,7 @@ struct AttnArgs {
     float *ws_acc;             // partial records: unnormalised acc [rec][d]
     float *ws_ml;              // partial records: (running max in log2 units, sum) [rec][2]
     int32_t batch, T, hq, hkv, group, max_len, head_dim;
+    int32_t window;            // keys a query sees: pos - window < key <= pos (kNoWindow: no lower bound)
     int64_t records;           // partial records available in the workspace
     float scale_log2;          // log2(e) / sqrt(d)
     AttnRows rows;
@@ -130,6 +133,11 @@ constexpr int kDecodeKeyTile = 32;
 constexpr int kDecodeWaves = 8;       // waves per decode work group (they split the keys)
 constexpr int kPrefillKeyTile = 64;
 constexpr int kPrefillCols = 128;
+// Window of a linear cache: pos - kNoWindow < 0 <= every key, so no lower bound.
+constexpr int32_t kNoWindow = 0x7fffffff;
+// Ring caches hold a multiple of this many slots, and key ranges start at a
+// multiple of it, so no key tile of either kernel wraps inside the ring.
+constexpr int32_t kRingAlign = 64;
 constexpr int kZeroSlice = 16384;   // bytes of output one zero-fill block clears
 constexpr int kAppendChunk = 4096;
 

@@ -194,7 +194,8 @@ __device__ inline float wave_sum_across_groups(float v) {
 
 // ---------------------------------------------------------------------------
 // append: bit copy of the new tokens into their slots ([GQA] "A strong answer":
-// written in place at the row's current length; nothing else moves)
+// written in place at the row's current length; nothing else moves). In a ring
+// cache token p lands in slot p mod max_len ([CH16] exercise 3).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int r = find_row(a.t.block0, a.t.n_rows, blockIdx.x);
@@ -207,8 +208,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int64_t off = (int64_t)chunk * kAppendChunk + threadIdx.x * 16;
     const int64_t head = (int64_t)b * a.hkv + kvh;
     if (off < span) {
+        // token i of the row goes to slot slot0 + i, wrapping at max_len (a
+        // ring; a linear cache never reaches the wrap)
+        const int tok = (int)(off >> a.row_shift);
+        int slot = a.t.slot0[r] + tok;
+        if (slot >= a.max_len) slot -= a.max_len;
         const int64_t src = head * a.T * a.row_bytes + off;
-        const int64_t dst = (head * a.max_len + a.t.start[r]) * a.row_bytes + off;
+        const int64_t dst = ((head * a.max_len + slot) << a.row_shift) + (off & (a.row_bytes - 1));
         const uint4 kx = *reinterpret_cast<const uint4 *>((const char *)a.k_new + src);
         const uint4 vx = *reinterpret_cast<const uint4 *>((const char *)a.v_new + src);
         *reinterpret_cast<uint4 *>((char *)a.k + dst) = kx;
@@ -339,7 +345,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     const int wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     unsigned char *lds = lds_all + wave * STAGE;
-    const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, C);
+    const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, C, a.window);
 
     // this wave's share of the item's keys: every W-th 32-key tile from its
     // own, so at any time the work group streams one contiguous run of K and
@@ -381,15 +387,18 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     //      tile is 64 VGPRs a lane; a second set would halve the waves a CU holds)
     vec kA[2][KC];
     uint4 vA[VCH];
+    // key position j lives in slot j mod max_len; a tile never wraps (ring
+    // capacities are multiples of kRingAlign, tiles start at multiples of KT)
     auto load_tile = [&](vec (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
+        const int slot = tile % a.max_len;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int key = tile + ks * 16 + lr;
-            const bool ok = key < w_end;
+            const int key = ks * 16 + lr;
+            const bool ok = tile + key < w_end;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 const int d0 = kc * 32 + lg * 8;
-                kop[ks][kc] = (ok && d0 < D) ? O::gload_stream(kbase + (int64_t)key * D + d0) : O::zero();
+                kop[ks][kc] = (ok && d0 < D) ? O::gload_stream(kbase + (int64_t)(slot + key) * D + d0) : O::zero();
             }
         }
 #pragma unroll
@@ -397,15 +406,21 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
             const int c = lane + 64 * i;
             const int key = c / CPK, part = c % CPK;
             const bool ok = (c < KT * CPK) && (tile + key < w_end);
-            vreg[i] = ok ? load_stream(reinterpret_cast<const unsigned char *>(vbase + (int64_t)(tile + key) * D) +
+            vreg[i] = ok ? load_stream(reinterpret_cast<const unsigned char *>(vbase + (int64_t)(slot + key) * D) +
                                        part * 16)
                          : make_uint4(0, 0, 0, 0);
         }
     };
 
     // smallest position among this item's real columns: tiles ending at or
-    // before it need no mask ([MASK] "A strong answer", tile cases)
+    // before it need no mask ([MASK] "A strong answer", tile cases); with a
+    // window, tiles starting at or below the largest position minus the
+    // window hold keys below some column's window
     const int pos_min = it.base + it.t0;
+    const int pos_max = it.base + it.t_end - 1;
+    int lo_key[NSUB];                              // lowest key each column sees (clamped at 0)
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) lo_key[s] = pos[s] - a.window + 1 > 0 ? pos[s] - a.window + 1 : 0;
 
     // compute the tile held in (kop, vreg), refilling the set with the next tile
     auto process = [&](vec (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
@@ -433,7 +448,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 
         // ---- mask (only tiles that straddle the diagonal or the range end),
         //      online softmax in log2 units
-        const bool need_mask = (tile + KT > w_end) || (tile + KT - 1 > pos_min);
+        const bool need_mask = (tile + KT > w_end) || (tile + KT - 1 > pos_min) || (tile <= pos_max - a.window);
         f32x8 p[NSUB];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
@@ -441,10 +456,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = sc[s][j >> 2][j & 3];
             if (need_mask) {                      // uniform over the wave
-                // key j is visible iff j <= pos and j < the range end
+                // key j is visible iff lo_key <= j <= pos and j < the range end
                 const int lim = imin(pos[s] + 1, w_end) - (tile + lg * 4);
+                const int lim_lo = lo_key[s] - (tile + lg * 4);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = ((j >> 2) * 16 + (j & 3) < lim) ? v[j] : -INFINITY;
+                for (int j = 0; j < 8; ++j) {
+                    const int off = (j >> 2) * 16 + (j & 3);
+                    v[j] = (off < lim && off >= lim_lo) ? v[j] : -INFINITY;
+                }
             }
             softmax_step<NB>(v, a.scale_log2, st[s], acc[s], p[s]);
         }
@@ -537,7 +556,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
-    const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, C);
+    const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, C, a.window);
 
     int pos[NS];
     vec qop[NS][KC];
@@ -590,8 +609,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // thread chunk c = tid + 256 i is key c / CPK, bytes (c % CPK) * 16.. of the
     // tile: byte offset c * 16 from the tile's first key. Keys at or past
     // k_end (and chunks past the tile) fall outside the view and read as zero.
+    // key position j lives in slot j mod max_len; no tile wraps (see decode)
     auto load = [&](uint4 (&reg)[PCH], const unsigned char *base, int tile) {
-        const __amdgpu_buffer_rsrc_t r = buffer_view(base + (int64_t)tile * ROWB, imin(it.k_end - tile, KT) * ROWB);
+        const __amdgpu_buffer_rsrc_t r =
+            buffer_view(base + (int64_t)(tile % a.max_len) * ROWB, imin(it.k_end - tile, KT) * ROWB);
 #pragma unroll
         for (int i = 0; i < PCH; ++i) reg[i] = buffer_load_stream(r, (tid + 256 * i) * 16);
     };
@@ -637,18 +658,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
     };
     // straddling tiles only: key (ch, ks, j) = tile + ch*32 + ks*16 + 4*lg + j
-    // is visible iff it is <= the column's position and < the split end
+    // is visible iff it is <= the column's position, > that position minus
+    // the window, and < the split end
     auto mask = [&](int tile, f32x4 (&sc)[2][NS][2]) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const int lim = imin(pos[s] + 1, it.k_end) - (tile + lg * 4);
+            const int lo_key = pos[s] - a.window + 1 > 0 ? pos[s] - a.window + 1 : 0;
+            const int lim_lo = lo_key - (tile + lg * 4);
 #pragma unroll
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        sc[ch][s][ks][j] = (ch * 32 + ks * 16 + j < lim) ? sc[ch][s][ks][j] : -INFINITY;
+                    for (int j = 0; j < 4; ++j) {
+                        const int off = ch * 32 + ks * 16 + j;
+                        sc[ch][s][ks][j] = (off < lim && off >= lim_lo) ? sc[ch][s][ks][j] : -INFINITY;
+                    }
         }
     };
     // column max of the tile in log2 units
@@ -680,7 +706,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // staged after the loop behind its own barrier. A wave computes tiles
     // 0..wave_last only (tiles past its last query are skipped; it still
     // takes part in staging and barriers).
-    const int ntiles = (it.k_end - it.k_begin + KT - 1) / KT;     // 0 for an empty item
+    const int ntiles = it.k_end > it.k_begin ? (it.k_end - it.k_begin + KT - 1) / KT : 0;
     const int wave_last = wave_pos_max < it.k_begin ? -1 : imin(ntiles - 1, (wave_pos_max - it.k_begin) / KT);
     f32x4 sc[2][NS][2];
     vec pb[2][NS];
@@ -790,7 +816,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             if (i == wave_last + 1 && wave_last >= 0) pv(vp, pb);   // the last tile this wave computed
             continue;
         }
-        if ((tile + KT > it.k_end) || (tile + KT - 1 > wave_pos_min)) mask(tile, sc);   // uniform over the wave
+        if ((tile + KT > it.k_end) || (tile + KT - 1 > wave_pos_min) || (tile <= wave_pos_max - a.window))
+            mask(tile, sc);                              // uniform over the wave
 
         float tmax[NS], m_use[NS];
         __builtin_amdgcn_s_setprio(1);

@@ -49,7 +49,8 @@ typedef struct kv_cache kv_cache;
 typedef enum kv_status {
     KV_OK = 0,
     KV_ERR_INVALID_ARG = 1,   /* bad pointer, shape, n_new or truncation length */
-    KV_ERR_CAPACITY = 2,      /* an append would pass max_len                    */
+    KV_ERR_CAPACITY = 2,      /* an append would pass max_len (or, in a ring,
+                                 evict keys the window still needs)              */
     KV_ERR_UNSUPPORTED = 3,   /* head_dim, dtype or group size not built         */
     KV_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required      */
     KV_ERR_DEVICE = 5         /* a HIP call failed                               */
@@ -79,6 +80,35 @@ kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int3
                           kv_dtype dtype, void *k_buf, void *v_buf, int32_t *lens_dev,
                           void *stream, kv_cache **out);
 
+/*
+ * Sliding-window cache: wrap caller-allocated buffers as a ring of `capacity`
+ * slots per row, keeping only the latest tokens, with attention limited to a
+ * window. [MASK] "A strong answer" (the reversal: with a window W the mask
+ * gains the lower bound j > (S - T) + i - W, and in a ring buffer the
+ * comparison uses the tokens' absolute positions, not slot indices) and
+ * [CH16] exercise 3 (a cache that keeps only the last positions in a ring).
+ *   capacity      slots per row, a positive multiple of 64; k_buf and v_buf
+ *                 hold B*Hkv*capacity*d elements each, laid out as
+ *                 [B, Hkv, capacity, d].
+ *   window        1 <= window <= capacity: a query at absolute position p
+ *                 sees keys p - window < j <= p.
+ * Token p of a row lives in slot p mod capacity. Lengths count every token
+ * ever appended (the next absolute position; below 2^31 - 64), and
+ * kv_get_lens, kv_truncate, lens_dev and the query positions of
+ * gqa_attention use those absolute positions. kv_append refuses (with
+ * KV_ERR_CAPACITY, "row {b}: {n} new tokens would evict keys the window still
+ * needs (capacity {C}, window {W})") a write that would overwrite a key its
+ * own first new query still needs, so at most capacity - window + 1 tokens
+ * per call once a row has wrapped. kv_truncate also refuses a rollback to a
+ * length whose next query would need a key already overwritten.
+ * Other arguments and errors as kv_cache_create; KV_ERR_INVALID_ARG for a
+ * capacity that is not a positive multiple of 64 or a window outside
+ * 1..capacity.
+ */
+kv_status kv_cache_create_ring(int32_t batch, int32_t kv_heads, int32_t capacity, int32_t head_dim,
+                               kv_dtype dtype, int32_t window, void *k_buf, void *v_buf,
+                               int32_t *lens_dev, void *stream, kv_cache **out);
+
 /* Release the handle (never the caller's buffers). NULL is ignored. */
 void kv_cache_destroy(kv_cache *c);
 
@@ -94,7 +124,8 @@ void kv_cache_destroy(kv_cache *c);
  * Every row is checked before anything is written: if lens[b] + n_new[b] >
  * max_len for any b the call returns KV_ERR_CAPACITY with the message
  * "row {b}: {lens[b]+n_new[b]} tokens > max_len {max_len}" and changes nothing.
- * The bytes are copied bit for bit.
+ * The bytes are copied bit for bit. In a ring cache (kv_cache_create_ring)
+ * token p goes to slot p mod capacity and the capacity rule is the ring's.
  */
 kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T,
                     const int32_t *n_new, void *stream);
@@ -114,7 +145,9 @@ kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32
  * repeated KV; query t of row b sits at absolute position
  * lens[b] - n_new[b] + t and sees key j iff j <= lens[b] - n_new[b] + t and
  * j < lens[b] ([MASK] TL;DR: the bottom-right-aligned rule j <= i + (S - T),
- * evaluated as index arithmetic, never as a mask tensor). Scores are scaled by
+ * evaluated as index arithmetic, never as a mask tensor); in a ring cache also
+ * j > lens[b] - n_new[b] + t - window, with key j read from slot j mod
+ * capacity ([MASK] "A strong answer", the reversal). Scores are scaled by
  * 1/sqrt(d). Slots t >= n_new[b], rows with n_new[b] == 0, B == 0 and T == 0
  * give +0.0 (never NaN).
  *   q             device [B, q_heads, T, d]; out device [B, q_heads, T, d].
@@ -142,7 +175,8 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
  * Roll back: set lens[b] = new_lens[b] for every row, copying and clearing
  * nothing. [CH16] "Layout and validity" (truncate for speculative rollback;
  * stale slots stay and are never read). new_lens is a HOST int32[B] with
- * 0 <= new_lens[b] <= lens[b]; otherwise KV_ERR_INVALID_ARG with the message
+ * 0 <= new_lens[b] <= lens[b] (and, in a ring cache, new_lens[b] no lower
+ * than the ring still supports); otherwise KV_ERR_INVALID_ARG with the message
  * "Invalid truncation length". Truncating every row to 0 is a reset.
  */
 kv_status kv_truncate(kv_cache *c, const int32_t *new_lens, void *stream);
@@ -158,7 +192,8 @@ uint64_t kv_cache_bytes(const kv_cache *c);
 
 /*
  * Bytes of valid K and V, 2 * sum(lens) * Hkv * d * element size
- * ([CH16] "How big is the cache?" with tokens = the current lengths).
+ * ([CH16] "How big is the cache?" with tokens = the current lengths; a ring
+ * row counts at most `capacity` tokens).
  */
 uint64_t kv_live_bytes(const kv_cache *c);
 

@@ -158,20 +158,33 @@ def attention(cache: RingCache, q, n_new):
     if B != cache.batch or d != cache.head_dim or hq % hk != 0 or hq == 0:
         raise ValueError("q must be [B, Hq, T, d] with the cache's B and d and Hq a multiple of Hkv")
     n_new = np.asarray(n_new, dtype=np.int64).reshape(-1)
-    G = hq // hk
     out = np.zeros((B, hq, T, d), np.float64)
     for b in range(B):
         L, n = int(cache.lens[b]), int(n_new[b])
         if n < 0 or n > T or n > L:
             raise ValueError(f"row {b}: bad n_new {n}")
-        k64 = to_float64(cache.k[b], cache.dtype)
-        v64 = to_float64(cache.v[b], cache.dtype)
-        stored = cache.pos[b]
-        for h in range(hq):
-            kvh = kv_head_of(h, G)
-            for t in range(n):
-                p = query_position(L, n, t)
-                vis = window_visible(stored, p, L, cache.window)
-                qv = to_float64(q[b, h, t], cache.dtype)
-                out[b, h, t] = attend_one(k64[kvh][vis], v64[kvh][vis], qv, d)
+        out[b] = attention_row(cache.k[b], cache.v[b], cache.pos[b], L, n, q[b], cache.dtype, cache.window,
+                               [(h, t) for h in range(hq) for t in range(n)])
+    return out
+
+
+def attention_row(k_slots, v_slots, stored, length, n_new_b, q_row, dtype, window, pairs):
+    """Outputs of one row for the listed (head, t) pairs; zeros elsewhere.
+
+    k_slots, v_slots: [Hkv, C, d] stored values of the row's ring; stored: [C]
+    absolute position held by each slot (-1: empty); q_row: [Hq, T, d]. Used by
+    ``attention`` and by the full-size tests to check sampled outputs.
+    """
+    hk, _, d = k_slots.shape
+    hq, T, _ = q_row.shape
+    G = hq // hk
+    out = np.zeros((hq, T, d), np.float64)
+    for h, t in pairs:
+        if t >= n_new_b:
+            continue
+        kvh = kv_head_of(h, G)
+        p = query_position(length, n_new_b, t)
+        vis = window_visible(np.asarray(stored), p, length, window)
+        out[h, t] = attend_one(to_float64(k_slots[kvh][vis], dtype), to_float64(v_slots[kvh][vis], dtype),
+                               to_float64(q_row[h, t], dtype), d)
     return out

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <map>
 #include <string>
@@ -125,14 +126,19 @@ hipError_t launch_append(const AppendArgs &a, int n_blocks, hipStream_t) {
         for (int tid = 0; tid < 256; ++tid) {
             const int64_t off = (int64_t)chunk * kAppendChunk + tid * 16;
             if (off >= span) continue;
+            if ((int64_t(1) << a.row_shift) != a.row_bytes) err("append: row_shift does not match row_bytes");
+            if (a.t.slot0[r] != a.t.start[r] % a.max_len) err("append: slot0 is not start mod max_len");
+            // the kernel's mapping: token i -> slot slot0 + i, wrapped once at max_len
+            const int tok = (int)(off >> a.row_shift);
+            int slot = a.t.slot0[r] + tok;
+            if (slot >= a.max_len) slot -= a.max_len;
             const int64_t src = head * a.T * a.row_bytes + off;
-            const int64_t dst = (head * a.max_len + a.t.start[r]) * a.row_bytes + off;
+            const int64_t dst = ((head * a.max_len + slot) << a.row_shift) + (off & (a.row_bytes - 1));
             access((const char *)a.k_new + src, 16, "k_new", "append read k_new");
             access((const char *)a.v_new + src, 16, "v_new", "append read v_new");
             access((const char *)a.k + dst, 16, "k", "append write K");
             access((const char *)a.v + dst, 16, "v", "append write V");
-            const int64_t slot = dst / a.row_bytes - head * a.max_len;
-            if (slot < a.t.start[r] || slot >= a.t.start[r] + a.t.n[r] || slot >= a.max_len)
+            if (slot < 0 || slot >= a.max_len || slot != (a.t.start[r] + tok) % a.max_len || tok >= a.t.n[r])
                 err("append: write outside the row's new slots");
             g_appended[(uintptr_t)a.k + dst]++;
         }
@@ -160,23 +166,39 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem) {
     const int D = a.head_dim;
     const int64_t row_bytes = (int64_t)D * elem;
     if (R.item0[R.n_rows] != R.total_items) err("item0 does not end at total_items");
+    const bool windowed = a.window != kNoWindow;
+    if (windowed && (a.window < 1 || a.window > a.max_len || a.max_len % kRingAlign != 0))
+        err("attention: bad ring window or capacity");
     for (int r = 0; r < R.n_rows; ++r) {
-        if (R.len[r] > a.max_len || R.nnew[r] > R.len[r] || R.nnew[r] <= 0 || R.nnew[r] > a.T)
+        if ((!windowed && R.len[r] > a.max_len) || R.nnew[r] > R.len[r] || R.nnew[r] <= 0 || R.nnew[r] > a.T)
             err("attention: bad row table entry");
         if (R.lsplit[r] % key_tile != 0 || R.nsplit[r] <= 0) err("attention: bad split");
-        if ((int64_t)R.nsplit[r] * R.lsplit[r] < R.len[r]) err("attention: splits do not cover the row");
     }
     for (int item = 0; item < R.total_items; ++item) {
-        const Item it = decode_item(R, item, a.hkv, a.group, cols);
+        const Item it = decode_item(R, item, a.hkv, a.group, cols, a.window);
         const int r = find_row(R.item0, R.n_rows, item);
         if (it.b < 0 || it.b >= a.batch || it.kvh < 0 || it.kvh >= a.hkv || it.qtile < 0 || it.qtile >= it.nq ||
             it.split < 0 || it.split >= it.nsplit)
             err("attention: item decodes outside the launch");
         if (it.k_begin < 0 || it.k_end > R.len[r]) err("attention: key range outside the row");
+        if (it.k_begin % key_tile != 0) err("attention: key range does not start on a tile");
+        // the item's splits cover every key its queries may see: from the
+        // first query's window start to the last query's position
+        const int first_pos = it.base + it.t0;
+        const int lo_visible = windowed ? std::max(0, first_pos - a.window + 1) : 0;
+        if (it.split == 0 && range_start(first_pos, a.window) > lo_visible) err("attention: range starts too late");
+        if (it.split == it.nsplit - 1 && it.k_begin + R.lsplit[r] < it.base + it.t_end)
+            err("attention: splits do not cover the item's keys");
+        // every visible key is still held by the ring (positions >= len - max_len)
+        if (windowed && lo_visible < std::max(0, R.len[r] - a.max_len)) err("attention: window key evicted");
         const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
-        // keys read: [k_begin, k_end), loaded tile by tile with loads past k_end predicated off
-        if (it.k_begin < it.k_end) {
-            for (int key : {it.k_begin, it.k_end - 1}) {
+        // keys read: [k_begin, k_end) tile by tile; key j from slot j mod max_len,
+        // and no tile may wrap inside the ring
+        for (int t0 = it.k_begin; t0 < it.k_end; t0 += key_tile) {
+            const int n = std::min(key_tile, it.k_end - t0);
+            const int slot = t0 % a.max_len;
+            if (slot + n > a.max_len) err("attention: key tile wraps");
+            for (int key : {slot, slot + n - 1}) {
                 access((const char *)a.k + (head * a.max_len + key) * row_bytes, row_bytes, "k", "attention K");
                 access((const char *)a.v + (head * a.max_len + key) * row_bytes, row_bytes, "v", "attention V");
             }

@@ -34,6 +34,7 @@ def sim(tmp_path_factory):
     P, I32 = ctypes.c_void_p, ctypes.c_int32
     I32P = ctypes.POINTER(ctypes.c_int32)
     lib.kv_cache_create.argtypes = [I32, I32, I32, I32, ctypes.c_int, P, P, P, P, ctypes.POINTER(P)]
+    lib.kv_cache_create_ring.argtypes = [I32, I32, I32, I32, ctypes.c_int, I32, P, P, P, P, ctypes.POINTER(P)]
     lib.kv_append.argtypes = [P, P, P, I32, I32P, P]
     lib.gqa_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]
     lib.gqa_attention.argtypes = [P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
@@ -61,7 +62,7 @@ class SimCache:
 
     GAP = 1 << 44
 
-    def __init__(self, lib, B, hk, max_len, d, dtype, hq, t_max):
+    def __init__(self, lib, B, hk, max_len, d, dtype, hq, t_max, window=None):
         self.lib, self.B, self.hk, self.max_len, self.d, self.hq = lib, B, hk, max_len, d, hq
         self.elem = 4 if dtype == "f32" else 2
         lib.hostcheck_reset()
@@ -78,10 +79,14 @@ class SimCache:
             self.addr[name] = base
             lib.hostcheck_region(base, max(size, 1), name.encode())
         h = ctypes.c_void_p()
-        st = lib.kv_cache_create(B, hk, max_len, d, 0 if dtype == "f32" else 1, ctypes.c_void_p(self.addr["k"]),
-                                 ctypes.c_void_p(self.addr["v"]), ctypes.c_void_p(self.addr["lens"]), None,
-                                 ctypes.byref(h))
+        bufs = (ctypes.c_void_p(self.addr["k"]), ctypes.c_void_p(self.addr["v"]), ctypes.c_void_p(self.addr["lens"]))
+        if window is None:
+            st = lib.kv_cache_create(B, hk, max_len, d, 0 if dtype == "f32" else 1, *bufs, None, ctypes.byref(h))
+        else:
+            st = lib.kv_cache_create_ring(B, hk, max_len, d, 0 if dtype == "f32" else 1, window, *bufs, None,
+                                          ctypes.byref(h))
         assert st == 0, lib.kv_last_error()
+        self.window = window
         self.h = h
         self.lens = np.zeros(B, np.int64)
         self.appended = 0
@@ -93,6 +98,8 @@ class SimCache:
         assert st == 0, self.lib.kv_last_error()
         self.lens += np.asarray(n_new)
         self.appended += int(np.sum(n_new)) * self.hk * self.d * self.elem // 16
+        if (self.lens > self.max_len).any():
+            self.rewrote = True              # a ring has wrapped: slots are written again
 
     def attention(self, T, n_new):
         size = ctypes.c_size_t()
@@ -235,3 +242,42 @@ def test_mqa_and_mha_shapes(sim):
         c.append(3, [1, 3])
         c.attention(3, [1, 3])
         c.check(3)
+
+
+@pytest.mark.parametrize("d,C,win", [(16, 64, 1), (64, 128, 50), (128, 128, 128), (128, 192, 64), (32, 256, 200)])
+def test_ring_schedules(sim, d, C, win):
+    """Sliding-window rings: every launch stays inside its buffers, reads only
+    held keys through slots that never wrap inside a tile, and writes every
+    output row once, over many wraps, under every kernel selection."""
+    calls, lens = W.ring_schedule(d * 1000 + C + win, 3, C, win, 200, min(40, C - win + 1))
+    assert lens.max() > C + 8                     # the schedule wraps the ring
+    for policy in [(0, 0), (1, 0), (2, 0), (1, 32), (2, 64)]:
+        c = SimCache(sim, 3, 2, C, d, "bf16", 8, max(x["T"] for x in calls), window=win)
+        sim.kv_cache_set_policy(c.h, *policy)
+        for call in calls:
+            c.append(call["T"], call["n_new"])
+            if max(call["n_new"]) > 0:
+                c.attention(call["T"], call["n_new"])
+                c.check(call["T"])
+
+
+def test_ring_capacity_and_rollback_rules(sim):
+    """An append that would evict a key its first new query needs, and a rollback
+    below what the ring still holds, are refused and change nothing."""
+    C, W = 128, 64
+    c = SimCache(sim, 1, 1, C, 64, "bf16", 4, 128, window=W)
+    c.append(128, [128])
+    assert sim.kv_append(c.h, ctypes.c_void_p(c.addr["k_new"]), ctypes.c_void_p(c.addr["v_new"]), 128,
+                         _i32([66]), None) == 2          # KV_ERR_CAPACITY: 66 > C - W + 1
+    assert b"evict" in sim.kv_last_error()
+    c.append(65, [65])                                   # the limit: the ring now holds positions 65..192
+    # a rollback to n' needs keys from n' - 63 on: 127 needs key 64 (evicted), 128 needs 65 (held)
+    assert sim.kv_truncate(c.h, _i32([127]), None) == 1
+    assert b"Invalid truncation length" in sim.kv_last_error()
+    assert sim.kv_truncate(c.h, _i32([128]), None) == 0
+    c.lens[:] = 128
+    c.rewrote = True
+    c.check()
+    c.append(65, [65])
+    c.attention(65, [65])
+    c.check(65)

@@ -14,6 +14,7 @@ from .synth import (  # noqa: F401
     LLAMA8B_VERIFY,
     LLAMA8B_CHUNKED_PREFILL,
     LLAMA8B_RAGGED,
+    LLAMA8B_WINDOW_DECODE,
     WORKLOADS,
     to_bf16_bits,
     bf16_bits_to_f32,
@@ -25,4 +26,5 @@ from .synth import (  # noqa: F401
     tiny_schedule,
     trial_spec,
     ragged_rows,
+    ring_schedule,
 )

@@ -99,6 +99,12 @@ TINY_FP32 = Shape("tiny_fp32", "f32", 2, 4, 2, 16, 64,
 LLAMA8B_DECODE = Shape("llama8b_decode_b32_s4096", "bf16", 32, 32, 8, 128, 8192,
                        value_scale=1.0 / math.sqrt(128.0),
                        notes={"cached": 4096, "T": 1})
+# Sliding window over a ring: max_len is the ring capacity (slots per row);
+# 20,000 tokens precede the step, so the ring has wrapped twice and a decode
+# query at position 20,000 reads keys 16,905 .. 20,000 through wrapped slots.
+LLAMA8B_WINDOW_DECODE = Shape("llama8b_window_decode_b32_w4096_c8192", "bf16", 32, 32, 8, 128, 8192,
+                              value_scale=1.0 / math.sqrt(128.0),
+                              notes={"window": 4096, "cached": 20000, "T": 1})
 LLAMA8B_VERIFY = Shape("llama8b_verify_b16_t4_s4096", "bf16", 16, 32, 8, 128, 8192,
                        notes={"cached": 4092, "T": 4})
 LLAMA8B_CHUNKED_PREFILL = Shape("llama8b_chunked_prefill_b4_10240x512", "bf16", 4, 32, 8, 128, 16384,
@@ -241,3 +247,22 @@ def ragged_rows(seed: int = 4, batch: int = 64, lo: int = 1, hi: int = 32000,
     lens = np.clip(np.rint(np.exp(u)), lo, hi).astype(np.int64)
     n_new = rng.choice(np.asarray(choices, dtype=np.int64), size=batch)
     return lens, n_new
+
+
+def ring_schedule(seed, batch, capacity, window, steps, t_cap):
+    """Seeded calls for a sliding-window ring: decode steps (T=1), short chunks
+    (T=4) and chunks of t_cap, some rows idle, every row's n_new kept within
+    what the ring accepts (any n while the row fits in the ring, at most
+    capacity - window + 1 once it would wrap). Returns (calls, final lengths)."""
+    rng = np.random.default_rng(seed)
+    lens = np.zeros(batch, np.int64)
+    calls = []
+    for _ in range(steps):
+        T = int(rng.choice([1, 1, 4, t_cap]))
+        n = []
+        for b in range(batch):
+            lim = T if lens[b] + T <= capacity else min(T, capacity - window + 1)
+            n.append(int(rng.integers(0, lim + 1)) if rng.random() < 0.8 else 0)
+        calls.append({"T": T, "n_new": n})
+        lens += np.asarray(n)
+    return calls, lens
