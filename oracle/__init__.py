@@ -16,9 +16,12 @@ check it against the pages by eye:
                       used to cross-check ``direct``.
   * ``window``     -- sliding-window attention over a ring-buffer cache whose
                       slots store the absolute positions they hold.
+  * ``fp8``        -- an E4M3 cache with one scale per KV head: the format's
+                      decoder and round-to-nearest-even encoder, attention on
+                      the dequantized values.
 
 Where the pages are silent or disagree, the reading taken is stated in the
 docstring of the function that depends on it.
 """
 
-from . import direct, vectorised, window  # noqa: F401
+from . import direct, fp8, vectorised, window  # noqa: F401
