@@ -306,6 +306,33 @@ def run_window(torch, reps=30):
             "config": {"workload": sh.name, "batch": B, "window": win, "ring_slots": C, "position": L, "T": 1}}
 
 
+def run_fp8(torch, reps=30):
+    """Decode over an E4M3 cache: the Llama decode shape (B=32, 4,096 cached + 1,
+    T=1) with K and V stored as codes and one scale per KV head. Two caches in turn."""
+    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    import workloads as W
+    sh = W.LLAMA8B_DECODE
+    B, hq, hkv, d = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim
+    sc = [2.0 ** -9] * hkv
+    caches = [KVCache(B, hkv, sh.max_len, d, device_lens=False, fp8_scales=(sc, sc)) for _ in range(2)]
+    g = torch.Generator(device="cuda").manual_seed(12)
+    for c in caches:
+        for n in (2048, 2048, 1):
+            x = (torch.randn(B, hkv, n, d, device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+            c.append(x, x, [n] * B)
+    q = (torch.randn(B, hq, 1, d, device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    n = [1] * B
+    ws = torch.zeros(max(max(c.workspace_bytes(hq, 1, n) for c in caches), 256), dtype=torch.uint8, device="cuda")
+    t = _time_calls(torch, lambda i: gqa_attention(q, caches[i & 1], n, out=out, workspace=ws), reps)
+    # live K+V codes (one byte each), q and out in bfloat16
+    nbytes = B * 4097 * hkv * d * 2 + 2 * B * hq * d * 2
+    return {"metric": "E4M3-cache decode attention HBM GB/s", "value": round(nbytes / t / 1e9, 2), "unit": "GB/s",
+            "frac_of_8TBs": round(nbytes / t / 8e12, 4), "ms": round(t * 1e3, 5), "bytes": nbytes,
+            "config": {"workload": "llama8b_fp8_decode_b32_s4096", "batch": B, "keys": 4097, "T": 1,
+                       "cache": "e4m3, one scale per kv head"}}
+
+
 def run_ragged(torch, seed=4, reps=20):
     """Ragged batch: 64 rows, log-uniform lengths in [1, 32000], n_new in {0, 1, 4, 256}, T=256."""
     from gqa_attention_preallocated_amd import KVCache, gqa_attention
@@ -433,7 +460,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "window", "cpu"],
+    ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "window", "fp8", "cpu"],
                     default=None,
                     help="time one workload only (for profiling); prints its own JSON line")
     ap.add_argument("--copy-probe", action="store_true",
@@ -467,8 +494,9 @@ def main():
     if args.only == "ragged":
         print(json.dumps({"ragged": [run_ragged(torch, seed) for seed in (4, 5, 6)]}), flush=True)
         return
-    if args.only in ("prefill", "verify", "append", "window"):
-        fn = {"prefill": run_prefill, "verify": run_verify, "append": run_append, "window": run_window}[args.only]
+    if args.only in ("prefill", "verify", "append", "window", "fp8"):
+        fn = {"prefill": run_prefill, "verify": run_verify, "append": run_append, "window": run_window,
+              "fp8": run_fp8}[args.only]
         print(json.dumps({args.only: fn(torch)}), flush=True)
         return
     res = run_decode(torch, args.steps, args.warmup)

@@ -60,10 +60,14 @@ class KVCache:
     multiple of 64) that keeps only the latest tokens, and attention sees the
     last W positions ([MASK] "A strong answer", the reversal); lengths are then
     absolute positions and may exceed ``max_len``.
+
+    With ``fp8_scales=(k_scale, v_scale)`` (one float per KV head each) K and
+    V are stored as E4M3 codes (``k``/``v`` are uint8 tensors) and read back
+    dequantized ([CH16] exercise 4); inputs and outputs stay bfloat16.
     """
 
     def __init__(self, batch, kv_heads, max_len, head_dim, dtype=torch.bfloat16, device="cuda",
-                 device_lens=True, window=None):
+                 device_lens=True, window=None, fp8_scales=None):
         if dtype not in _DTYPES:
             raise ValueError(f"dtype {dtype} not supported (float32 or bfloat16)")
         self._lib = _lib.load()
@@ -71,8 +75,11 @@ class KVCache:
         if device.type != "cuda":
             raise ValueError("the cache lives in GPU memory (device='cuda')")
         shape = (batch, kv_heads, max_len, head_dim)
-        self.k = torch.zeros(shape, dtype=dtype, device=device)
-        self.v = torch.zeros(shape, dtype=dtype, device=device)
+        if fp8_scales is not None and (dtype != torch.bfloat16 or window is not None):
+            raise ValueError("an E4M3 cache takes bfloat16 inputs and has no window")
+        store = torch.uint8 if fp8_scales is not None else dtype
+        self.k = torch.zeros(shape, dtype=store, device=device)
+        self.v = torch.zeros(shape, dtype=store, device=device)
         self.lens_dev = torch.zeros(max(batch, 1), dtype=torch.int32, device=device) if device_lens else None
         self.dtype = dtype
         self.batch, self.kv_heads, self.max_len, self.head_dim = shape
@@ -82,7 +89,16 @@ class KVCache:
         bufs = (ctypes.c_void_p(self.k.data_ptr()), ctypes.c_void_p(self.v.data_ptr()),
                 ctypes.c_void_p(self.lens_dev.data_ptr() if device_lens else 0))
         with torch.cuda.device(device):
-            if window is None:
+            if fp8_scales is not None:
+                ks, vs = ([float(x) for x in sc] for sc in fp8_scales)
+                if len(ks) != kv_heads or len(vs) != kv_heads:
+                    raise ValueError("fp8_scales needs one K and one V scale per KV head")
+                self.fp8_scales = (ks, vs)
+                st = self._lib.kv_cache_create_fp8(batch, kv_heads, max_len, head_dim,
+                                                   (ctypes.c_float * max(kv_heads, 1))(*ks),
+                                                   (ctypes.c_float * max(kv_heads, 1))(*vs), *bufs,
+                                                   _stream_ptr(), ctypes.byref(h))
+            elif window is None:
                 st = self._lib.kv_cache_create(batch, kv_heads, max_len, head_dim, _DTYPES[dtype], *bufs,
                                                _stream_ptr(), ctypes.byref(h))
             else:

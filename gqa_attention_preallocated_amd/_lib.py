@@ -25,7 +25,7 @@ KV_DTYPE_BF16 = 1
 EXPORTED = (
     "kv_cache_create", "kv_cache_destroy", "kv_append", "gqa_attention_workspace_size",
     "gqa_attention", "kv_truncate", "kv_get_lens", "kv_cache_bytes", "kv_live_bytes",
-    "kv_last_error", "kv_cache_set_policy", "kv_cache_create_ring",
+    "kv_last_error", "kv_cache_set_policy", "kv_cache_create_ring", "kv_cache_create_fp8",
 )
 
 _lib = None
@@ -49,6 +49,9 @@ def load():
     lib.kv_cache_create.restype = ctypes.c_int
     lib.kv_cache_create_ring.argtypes = [I32, I32, I32, I32, ctypes.c_int, I32, P, P, P, P, ctypes.POINTER(P)]
     lib.kv_cache_create_ring.restype = ctypes.c_int
+    FP = ctypes.POINTER(ctypes.c_float)
+    lib.kv_cache_create_fp8.argtypes = [I32, I32, I32, I32, FP, FP, P, P, P, P, ctypes.POINTER(P)]
+    lib.kv_cache_create_fp8.restype = ctypes.c_int
     lib.kv_cache_destroy.argtypes = [P]
     lib.kv_cache_destroy.restype = None
     lib.kv_append.argtypes = [P, P, P, I32, I32P, P]

@@ -29,7 +29,10 @@ using namespace gqakv;
 struct kv_cache {
     int32_t batch, kv_heads, max_len, head_dim;
     kv_dtype dtype;
-    int32_t elem_bytes;
+    int32_t elem_bytes;          // bytes of one cached K or V element
+    int32_t io_bytes;            // bytes of one q / out / k_new / v_new element
+    std::vector<float> k_scale, v_scale;   // E4M3 caches: per KV head
+    std::vector<float> k_inv, v_inv;       // float32 1 / scale, used by the append
     void *k, *v;
     int32_t *lens_dev;
     std::vector<int32_t> lens;   // host copy, authoritative, updated at enqueue
@@ -273,7 +276,7 @@ void fill_attn_rows(const std::vector<RowPlan> &rows, size_t lo, size_t hi, int 
 
 kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim, kv_dtype dtype,
                        void *k_buf, void *v_buf, int32_t *lens_dev, void *stream, bool ring, int32_t window,
-                       kv_cache **out);
+                       const float *k_scale, const float *v_scale, kv_cache **out);
 
 // Ring caches: the lowest position a row of this length still holds, and the
 // lowest key a query at position pos sees ([MASK] "A strong answer", reversal).
@@ -288,8 +291,26 @@ extern "C" {
 kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim,
                           kv_dtype dtype, void *k_buf, void *v_buf, int32_t *lens_dev, void *stream,
                           kv_cache **out) {
+    if (dtype == KV_DTYPE_FP8_E4M3)
+        return fail(KV_ERR_UNSUPPORTED, "an E4M3 cache needs its scales: use kv_cache_create_fp8");
     return create_cache(batch, kv_heads, max_len, head_dim, dtype, k_buf, v_buf, lens_dev, stream, false,
-                        kNoWindow, out);
+                        kNoWindow, nullptr, nullptr, out);
+}
+
+kv_status kv_cache_create_fp8(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim,
+                              const float *k_scale, const float *v_scale, void *k_buf, void *v_buf,
+                              int32_t *lens_dev, void *stream, kv_cache **out) {
+    if (out == nullptr) return fail(KV_ERR_INVALID_ARG, "out is null");
+    *out = nullptr;
+    if (kv_heads > kMaxScaleHeads)
+        return fail(KV_ERR_UNSUPPORTED, "an E4M3 cache supports at most %d kv heads", kMaxScaleHeads);
+    if (kv_heads > 0 && (k_scale == nullptr || v_scale == nullptr))
+        return fail(KV_ERR_INVALID_ARG, "k_scale/v_scale is null");
+    for (int h = 0; h < kv_heads; ++h)
+        if (!(std::isfinite(k_scale[h]) && k_scale[h] > 0.f && std::isfinite(v_scale[h]) && v_scale[h] > 0.f))
+            return fail(KV_ERR_INVALID_ARG, "kv head %d: scales must be finite and positive", h);
+    return create_cache(batch, kv_heads, max_len, head_dim, KV_DTYPE_FP8_E4M3, k_buf, v_buf, lens_dev, stream,
+                        false, kNoWindow, k_scale, v_scale, out);
 }
 
 kv_status kv_cache_create_ring(int32_t batch, int32_t kv_heads, int32_t capacity, int32_t head_dim,
@@ -301,8 +322,9 @@ kv_status kv_cache_create_ring(int32_t batch, int32_t kv_heads, int32_t capacity
         return fail(KV_ERR_INVALID_ARG, "ring capacity %d is not a positive multiple of %d", capacity, kRingAlign);
     if (window < 1 || window > capacity)
         return fail(KV_ERR_INVALID_ARG, "window %d outside 1..capacity %d", window, capacity);
+    if (dtype == KV_DTYPE_FP8_E4M3) return fail(KV_ERR_UNSUPPORTED, "ring caches hold float32 or bfloat16");
     return create_cache(batch, kv_heads, capacity, head_dim, dtype, k_buf, v_buf, lens_dev, stream, true, window,
-                        out);
+                        nullptr, nullptr, out);
 }
 
 }  // extern "C"
@@ -310,10 +332,10 @@ kv_status kv_cache_create_ring(int32_t batch, int32_t kv_heads, int32_t capacity
 namespace {
 kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim, kv_dtype dtype,
                        void *k_buf, void *v_buf, int32_t *lens_dev, void *stream, bool ring, int32_t window,
-                       kv_cache **out) {
+                       const float *k_scale, const float *v_scale, kv_cache **out) {
     if (out == nullptr) return fail(KV_ERR_INVALID_ARG, "out is null");
     *out = nullptr;
-    if (dtype != KV_DTYPE_F32 && dtype != KV_DTYPE_BF16)
+    if (dtype != KV_DTYPE_F32 && dtype != KV_DTYPE_BF16 && dtype != KV_DTYPE_FP8_E4M3)
         return fail(KV_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
     if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
         return fail(KV_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", head_dim);
@@ -332,7 +354,16 @@ kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t
     c->max_len = max_len;
     c->head_dim = head_dim;
     c->dtype = dtype;
-    c->elem_bytes = dtype == KV_DTYPE_F32 ? 4 : 2;
+    c->elem_bytes = dtype == KV_DTYPE_F32 ? 4 : (dtype == KV_DTYPE_BF16 ? 2 : 1);
+    c->io_bytes = dtype == KV_DTYPE_F32 ? 4 : 2;
+    if (dtype == KV_DTYPE_FP8_E4M3) {
+        c->k_scale.assign(k_scale, k_scale + kv_heads);
+        c->v_scale.assign(v_scale, v_scale + kv_heads);
+        for (int h = 0; h < kv_heads; ++h) {
+            c->k_inv.push_back(1.0f / k_scale[h]);
+            c->v_inv.push_back(1.0f / v_scale[h]);
+        }
+    }
     c->k = k_buf;
     c->v = v_buf;
     c->lens_dev = lens_dev;
@@ -397,7 +428,7 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
     std::vector<int> rows;
     for (int b = 0; b < c->batch; ++b)
         if (n_new[b] > 0) rows.push_back(b);
-    const int64_t row_bytes = (int64_t)c->head_dim * c->elem_bytes;
+    const int64_t row_bytes = (int64_t)c->head_dim * c->io_bytes;      // of k_new / v_new
     for (size_t lo = 0; lo < rows.size(); lo += kMaxRows) {
         AppendArgs a{};
         a.k = c->k;
@@ -406,6 +437,11 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
         a.v_new = v_new;
         a.lens_dev = c->lens_dev;
         a.row_bytes = row_bytes;
+        a.quant = c->dtype == KV_DTYPE_FP8_E4M3;
+        for (size_t h = 0; h < c->k_inv.size(); ++h) {
+            a.k_inv[h] = c->k_inv[h];
+            a.v_inv[h] = c->v_inv[h];
+        }
         a.row_shift = 0;
         while ((int64_t(1) << a.row_shift) < row_bytes) ++a.row_shift;
         a.batch = c->batch;
@@ -488,7 +524,7 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
         z.T = T;
         z.hq = q_heads;
         z.head_dim = c->head_dim;
-        z.row_bytes = (int64_t)c->head_dim * c->elem_bytes;
+        z.row_bytes = (int64_t)c->head_dim * c->io_bytes;
         z.slices = (int32_t)ceil_div((int64_t)T * z.row_bytes, kZeroSlice);
         const size_t hi = std::min(p.pad_rows.size(), lo + kMaxRows);
         z.rows.n_rows = (int32_t)(hi - lo);
@@ -515,6 +551,10 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
     a.max_len = c->max_len;
     a.head_dim = c->head_dim;
     a.window = c->window;
+    for (size_t h = 0; h < c->k_scale.size(); ++h) {
+        a.k_scale[h] = c->k_scale[h];
+        a.v_scale[h] = c->v_scale[h];
+    }
     a.records = p.records;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c->head_dim));
 

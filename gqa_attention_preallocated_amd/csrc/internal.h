@@ -23,15 +23,20 @@ struct AppendTable {
     int32_t block0[kMaxRows + 1];
 };
 
+// E4M3 caches carry one scale per KV head for K and one for V.
+constexpr int kMaxScaleHeads = 64;
+
 struct AppendArgs {
     void *k;                   // cache K [B, Hkv, max_len, d]
     void *v;
     const void *k_new;         // [B, Hkv, T, d]
     const void *v_new;
     int32_t *lens_dev;         // optional
-    int64_t row_bytes;         // d * element size (a power of two)
+    int64_t row_bytes;         // bytes of one k_new row: d * input element size (a power of two)
     int32_t row_shift;         // log2(row_bytes)
     int32_t batch, hkv, max_len, T;
+    int32_t quant;             // 1: bfloat16 inputs stored as E4M3 codes of x * inv scale
+    float k_inv[kMaxScaleHeads], v_inv[kMaxScaleHeads];   // float32 1 / scale per KV head
     AppendTable t;
 };
 
@@ -68,6 +73,7 @@ struct AttnArgs {
     int32_t window;            // keys a query sees: pos - window < key <= pos (kNoWindow: no lower bound)
     int64_t records;           // partial records available in the workspace
     float scale_log2;          // log2(e) / sqrt(d)
+    float k_scale[kMaxScaleHeads], v_scale[kMaxScaleHeads];   // E4M3 caches: code x scale per KV head
     AttnRows rows;
 };
 

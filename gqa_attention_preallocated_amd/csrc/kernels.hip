@@ -32,6 +32,10 @@
 
 namespace gqakv {
 
+// every launch passes its tables by value: keep them inside the kernel-argument space
+static_assert(sizeof(AttnArgs) <= 4096 && sizeof(AppendArgs) <= 4096 && sizeof(CombineArgs) <= 4096 &&
+              sizeof(ZeroArgs) <= 4096, "kernel arguments too large");
+
 typedef __bf16 bf16_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
@@ -172,6 +176,52 @@ template <> struct Op<float> {
     }
 };
 
+// ---------------------------------------------------------------------------
+// cache storage: the kernel's own element type, or (F8) E4M3 codes that are
+// widened exactly to bfloat16 on read ([CH16] exercise 4: dequantize on read;
+// the head's scale is applied to the scores and to the output instead of to
+// every element). The gfx950 conversion is exact for every E4M3 value.
+// ---------------------------------------------------------------------------
+template <typename E, bool F8> struct Stor {
+    using vec = typename Op<E>::vec;
+    using kraw = vec;                                 // K operand as loaded
+    static constexpr int kBytes = Op<E>::kBytes;      // bytes per cached element
+    static constexpr int kLdsPerChunk = 16;           // LDS bytes a 16-byte cache chunk becomes
+    __device__ static inline kraw load_k(const unsigned char *p) {
+        return Op<E>::gload_stream(reinterpret_cast<const E *>(p));
+    }
+    __device__ static inline kraw zero_k() { return Op<E>::zero(); }
+    __device__ static inline vec widen_k(const kraw &r) { return r; }
+    __device__ static inline void stage(unsigned char *dst, const uint4 &raw) {
+        *reinterpret_cast<uint4 *>(dst) = raw;
+    }
+};
+
+template <> struct Stor<bf16_t, true> {
+    using vec = bf16x8;
+    typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+    using kraw = uint2;                               // 8 codes
+    static constexpr int kBytes = 1;
+    static constexpr int kLdsPerChunk = 32;           // 16 codes -> 16 bfloat16
+    __device__ static inline kraw load_k(const unsigned char *p) {
+        const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+        return make_uint2(t.x, t.y);
+    }
+    __device__ static inline kraw zero_k() { return make_uint2(0, 0); }
+    // codes in bytes 0,1 (HI false) or 2,3 (HI true) of w -> two bfloat16 (exact; scale 1)
+    template <bool HI> __device__ static inline uint32_t widen2(uint32_t w) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    }
+    __device__ static inline uint4 widen4x2(uint32_t a, uint32_t b) {
+        return make_uint4(widen2<false>(a), widen2<true>(a), widen2<false>(b), widen2<true>(b));
+    }
+    __device__ static inline vec widen_k(const kraw &r) { return __builtin_bit_cast(vec, widen4x2(r.x, r.y)); }
+    __device__ static inline void stage(unsigned char *dst, const uint4 &raw) {
+        reinterpret_cast<uint4 *>(dst)[0] = widen4x2(raw.x, raw.y);
+        reinterpret_cast<uint4 *>(dst)[1] = widen4x2(raw.z, raw.w);
+    }
+};
+
 // 2^x with the hardware instruction alone. exp2f adds a range fix for
 // results below 2^-126; a probability that small is zero for every purpose here.
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -197,6 +247,21 @@ __device__ inline float wave_sum_across_groups(float v) {
 // written in place at the row's current length; nothing else moves). In a ring
 // cache token p lands in slot p mod max_len ([CH16] exercise 3).
 // ---------------------------------------------------------------------------
+// E4M3 codes of 8 bfloat16 values (a 16-byte chunk) times inv, in memory order
+__device__ inline uint32_t quant4(uint32_t lo, uint32_t hi, float inv) {
+    auto f = [&](uint32_t bits) {                 // bfloat16 -> float32 is exact
+        const float y = __uint_as_float(bits << 16) * inv;
+        return fminf(fmaxf(y, -448.f), 448.f);    // saturate: the conversion rounds to nearest even
+    };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(f(lo & 0xffffu), f(lo >> 16), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(f(hi & 0xffffu), f(hi >> 16), w, true);
+    return (uint32_t)w;
+}
+
+__device__ inline uint2 quant8(const uint4 &x, float inv) {
+    return make_uint2(quant4(x.x, x.y, inv), quant4(x.z, x.w, inv));
+}
+
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int r = find_row(a.t.block0, a.t.n_rows, blockIdx.x);
     const int local = blockIdx.x - a.t.block0[r];
@@ -214,11 +279,20 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         int slot = a.t.slot0[r] + tok;
         if (slot >= a.max_len) slot -= a.max_len;
         const int64_t src = head * a.T * a.row_bytes + off;
-        const int64_t dst = ((head * a.max_len + slot) << a.row_shift) + (off & (a.row_bytes - 1));
         const uint4 kx = *reinterpret_cast<const uint4 *>((const char *)a.k_new + src);
         const uint4 vx = *reinterpret_cast<const uint4 *>((const char *)a.v_new + src);
-        *reinterpret_cast<uint4 *>((char *)a.k + dst) = kx;
-        *reinterpret_cast<uint4 *>((char *)a.v + dst) = vx;
+        if (!a.quant) {
+            const int64_t dst = ((head * a.max_len + slot) << a.row_shift) + (off & (a.row_bytes - 1));
+            *reinterpret_cast<uint4 *>((char *)a.k + dst) = kx;
+            *reinterpret_cast<uint4 *>((char *)a.v + dst) = vx;
+        } else {
+            // E4M3 cache ([CH16] exercise 4): 8 bfloat16 in, 8 codes out, each
+            // the code of x * (1 / scale) in float32, saturated to +-448,
+            // rounded to the nearest code (ties to even)
+            const int64_t dst = ((head * a.max_len + slot) << (a.row_shift - 1)) + ((off & (a.row_bytes - 1)) >> 1);
+            *reinterpret_cast<uint2 *>((char *)a.k + dst) = quant8(kx, a.k_inv[kvh]);
+            *reinterpret_cast<uint2 *>((char *)a.v + dst) = quant8(vx, a.v_inv[kvh]);
+        }
     }
     // the row's new length becomes visible to later kernels in stream order
     if (a.lens_dev != nullptr && local == 0 && threadIdx.x == 0) a.lens_dev[b] = a.t.start[r] + a.t.n[r];
@@ -323,17 +397,20 @@ __device__ inline void softmax_tile(const float (&v)[N], float c, ColState &st, 
 // merge their partial results through LDS (reusing the V staging space), so a
 // split-free row needs no second pass.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int NSUB, int W>
+template <typename E, int D, int NSUB, int W, bool F8>
 __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     using O = Op<E>;
+    using S = Stor<E, F8>;
     using vec = typename O::vec;
+    using kraw = typename S::kraw;
     constexpr int KT = kDecodeKeyTile;            // 32 keys per tile
     constexpr int KC = D >= 32 ? D / 32 : 1;      // 32-wide chunks of d
     constexpr int NB = D / 16;                    // 16-row blocks of O^T
     constexpr int C = 16 * NSUB;
-    constexpr int ROWB = D * O::kBytes;
+    constexpr int ROWB = D * O::kBytes;           // LDS bytes of one V row (compute type)
     constexpr int RS = ROWB + O::kPad;            // padded LDS row: conflict-free transposed reads
-    constexpr int CPK = ROWB / 16;                // 16-byte chunks per key row
+    constexpr int CROWB = D * S::kBytes;          // cache bytes of one K or V row
+    constexpr int CPK = CROWB / 16;               // 16-byte cache chunks per key row
     constexpr int VCH = (KT * CPK + 63) / 64;     // V chunks per lane per tile
     constexpr int STAGE = KT * RS;                // per-wave V staging bytes
     constexpr int PSTR = D + 4;                   // floats per column in the merge area
@@ -354,6 +431,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     const int w_end = it.k_end;
     constexpr int step = W * KT;
 
+    // k-slots of lane group lg in 32-wide chunk kc: d = dmap(kc) .. +7. The
+    // contraction over d is a sum, so Q and K only need the same map: for an
+    // E4M3 cache with an even chunk count, chunks 2j and 2j+1 take the two
+    // halves of 16 contiguous codes (one 16-byte load per lane for both)
+    constexpr bool KPAIR = F8 && KC % 2 == 0;
+    auto dmap = [&](int kc) { return KPAIR ? 64 * (kc >> 1) + 16 * lg + 8 * (kc & 1) : kc * 32 + lg * 8; };
+
     // ---- columns: absolute positions and Q operands (B of S^T)
     int pos[NSUB];
     vec qop[NSUB][KC];
@@ -364,14 +448,18 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         const E *qp = pos[s] >= 0 ? column_q<E>(a, it, col, D) : nullptr;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-            const int d0 = kc * 32 + lg * 8;
+            const int d0 = dmap(kc);
             qop[s][kc] = (qp != nullptr && d0 < D) ? O::gload(qp + d0) : O::zero();
         }
     }
 
     const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
-    const E *kbase = reinterpret_cast<const E *>(a.k) + head * a.max_len * D;
-    const E *vbase = reinterpret_cast<const E *>(a.v) + head * a.max_len * D;
+    const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k) + head * a.max_len * CROWB;
+    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v) + head * a.max_len * CROWB;
+    // an E4M3 cache stands for code x scale of the head: the K scale joins the
+    // score scale, the V scale multiplies the output
+    const float score_c = F8 ? a.scale_log2 * a.k_scale[it.kvh] : a.scale_log2;
+    const float out_c = F8 ? a.v_scale[it.kvh] : 1.f;
 
     f32x4 acc[NSUB][NB];
     ColState st[NSUB];
@@ -383,22 +471,37 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         for (int nb = 0; nb < NB; ++nb) acc[s][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- prefetch: the next tile is in flight while one is computed (one
-    //      tile is 64 VGPRs a lane; a second set would halve the waves a CU holds)
-    vec kA[2][KC];
-    uint4 vA[VCH];
+    // ---- prefetch: the next tile is in flight while one is computed (a
+    //      bfloat16 tile is 64 VGPRs a lane; a second set would cost occupancy).
+    //      An E4M3 tile is half the bytes, so two are kept in flight to keep
+    //      the same bytes outstanding per CU (up to 32 columns; wider items
+    //      have no registers to spare).
+    constexpr int PF = (F8 && NSUB <= 2) ? 2 : 1;
+    kraw kA[2][KC], kB[2][KC];
+    uint4 vA[VCH], vB[VCH];
     // key position j lives in slot j mod max_len; a tile never wraps (ring
     // capacities are multiples of kRingAlign, tiles start at multiples of KT)
-    auto load_tile = [&](vec (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
+    auto load_tile = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
         const int slot = tile % a.max_len;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int key = ks * 16 + lr;
             const bool ok = tile + key < w_end;
+            if constexpr (KPAIR) {
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const int d0 = kc * 32 + lg * 8;
-                kop[ks][kc] = (ok && d0 < D) ? O::gload_stream(kbase + (int64_t)(slot + key) * D + d0) : O::zero();
+                for (int j = 0; j < KC / 2; ++j) {
+                    const uint4 w = ok ? load_stream(kbase + (int64_t)(slot + key) * CROWB + dmap(2 * j))
+                                       : make_uint4(0, 0, 0, 0);
+                    kop[ks][2 * j] = make_uint2(w.x, w.y);
+                    kop[ks][2 * j + 1] = make_uint2(w.z, w.w);
+                }
+            } else {
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const int d0 = dmap(kc);
+                    kop[ks][kc] = (ok && d0 < D) ? S::load_k(kbase + (int64_t)(slot + key) * CROWB + d0 * S::kBytes)
+                                                 : S::zero_k();
+                }
             }
         }
 #pragma unroll
@@ -406,9 +509,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
             const int c = lane + 64 * i;
             const int key = c / CPK, part = c % CPK;
             const bool ok = (c < KT * CPK) && (tile + key < w_end);
-            vreg[i] = ok ? load_stream(reinterpret_cast<const unsigned char *>(vbase + (int64_t)(slot + key) * D) +
-                                       part * 16)
-                         : make_uint4(0, 0, 0, 0);
+            vreg[i] = ok ? load_stream(vbase + (int64_t)(slot + key) * CROWB + part * 16) : make_uint4(0, 0, 0, 0);
         }
     };
 
@@ -423,28 +524,32 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     for (int s = 0; s < NSUB; ++s) lo_key[s] = pos[s] - a.window + 1 > 0 ? pos[s] - a.window + 1 : 0;
 
     // compute the tile held in (kop, vreg), refilling the set with the next tile
-    auto process = [&](vec (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
-        // V tile into this wave's LDS stage (row-major, padded)
+    auto process = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
+        // V tile into this wave's LDS stage (row-major, padded, compute type)
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int c = lane + 64 * i;
             if (c < KT * CPK) {
                 const int key = c / CPK, part = c % CPK;
-                *reinterpret_cast<uint4 *>(lds + key * RS + part * 16) = vreg[i];
+                S::stage(lds + key * RS + part * S::kLdsPerChunk, vreg[i]);
             }
         }
         // ---- S^T = K Q^T for the 32 keys
         f32x4 sc[NSUB][2];
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s)
+        for (int ks = 0; ks < 2; ++ks) {
+            vec kv[KC];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int kc = 0; kc < KC; ++kc) kv[kc] = S::widen_k(kop[ks][kc]);
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) {
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kc = 0; kc < KC; ++kc) c = O::mma(kop[ks][kc], qop[s][kc], c);
+                for (int kc = 0; kc < KC; ++kc) c = O::mma(kv[kc], qop[s][kc], c);
                 sc[s][ks] = c;
             }
-        if (tile + step < w_end) load_tile(kop, vreg, tile + step);
+        }
+        if (tile + PF * step < w_end) load_tile(kop, vreg, tile + PF * step);
 
         // ---- mask (only tiles that straddle the diagonal or the range end),
         //      online softmax in log2 units
@@ -465,7 +570,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
                     v[j] = (off < lim && off >= lim_lo) ? v[j] : -INFINITY;
                 }
             }
-            softmax_step<NB>(v, a.scale_log2, st[s], acc[s], p[s]);
+            softmax_step<NB>(v, score_c, st[s], acc[s], p[s]);
         }
 
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's V stores have landed
@@ -483,7 +588,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     };
 
     if (w_begin < w_end) load_tile(kA, vA, w_begin);
-    for (int tile = w_begin; tile < w_end; tile += step) process(kA, vA, tile);
+    if constexpr (PF == 2) {
+        if (w_begin + step < w_end) load_tile(kB, vB, w_begin + step);
+        for (int tile = w_begin; tile < w_end; tile += 2 * step) {
+            process(kA, vA, tile);
+            if (tile + step < w_end) process(kB, vB, tile + step);
+        }
+    } else {
+        for (int tile = w_begin; tile < w_end; tile += step) process(kA, vA, tile);
+    }
 
     // ---- merge the W waves' partials in LDS, one 16-column subtile at a time
     float *part = reinterpret_cast<float *>(lds_all);                 // [W][16][PSTR]
@@ -517,6 +630,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
                 o[0] += wt * x.x; o[1] += wt * x.y; o[2] += wt * x.z; o[3] += wt * x.w;
                 L += wt * ml.y;
             }
+            o *= out_c;                            // the V scale of an E4M3 cache (1 otherwise)
             if (it.rec0 < 0) {
                 E *op = column_out<E>(a, it, col, D) + d;
                 O::store4(op, o * (L > 0.f ? 1.f / L : 0.f));
@@ -536,18 +650,20 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 // or below the first query's position are not masked; only tiles straddling
 // the diagonal compare indices ([MASK] "A strong answer", tiled-kernel rule).
 // ---------------------------------------------------------------------------
-template <typename E, int D>
+template <typename E, int D, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(AttnArgs a) {
     using O = Op<E>;
+    using S = Stor<E, F8>;
     using vec = typename O::vec;
     constexpr int KT = kPrefillKeyTile;           // 64 keys per tile
     constexpr int KC = D >= 32 ? D / 32 : 1;
     constexpr int NB = D / 16;
     constexpr int C = kPrefillCols;               // 128 columns per item
     constexpr int NS = 2;                         // 16-column subtiles per wave
-    constexpr int ROWB = D * O::kBytes;
+    constexpr int ROWB = D * O::kBytes;           // LDS bytes of a K or V row (compute type)
     constexpr int RS = ROWB + O::kPad;
-    constexpr int CPK = ROWB / 16;
+    constexpr int CROWB = D * S::kBytes;          // cache bytes of a row
+    constexpr int CPK = CROWB / 16;               // 16-byte cache chunks per row
     constexpr int TILE_BYTES = KT * RS;
     constexpr int PCH = (KT * CPK + 255) / 256;   // 16-byte chunks per thread per tensor
     __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE_BYTES];
@@ -587,10 +703,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
 
     const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
-    const unsigned char *kbase = reinterpret_cast<const unsigned char *>(
-        reinterpret_cast<const E *>(a.k) + head * a.max_len * D);
-    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(
-        reinterpret_cast<const E *>(a.v) + head * a.max_len * D);
+    const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k) + head * a.max_len * CROWB;
+    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v) + head * a.max_len * CROWB;
+    // an E4M3 cache: the K scale joins the score scale, the V scale the output
+    const float score_c = F8 ? a.scale_log2 * a.k_scale[it.kvh] : a.scale_log2;
+    const float out_c = F8 ? a.v_scale[it.kvh] : 1.f;
 
     // acc[s][0..NB-1]: O^T rows; acc[s][NB]: a 16-row block whose A operand is
     // all ones, so each of its rows is the column's running sum of p (the
@@ -612,16 +729,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // key position j lives in slot j mod max_len; no tile wraps (see decode)
     auto load = [&](uint4 (&reg)[PCH], const unsigned char *base, int tile) {
         const __amdgpu_buffer_rsrc_t r =
-            buffer_view(base + (int64_t)(tile % a.max_len) * ROWB, imin(it.k_end - tile, KT) * ROWB);
+            buffer_view(base + (int64_t)(tile % a.max_len) * CROWB, imin(it.k_end - tile, KT) * CROWB);
 #pragma unroll
         for (int i = 0; i < PCH; ++i) reg[i] = buffer_load_stream(r, (tid + 256 * i) * 16);
     };
+    // into LDS in the compute type (an E4M3 chunk of 16 codes becomes 32 bytes)
     auto store = [&](const uint4 (&reg)[PCH], unsigned char *dst) {
 #pragma unroll
         for (int i = 0; i < PCH; ++i) {
             const int c = tid + 256 * i;
-            if ((KT * CPK) % 256 == 0 || c < KT * CPK)
-                *reinterpret_cast<uint4 *>(dst + (c / CPK) * RS + (c % CPK) * 16) = reg[i];
+            if ((KT * CPK) % 256 == 0 || c < KT * CPK) S::stage(dst + (c / CPK) * RS + (c % CPK) * S::kLdsPerChunk, reg[i]);
         }
     };
     // S^T of one 64-key tile for the wave's 32 columns (32 MFMAs)
@@ -688,7 +805,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 for (int ks = 0; ks < 2; ++ks)
                     t = fmaxf(t, fmaxf(fmaxf(sc[ch][s][ks][0], sc[ch][s][ks][1]),
                                        fmaxf(sc[ch][s][ks][2], sc[ch][s][ks][3])));
-            tmax[s] = wave_max_across_groups(t) * a.scale_log2;
+            tmax[s] = wave_max_across_groups(t) * score_c;
         }
     };
     // Software pipeline over the item's key tiles, two matrix phases per tile,
@@ -736,7 +853,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 } else {
                     const int s = t - 8;
                     const float m4 = fmaxf(fmaxf(part[s][0], part[s][1]), fmaxf(part[s][2], part[s][3]));
-                    tmax[s] = wave_max_across_groups(m4) * a.scale_log2;
+                    tmax[s] = wave_max_across_groups(m4) * score_c;
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -772,8 +889,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             // probabilities: step g covers (ch', s') = (g / 8, (g / 4) % 2), elements 2 (g % 4) .. +1
             {
                 const int pc = g >> 3, ps = (g >> 2) & 1, j = (g & 3) * 2;
-                O::set_pair(pb[pc][ps], j, fast_exp2(fmaf(sc[pc][ps][j >> 2][j & 3], a.scale_log2, -m_use[ps])),
-                            fast_exp2(fmaf(sc[pc][ps][(j + 1) >> 2][(j + 1) & 3], a.scale_log2, -m_use[ps])));
+                O::set_pair(pb[pc][ps], j, fast_exp2(fmaf(sc[pc][ps][j >> 2][j & 3], score_c, -m_use[ps])),
+                            fast_exp2(fmaf(sc[pc][ps][(j + 1) >> 2][(j + 1) & 3], score_c, -m_use[ps])));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -849,7 +966,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         if (pos[s] < 0) continue;
         if (it.rec0 < 0) {
             E *op = column_out<E>(a, it, col, D);
-            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const float inv = l > 0.f ? out_c / l : 0.f;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) O::store4(op + nb * 16 + lg * 4, acc[s][nb] * inv);
         } else {
@@ -858,7 +975,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
                 *reinterpret_cast<float4 *>(ap + nb * 16 + lg * 4) =
-                    make_float4(acc[s][nb][0], acc[s][nb][1], acc[s][nb][2], acc[s][nb][3]);
+                    make_float4(acc[s][nb][0] * out_c, acc[s][nb][1] * out_c, acc[s][nb][2] * out_c,
+                                acc[s][nb][3] * out_c);
             if (lg == 0) *reinterpret_cast<float2 *>(a.ws_ml + rec * 2) = make_float2(st[s].m, l);
         }
     }
@@ -967,43 +1085,49 @@ hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename E, int D>
+// dtype codes (kv_dtype): 0 float32, 1 bfloat16, 2 E4M3 cache with bfloat16 q/out
+template <typename E, int D, bool F8>
 static hipError_t decode_d(int nsub, const AttnArgs &a, hipStream_t s) {
     constexpr int W = kDecodeWaves;
     const dim3 grid(a.rows.total_items), block(64 * W);
     switch (nsub) {
-        case 1: hipLaunchKernelGGL((decode_kernel<E, D, 1, W>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<E, D, 2, W>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<E, D, 4, W>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<E, D, 1, W, F8>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<E, D, 2, W, F8>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<E, D, 4, W, F8>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <typename E>
+template <typename E, bool F8>
 static hipError_t decode_e(int head_dim, int nsub, const AttnArgs &a, hipStream_t s) {
     switch (head_dim) {
-        case 16: return decode_d<E, 16>(nsub, a, s);
-        case 32: return decode_d<E, 32>(nsub, a, s);
-        case 64: return decode_d<E, 64>(nsub, a, s);
-        case 128: return decode_d<E, 128>(nsub, a, s);
+        case 16: return decode_d<E, 16, F8>(nsub, a, s);
+        case 32: return decode_d<E, 32, F8>(nsub, a, s);
+        case 64: return decode_d<E, 64, F8>(nsub, a, s);
+        case 128: return decode_d<E, 128, F8>(nsub, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t s) {
     if (a.rows.total_items <= 0) return hipSuccess;
-    return dtype == 0 ? decode_e<float>(head_dim, nsub, a, s) : decode_e<bf16_t>(head_dim, nsub, a, s);
+    switch (dtype) {
+        case 0: return decode_e<float, false>(head_dim, nsub, a, s);
+        case 1: return decode_e<bf16_t, false>(head_dim, nsub, a, s);
+        case 2: return decode_e<bf16_t, true>(head_dim, nsub, a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
-template <typename E>
+template <typename E, bool F8>
 static hipError_t prefill_e(int head_dim, const AttnArgs &a, hipStream_t s) {
     const dim3 grid(a.rows.total_items), block(256);
     switch (head_dim) {
-        case 16: hipLaunchKernelGGL((prefill_kernel<E, 16>), grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((prefill_kernel<E, 32>), grid, block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((prefill_kernel<E, 64>), grid, block, 0, s, a); break;
-        case 128: hipLaunchKernelGGL((prefill_kernel<E, 128>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<E, 16, F8>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((prefill_kernel<E, 32, F8>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((prefill_kernel<E, 64, F8>), grid, block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((prefill_kernel<E, 128, F8>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1011,7 +1135,12 @@ static hipError_t prefill_e(int head_dim, const AttnArgs &a, hipStream_t s) {
 
 hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t s) {
     if (a.rows.total_items <= 0) return hipSuccess;
-    return dtype == 0 ? prefill_e<float>(head_dim, a, s) : prefill_e<bf16_t>(head_dim, a, s);
+    switch (dtype) {
+        case 0: return prefill_e<float, false>(head_dim, a, s);
+        case 1: return prefill_e<bf16_t, false>(head_dim, a, s);
+        case 2: return prefill_e<bf16_t, true>(head_dim, a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <typename E>

@@ -58,7 +58,9 @@ typedef enum kv_status {
 
 typedef enum kv_dtype {
     KV_DTYPE_F32 = 0,         /* IEEE float32 storage and float32 arithmetic     */
-    KV_DTYPE_BF16 = 1         /* bfloat16 storage, float32 accumulation          */
+    KV_DTYPE_BF16 = 1,        /* bfloat16 storage, float32 accumulation          */
+    KV_DTYPE_FP8_E4M3 = 2     /* E4M3 codes with one scale per KV head; q, out,
+                                 k_new and v_new are bfloat16 (kv_cache_create_fp8) */
 } kv_dtype;
 
 /*
@@ -108,6 +110,27 @@ kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int3
 kv_status kv_cache_create_ring(int32_t batch, int32_t kv_heads, int32_t capacity, int32_t head_dim,
                                kv_dtype dtype, int32_t window, void *k_buf, void *v_buf,
                                int32_t *lens_dev, void *stream, kv_cache **out);
+
+/*
+ * FP8 cache: K and V stored as E4M3 codes with one scale per KV head, read back
+ * dequantized. [CH16] exercise 4 (store the cache in FP8, E4M3 with one scale
+ * per head, and dequantize on read) and "How big is the cache?" (half the
+ * bytes of a bfloat16 cache, which a bandwidth-bound decode reads every step).
+ *   k_buf, v_buf  device, B*Hkv*max_len*d BYTES each, [B, Hkv, max_len, d].
+ *   k_scale, v_scale  HOST float[kv_heads], finite and > 0, copied here: a
+ *                 code c of KV head h stands for c * scale[h] (E4M3 is the
+ *                 OCP format: bias 7, largest finite 448, no infinities).
+ * kv_append then takes bfloat16 k_new/v_new and stores, for each element x of
+ * head h, the E4M3 code of x * (1 / scale[h]) computed in float32, saturated
+ * to +-448 and rounded to the nearest code, ties to even. gqa_attention takes
+ * bfloat16 q and writes bfloat16 out; scores use the dequantized keys and the
+ * output the dequantized values (every E4M3 value is exact in bfloat16). At
+ * most 64 KV heads. Other arguments, errors and the linear-cache rules as
+ * kv_cache_create (kv_cache_create refuses this dtype).
+ */
+kv_status kv_cache_create_fp8(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim,
+                              const float *k_scale, const float *v_scale, void *k_buf, void *v_buf,
+                              int32_t *lens_dev, void *stream, kv_cache **out);
 
 /* Release the handle (never the caller's buffers). NULL is ignored. */
 void kv_cache_destroy(kv_cache *c);

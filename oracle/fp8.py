@@ -79,10 +79,20 @@ def encode_one(y):
 
 
 def quantize(x_f32, inv_scale_f32):
-    """Codes of float32 values x times the float32 reciprocal scale (both in float32)."""
+    """Codes of float32 values x times the float32 reciprocal scale (the product
+    in float32). The same rule as ``encode_one``, applied to whole arrays: the
+    two finite codes around |y| (after saturation), the nearer one, on a tie
+    the even one; the sign bit from y."""
     y = (np.asarray(x_f32, dtype=np.float32) * np.float32(inv_scale_f32)).astype(np.float32)
-    flat = np.array([encode_one(v) for v in y.reshape(-1)], dtype=np.uint8)
-    return flat.reshape(y.shape)
+    mags = DECODE[:0x7F]
+    a = np.minimum(np.abs(y.astype(np.float64)), E4M3_MAX)
+    hi = np.minimum(np.searchsorted(mags, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    c = np.where(mags[hi] == a, hi,
+                 np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi))))
+    code = (c | (np.signbit(y).astype(np.int64) << 7)).astype(np.uint8)
+    return np.where(np.isnan(y), np.uint8(0x7F), code)
 
 
 class Fp8Cache:

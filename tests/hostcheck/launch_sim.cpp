@@ -133,11 +133,16 @@ hipError_t launch_append(const AppendArgs &a, int n_blocks, hipStream_t) {
             int slot = a.t.slot0[r] + tok;
             if (slot >= a.max_len) slot -= a.max_len;
             const int64_t src = head * a.T * a.row_bytes + off;
-            const int64_t dst = ((head * a.max_len + slot) << a.row_shift) + (off & (a.row_bytes - 1));
+            // a quantizing append writes one code byte per two input bytes
+            const int sh = a.quant ? a.row_shift - 1 : a.row_shift;
+            const int64_t dst = ((head * a.max_len + slot) << sh) + ((off & (a.row_bytes - 1)) >> (a.quant ? 1 : 0));
+            const int wbytes = a.quant ? 8 : 16;
             access((const char *)a.k_new + src, 16, "k_new", "append read k_new");
             access((const char *)a.v_new + src, 16, "v_new", "append read v_new");
-            access((const char *)a.k + dst, 16, "k", "append write K");
-            access((const char *)a.v + dst, 16, "v", "append write V");
+            access((const char *)a.k + dst, wbytes, "k", "append write K");
+            access((const char *)a.v + dst, wbytes, "v", "append write V");
+            if (a.quant && (kvh >= kMaxScaleHeads || !(a.k_inv[kvh] > 0.f) || !(a.v_inv[kvh] > 0.f)))
+                err("append: missing E4M3 scale");
             if (slot < 0 || slot >= a.max_len || slot != (a.t.start[r] + tok) % a.max_len || tok >= a.t.n[r])
                 err("append: write outside the row's new slots");
             g_appended[(uintptr_t)a.k + dst]++;
@@ -160,11 +165,12 @@ hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t) {
     return hipSuccess;
 }
 
-static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem) {
+static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, int cache_elem) {
     ++g_launches;
     const AttnRows &R = a.rows;
     const int D = a.head_dim;
-    const int64_t row_bytes = (int64_t)D * elem;
+    const int64_t row_bytes = (int64_t)D * elem;             // q / out rows
+    const int64_t cache_row = (int64_t)D * cache_elem;       // K / V rows
     if (R.item0[R.n_rows] != R.total_items) err("item0 does not end at total_items");
     const bool windowed = a.window != kNoWindow;
     if (windowed && (a.window < 1 || a.window > a.max_len || a.max_len % kRingAlign != 0))
@@ -199,8 +205,8 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem) {
             const int slot = t0 % a.max_len;
             if (slot + n > a.max_len) err("attention: key tile wraps");
             for (int key : {slot, slot + n - 1}) {
-                access((const char *)a.k + (head * a.max_len + key) * row_bytes, row_bytes, "k", "attention K");
-                access((const char *)a.v + (head * a.max_len + key) * row_bytes, row_bytes, "v", "attention V");
+                access((const char *)a.k + (head * a.max_len + key) * cache_row, cache_row, "k", "attention K");
+                access((const char *)a.v + (head * a.max_len + key) * cache_row, cache_row, "v", "attention V");
             }
         }
         for (int col = 0; col < cols; ++col) {
@@ -228,13 +234,13 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem) {
 
 hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t) {
     if (head_dim != a.head_dim) err("decode: head_dim mismatch");
-    sim_attention(a, 16 * nsub, kDecodeKeyTile, dtype == 0 ? 4 : 2);
+    sim_attention(a, 16 * nsub, kDecodeKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
     return hipSuccess;
 }
 
 hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t) {
     if (head_dim != a.head_dim) err("prefill: head_dim mismatch");
-    sim_attention(a, kPrefillCols, kPrefillKeyTile, dtype == 0 ? 4 : 2);
+    sim_attention(a, kPrefillCols, kPrefillKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
     return hipSuccess;
 }
 

@@ -63,6 +63,21 @@ def test_quantize_uses_the_float32_product():
     assert fp8.quantize(np.array([x]), inv)[0] == fp8.encode_one(np.float32(x * inv))
 
 
+def test_array_quantizer_equals_the_scalar_encoder():
+    """quantize (whole arrays) takes the same decision as encode_one on the tie
+    grid, random values across magnitudes, saturating values and signed zeros."""
+    rng = np.random.default_rng(5)
+    grid = []
+    for c in range(0x7E):
+        lo, hi = fp8.DECODE[c], fp8.DECODE[c + 1]
+        grid += [lo, (lo + hi) / 2, lo + (hi - lo) * 0.3, lo + (hi - lo) * 0.7]
+    x = np.concatenate([grid, rng.standard_normal(5000) * rng.choice([1e-3, 0.1, 3, 80, 900], 5000),
+                        [0.0, 448, 460, 1e9, 2.0 ** -12]]).astype(np.float32)
+    x = np.concatenate([x, -x])
+    want = np.array([fp8.encode_one(v) for v in x], np.uint8)
+    assert np.array_equal(fp8.quantize(x, np.float32(1.0)), want)
+
+
 def test_quantization_error_is_within_half_a_step():
     rng = np.random.default_rng(0)
     x = rng.standard_normal(20000).astype(np.float32) * 3

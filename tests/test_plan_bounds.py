@@ -35,6 +35,8 @@ def sim(tmp_path_factory):
     I32P = ctypes.POINTER(ctypes.c_int32)
     lib.kv_cache_create.argtypes = [I32, I32, I32, I32, ctypes.c_int, P, P, P, P, ctypes.POINTER(P)]
     lib.kv_cache_create_ring.argtypes = [I32, I32, I32, I32, ctypes.c_int, I32, P, P, P, P, ctypes.POINTER(P)]
+    FP = ctypes.POINTER(ctypes.c_float)
+    lib.kv_cache_create_fp8.argtypes = [I32, I32, I32, I32, FP, FP, P, P, P, P, ctypes.POINTER(P)]
     lib.kv_append.argtypes = [P, P, P, I32, I32P, P]
     lib.gqa_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]
     lib.gqa_attention.argtypes = [P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
@@ -64,11 +66,12 @@ class SimCache:
 
     def __init__(self, lib, B, hk, max_len, d, dtype, hq, t_max, window=None):
         self.lib, self.B, self.hk, self.max_len, self.d, self.hq = lib, B, hk, max_len, d, hq
-        self.elem = 4 if dtype == "f32" else 2
+        self.elem = 4 if dtype == "f32" else 2                  # q, out, k_new, v_new
+        cache_elem = {"f32": 4, "bf16": 2, "fp8": 1}[dtype]       # K, V
         lib.hostcheck_reset()
         self.addr = {}
         sizes = {
-            "k": B * hk * max_len * d * self.elem, "v": B * hk * max_len * d * self.elem,
+            "k": B * hk * max_len * d * cache_elem, "v": B * hk * max_len * d * cache_elem,
             "lens": 4 * max(B, 1),
             "k_new": B * hk * t_max * d * self.elem, "v_new": B * hk * t_max * d * self.elem,
             "q": B * hq * t_max * d * self.elem, "out": B * hq * t_max * d * self.elem,
@@ -80,7 +83,10 @@ class SimCache:
             lib.hostcheck_region(base, max(size, 1), name.encode())
         h = ctypes.c_void_p()
         bufs = (ctypes.c_void_p(self.addr["k"]), ctypes.c_void_p(self.addr["v"]), ctypes.c_void_p(self.addr["lens"]))
-        if window is None:
+        if dtype == "fp8":
+            sc = (ctypes.c_float * max(hk, 1))(*([0.05] * hk))
+            st = lib.kv_cache_create_fp8(B, hk, max_len, d, sc, sc, *bufs, None, ctypes.byref(h))
+        elif window is None:
             st = lib.kv_cache_create(B, hk, max_len, d, 0 if dtype == "f32" else 1, *bufs, None, ctypes.byref(h))
         else:
             st = lib.kv_cache_create_ring(B, hk, max_len, d, 0 if dtype == "f32" else 1, window, *bufs, None,
@@ -281,3 +287,22 @@ def test_ring_capacity_and_rollback_rules(sim):
     c.append(65, [65])
     c.attention(65, [65])
     c.check(65)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fp8_random_trials(sim, seed):
+    """E4M3 caches: appends write one code byte per element inside the cache,
+    and attention reads 1-byte rows, at every head dim and kernel selection."""
+    shape, calls = W.trial_spec(seed, head_dims=(16, 32, 64, 128))
+    for policy in [(0, 0), (1, 32), (2, 64)]:
+        _run(sim, shape.batch, shape.kv_heads, shape.group, shape.head_dim, shape.max_len, "fp8", calls, policy)
+
+
+def test_llama_fp8_decode(sim):
+    sh = W.LLAMA8B_DECODE
+    c = SimCache(sim, sh.batch, sh.kv_heads, sh.max_len, sh.head_dim, "fp8", sh.q_heads, 4096)
+    for call in _prefix_calls([4096] * sh.batch):
+        c.append(call["T"], call["n_new"])
+    c.append(1, [1] * sh.batch)
+    assert c.attention(1, [1] * sh.batch) == 0
+    c.check(1)
