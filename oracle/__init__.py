@@ -19,9 +19,11 @@ check it against the pages by eye:
   * ``fp8``        -- an E4M3 cache with one scale per KV head: the format's
                       decoder and round-to-nearest-even encoder, attention on
                       the dequantized values.
+  * ``tree``       -- tree-based speculative verify: each draft node attends
+                      the committed keys and its ancestors (parent pointers).
 
 Where the pages are silent or disagree, the reading taken is stated in the
 docstring of the function that depends on it.
 """
 
-from . import direct, fp8, vectorised, window  # noqa: F401
+from . import direct, fp8, tree, vectorised, window  # noqa: F401
