@@ -333,6 +333,30 @@ def run_fp8(torch, reps=30):
                        "cache": "e4m3, one scale per kv head"}}
 
 
+def run_tree(torch, reps=30):
+    """Tree-based speculative verify: B=16 rows of 4,092 committed tokens, 8 draft
+    nodes per row in a tree (two branches off node 0 and a second root)."""
+    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    import workloads as W
+    sh = W.LLAMA8B_VERIFY
+    B, hq, hkv, d, T = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim, 8
+    caches = [KVCache(B, hkv, sh.max_len, d, device_lens=False) for _ in range(2)]
+    n = [T] * B
+    for i, c in enumerate(caches):
+        _fill_gpu_random(torch, c, [4092 + T] * B, 40 + i)
+    g = torch.Generator(device="cuda").manual_seed(13)
+    q = torch.randn(B, hq, T, d, device="cuda", generator=g).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    parents = [[-1, 0, 1, 2, 0, 4, -1, 6]] * B
+    ws = torch.zeros(max(max(c.workspace_bytes(hq, T, n) for c in caches), 256), dtype=torch.uint8, device="cuda")
+    t = _time_calls(torch, lambda i: gqa_attention(q, caches[i & 1], n, out=out, workspace=ws, parents=parents),
+                    reps)
+    nbytes = attention_bytes([4092 + T] * B, n, hq, hkv, d, T)
+    return {"metric": "tree verify attention HBM GB/s", "value": round(nbytes / t / 1e9, 2), "unit": "GB/s",
+            "frac_of_8TBs": round(nbytes / t / 8e12, 4), "ms": round(t * 1e3, 5), "bytes": nbytes,
+            "config": {"workload": "llama8b_tree_verify_b16_n8_s4100", "batch": B, "nodes": T, "keys": 4092 + T}}
+
+
 def run_ragged(torch, seed=4, reps=20):
     """Ragged batch: 64 rows, log-uniform lengths in [1, 32000], n_new in {0, 1, 4, 256}, T=256."""
     from gqa_attention_preallocated_amd import KVCache, gqa_attention
@@ -460,7 +484,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "window", "fp8", "cpu"],
+    ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "window", "fp8", "tree",
+                                       "cpu"],
                     default=None,
                     help="time one workload only (for profiling); prints its own JSON line")
     ap.add_argument("--copy-probe", action="store_true",
@@ -494,9 +519,9 @@ def main():
     if args.only == "ragged":
         print(json.dumps({"ragged": [run_ragged(torch, seed) for seed in (4, 5, 6)]}), flush=True)
         return
-    if args.only in ("prefill", "verify", "append", "window", "fp8"):
+    if args.only in ("prefill", "verify", "append", "window", "fp8", "tree"):
         fn = {"prefill": run_prefill, "verify": run_verify, "append": run_append, "window": run_window,
-              "fp8": run_fp8}[args.only]
+              "fp8": run_fp8, "tree": run_tree}[args.only]
         print(json.dumps({args.only: fn(torch)}), flush=True)
         return
     res = run_decode(torch, args.steps, args.warmup)

@@ -185,12 +185,15 @@ class KVCache:
         return self._ws
 
 
-def gqa_attention(q, cache: KVCache, n_new, out=None, workspace=None):
+def gqa_attention(q, cache: KVCache, n_new, out=None, workspace=None, parents=None):
     """Attention output [B, Hq, T, d] for the n_new[b] tokens each row just appended.
 
     q: [B, Hq, T, d] (Hq a multiple of the cache's Hkv); padded slots
     t >= n_new[b] come back as zeros. ``workspace`` (a uint8 CUDA tensor) may be
-    given to avoid the cache's own grow-once scratch buffer.
+    given to avoid the cache's own grow-once scratch buffer. With ``parents``
+    ([B, T] ints: -1 or an earlier node) the new tokens are a draft tree and
+    each attends the committed keys plus its ancestors ([MASK] "What
+    interviewers probe next").
     """
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a 4-d tensor [B, Hq, T, d]")
@@ -216,7 +219,15 @@ def gqa_attention(q, cache: KVCache, n_new, out=None, workspace=None):
         ws = workspace
     ws_ptr = ctypes.c_void_p(ws.data_ptr() if ws is not None else 0)
     ws_len = ws.numel() if ws is not None else 0
-    st = lib.gqa_attention(cache.handle, ctypes.c_void_p(q.data_ptr()), hq, T, arr,
-                           ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_len, _stream_ptr())
+    if parents is None:
+        st = lib.gqa_attention(cache.handle, ctypes.c_void_p(q.data_ptr()), hq, T, arr,
+                               ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_len, _stream_ptr())
+    else:
+        flat = [int(x) for row in (parents.tolist() if hasattr(parents, "tolist") else parents) for x in row]
+        if len(flat) != B * T:
+            raise ValueError(f"parents must be [B={B}, T={T}]")
+        st = lib.gqa_attention_tree(cache.handle, ctypes.c_void_p(q.data_ptr()), hq, T, arr,
+                                    _lib.int32_array(flat), ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_len,
+                                    _stream_ptr())
     _lib.check(st, lib)
     return out

@@ -26,6 +26,7 @@ EXPORTED = (
     "kv_cache_create", "kv_cache_destroy", "kv_append", "gqa_attention_workspace_size",
     "gqa_attention", "kv_truncate", "kv_get_lens", "kv_cache_bytes", "kv_live_bytes",
     "kv_last_error", "kv_cache_set_policy", "kv_cache_create_ring", "kv_cache_create_fp8",
+    "gqa_attention_tree",
 )
 
 _lib = None
@@ -60,6 +61,8 @@ def load():
     lib.gqa_attention_workspace_size.restype = ctypes.c_int
     lib.gqa_attention.argtypes = [P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
     lib.gqa_attention.restype = ctypes.c_int
+    lib.gqa_attention_tree.argtypes = [P, P, I32, I32, I32P, I32P, P, P, ctypes.c_size_t, P]
+    lib.gqa_attention_tree.restype = ctypes.c_int
     lib.kv_truncate.argtypes = [P, I32P, P]
     lib.kv_truncate.restype = ctypes.c_int
     lib.kv_get_lens.argtypes = [P, I32P]

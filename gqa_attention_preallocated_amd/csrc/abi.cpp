@@ -278,6 +278,9 @@ kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t
                        void *k_buf, void *v_buf, int32_t *lens_dev, void *stream, bool ring, int32_t window,
                        const float *k_scale, const float *v_scale, kv_cache **out);
 
+kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
+                         const int32_t *parents, void *out, void *workspace, size_t workspace_bytes, void *stream);
+
 // Ring caches: the lowest position a row of this length still holds, and the
 // lowest key a query at position pos sees ([MASK] "A strong answer", reversal).
 int64_t oldest_kept(const kv_cache *c, int64_t len) { return c->ring ? std::max<int64_t>(0, len - c->max_len) : 0; }
@@ -485,6 +488,36 @@ kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32
 
 kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
                         void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    return attention_call(c, q, q_heads, T, n_new, nullptr, out, workspace, workspace_bytes, stream);
+}
+
+kv_status gqa_attention_tree(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
+                             const int32_t *parents, void *out, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    kv_status s = check_attention_args(c, q_heads, T, n_new);
+    if (s != KV_OK) return s;
+    if (T > kMaxTreeNodes || (int64_t)(q_heads / c->kv_heads) * T > 64)
+        return fail(KV_ERR_UNSUPPORTED, "tree verify takes at most %d nodes and G * T <= 64", kMaxTreeNodes);
+    if (c->ring) return fail(KV_ERR_UNSUPPORTED, "tree verify runs on linear caches");
+    if (c->path_policy == 2) return fail(KV_ERR_UNSUPPORTED, "tree verify runs on the split-K decode kernel");
+    if (c->batch > 0 && T > 0 && parents == nullptr) return fail(KV_ERR_INVALID_ARG, "parents is null");
+    // [MASK] "What interviewers probe next": parent pointers; here every parent
+    // is -1 (the committed prefix) or an earlier node of the same row
+    for (int b = 0; b < c->batch; ++b)
+        for (int u = 0; u < n_new[b]; ++u) {
+            const int p = parents[(int64_t)b * T + u];
+            if (p < -1 || p >= u)
+                return fail(KV_ERR_INVALID_ARG, "row %d node %d: parent %d is not -1 or an earlier node", b, u, p);
+        }
+    return attention_call(c, q, q_heads, T, n_new, parents, out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
+                         const int32_t *parents, void *out, void *workspace, size_t workspace_bytes,
+                         void *stream) {
     kv_status s = check_attention_args(c, q_heads, T, n_new);
     if (s != KV_OK) return s;
     if (c->batch == 0 || T == 0) return ok();
@@ -558,8 +591,15 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
     a.records = p.records;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c->head_dim));
 
+    a.tree = parents != nullptr;
     for (size_t lo = 0; lo < p.dec.size(); lo += kMaxRows) {
         fill_attn_rows(p.dec, lo, std::min(p.dec.size(), lo + kMaxRows), c->kv_heads, a.rows);
+        if (a.tree) {
+            std::memset(a.parent, -1, sizeof a.parent);
+            for (int j = 0; j < a.rows.n_rows; ++j)
+                for (int u = 0; u < a.rows.nnew[j]; ++u)
+                    a.parent[j][u] = (int8_t)parents[(int64_t)a.rows.b[j] * T + u];
+        }
         hipError_t e = launch_decode((int)c->dtype, c->head_dim, p.nsub, a, dec_stream);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (decode kernel)");
     }
@@ -612,6 +652,9 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, 
     }
     return ok();
 }
+}  // namespace
+
+extern "C" {
 
 kv_status kv_truncate(kv_cache *c, const int32_t *new_lens, void *stream) {
     if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");

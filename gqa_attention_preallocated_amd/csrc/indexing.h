@@ -30,6 +30,7 @@ GQAKV_HD inline int find_row(const int32_t *item0, int n_rows, int item) {
 
 // One work item of an attention launch (see AttnRows for the numbering).
 struct Item {
+    int r;                // row of the launch table
     int b, kvh, qtile, split, nq, nsplit;
     int base;             // absolute position of the row's query 0 = len - n_new
     int t0, t_end;        // queries [t0, t_end) of this tile
@@ -47,6 +48,7 @@ GQAKV_HD inline int range_start(int first_pos, int window) {
 GQAKV_HD inline Item decode_item(const AttnRows &R, int item, int hkv, int group, int cols, int window) {
     Item it;
     const int r = find_row(R.item0, R.n_rows, item);
+    it.r = r;
     const int n = R.nnew[r];
     const int tq = cols / group;                  // queries per tile
     it.nq = (n + tq - 1) / tq;

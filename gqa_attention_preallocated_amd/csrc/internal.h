@@ -25,6 +25,8 @@ struct AppendTable {
 
 // E4M3 caches carry one scale per KV head for K and one for V.
 constexpr int kMaxScaleHeads = 64;
+// Tree verify: at most this many draft nodes per row.
+constexpr int kMaxTreeNodes = 16;
 
 struct AppendArgs {
     void *k;                   // cache K [B, Hkv, max_len, d]
@@ -74,6 +76,8 @@ struct AttnArgs {
     int64_t records;           // partial records available in the workspace
     float scale_log2;          // log2(e) / sqrt(d)
     float k_scale[kMaxScaleHeads], v_scale[kMaxScaleHeads];   // E4M3 caches: code x scale per KV head
+    int32_t tree;              // 1: the new tokens of each row form a tree (parent below)
+    int8_t parent[kMaxRows][kMaxTreeNodes];   // per launch row: parent node of node u, -1 = the committed prefix
     AttnRows rows;
 };
 

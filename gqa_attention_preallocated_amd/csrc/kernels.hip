@@ -513,6 +513,23 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         }
     };
 
+    // tree verify ([MASK] "What interviewers probe next"): the new tokens of
+    // the row are tree nodes; a column's query (node t) sees the committed keys
+    // and the nodes on its path to the root. anc = that path as a bit set.
+    uint32_t anc[NSUB];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+        anc[s] = 0;
+        if (a.tree && pos[s] >= 0) {
+            const int8_t *par = a.parent[it.r];
+            int u = column_t(it, s * 16 + lr, a.group);
+            for (int k = 0; k < kMaxTreeNodes && u >= 0; ++k) {   // parents point to earlier nodes
+                anc[s] |= 1u << u;
+                u = par[u];
+            }
+        }
+    }
+
     // smallest position among this item's real columns: tiles ending at or
     // before it need no mask ([MASK] "A strong answer", tile cases); with a
     // window, tiles starting at or below the largest position minus the
@@ -553,7 +570,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 
         // ---- mask (only tiles that straddle the diagonal or the range end),
         //      online softmax in log2 units
-        const bool need_mask = (tile + KT > w_end) || (tile + KT - 1 > pos_min) || (tile <= pos_max - a.window);
+        const bool need_mask = (tile + KT > w_end) || (tile + KT - 1 > pos_min) || (tile <= pos_max - a.window) ||
+                               (a.tree && tile + KT > it.base);
         f32x8 p[NSUB];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
@@ -561,13 +579,17 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[j] = sc[s][j >> 2][j & 3];
             if (need_mask) {                      // uniform over the wave
-                // key j is visible iff lo_key <= j <= pos and j < the range end
+                // key j is visible iff lo_key <= j <= pos and j < the range end,
+                // and (tree) j is committed or on the column's path to the root
                 const int lim = imin(pos[s] + 1, w_end) - (tile + lg * 4);
                 const int lim_lo = lo_key[s] - (tile + lg * 4);
+                const int node0 = tile + lg * 4 - it.base;        // node index of offset 0
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int off = (j >> 2) * 16 + (j & 3);
-                    v[j] = (off < lim && off >= lim_lo) ? v[j] : -INFINITY;
+                    const int u = node0 + off;
+                    const bool on_path = u < 0 || (u < 32 && ((anc[s] >> (u & 31)) & 1u));
+                    v[j] = (off < lim && off >= lim_lo && (!a.tree || on_path)) ? v[j] : -INFINITY;
                 }
             }
             softmax_step<NB>(v, score_c, st[s], acc[s], p[s]);

@@ -195,6 +195,28 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
                         size_t workspace_bytes, void *stream);
 
 /*
+ * Tree-based speculative verify: as gqa_attention, but the n_new[b] tokens just
+ * appended to row b are the nodes of a draft tree rather than a chain. [MASK]
+ * "What interviewers probe next": each draft token attends the full cache plus
+ * its own ancestors, so the T x T corner of the mask becomes an ancestor mask
+ * built from parent pointers.
+ *   parents       HOST int32[B * T]; parents[b * T + u] for u < n_new[b] is -1
+ *                 (node u follows the committed prefix) or the index of an
+ *                 earlier node (0 <= parent < u). Entries for u >= n_new[b]
+ *                 are ignored.
+ * Node u of row b is the key at absolute position lens[b] - n_new[b] + u, and
+ * query t sees key j iff j < lens[b] - n_new[b] (committed) or j is node t or
+ * one of its ancestors. Needs T <= 16, G * T <= 64 and a linear cache (not a
+ * ring); runs on the split-K decode kernel (KV_ERR_UNSUPPORTED when the
+ * policy forces the prefill kernel). The workspace is that of gqa_attention
+ * for the same arguments. A chain (parent u - 1 for every u) gives the bits
+ * gqa_attention gives. KV_ERR_INVALID_ARG for a parent outside -1 .. u - 1.
+ */
+kv_status gqa_attention_tree(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
+                             const int32_t *n_new, const int32_t *parents, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Roll back: set lens[b] = new_lens[b] for every row, copying and clearing
  * nothing. [CH16] "Layout and validity" (truncate for speculative rollback;
  * stale slots stay and are never read). new_lens is a HOST int32[B] with

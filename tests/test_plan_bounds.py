@@ -40,6 +40,7 @@ def sim(tmp_path_factory):
     lib.kv_append.argtypes = [P, P, P, I32, I32P, P]
     lib.gqa_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]
     lib.gqa_attention.argtypes = [P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
+    lib.gqa_attention_tree.argtypes = [P, P, I32, I32, I32P, I32P, P, P, ctypes.c_size_t, P]
     lib.kv_truncate.argtypes = [P, I32P, P]
     lib.kv_cache_set_policy.argtypes = [P, I32, I32]
     lib.kv_cache_destroy.argtypes = [P]
@@ -306,3 +307,35 @@ def test_llama_fp8_decode(sim):
     c.append(1, [1] * sh.batch)
     assert c.attention(1, [1] * sh.batch) == 0
     c.check(1)
+
+
+def test_tree_verify_launches_and_rules(sim):
+    """Tree verify plans decode launches only, inside every buffer, one write
+    per output row; bad parents, too many nodes, rings and a forced prefill
+    kernel are refused."""
+    sh = W.LLAMA8B_VERIFY
+    c = SimCache(sim, sh.batch, sh.kv_heads, sh.max_len, sh.head_dim, "bf16", sh.q_heads, 4096)
+    for call in _prefix_calls([4092] * sh.batch):
+        c.append(call["T"], call["n_new"])
+    T = 8
+    n = [8] * (sh.batch - 2) + [5, 0]
+    c.append(T, n)
+    parents = [-1, 0, 1, 2, 0, 4, -1, 6] * sh.batch
+    size = ctypes.c_size_t()
+    assert sim.gqa_attention_workspace_size(c.h, sh.q_heads, T, _i32(n), ctypes.byref(size)) == 0
+    sim.hostcheck_begin_call()
+    st = sim.gqa_attention_tree(c.h, ctypes.c_void_p(c.addr["q"]), sh.q_heads, T, _i32(n), _i32(parents),
+                                ctypes.c_void_p(c.addr["out"]), ctypes.c_void_p(c.addr["ws"]), size.value, None)
+    assert st == 0, sim.kv_last_error()
+    c.check(T)
+
+    def call(par, T_=T, n_=n):
+        return sim.gqa_attention_tree(c.h, ctypes.c_void_p(c.addr["q"]), sh.q_heads, T_, _i32(n_), _i32(par),
+                                      ctypes.c_void_p(c.addr["out"]), ctypes.c_void_p(c.addr["ws"]), 1 << 30,
+                                      None)
+    bad = list(parents)
+    bad[3] = 3                                  # a node cannot be its own parent
+    assert call(bad) == 1 and b"parent" in sim.kv_last_error()
+    assert call([-1] * (sh.batch * 17), 17, [0] * sh.batch) == 3       # more than 16 nodes
+    sim.kv_cache_set_policy(c.h, 2, 0)
+    assert call(parents) == 3
