@@ -21,9 +21,11 @@ check it against the pages by eye:
                       the dequantized values.
   * ``tree``       -- tree-based speculative verify: each draft node attends
                       the committed keys and its ancestors (parent pointers).
+  * ``paged``      -- a pool of fixed-size pages shared by all rows and a block
+                      table per row; attention over the keys gathered through it.
 
 Where the pages are silent or disagree, the reading taken is stated in the
 docstring of the function that depends on it.
 """
 
-from . import direct, fp8, tree, vectorised, window  # noqa: F401
+from . import direct, fp8, paged, tree, vectorised, window  # noqa: F401
