@@ -64,10 +64,15 @@ class KVCache:
     With ``fp8_scales=(k_scale, v_scale)`` (one float per KV head each) K and
     V are stored as E4M3 codes (``k``/``v`` are uint8 tensors) and read back
     dequantized ([CH16] exercise 4); inputs and outputs stay bfloat16.
+
+    With ``page_size=P, num_pages=N`` the cache is paged: ``k``/``v`` are one
+    pool [N, Hkv, P, d] shared by all rows, ``block_table_dev`` the device
+    block table [B, max_len // P] the library keeps, and a row takes pages only
+    as it grows ([GQA] reversal: a block table and a paged kernel).
     """
 
     def __init__(self, batch, kv_heads, max_len, head_dim, dtype=torch.bfloat16, device="cuda",
-                 device_lens=True, window=None, fp8_scales=None):
+                 device_lens=True, window=None, fp8_scales=None, page_size=None, num_pages=None):
         if dtype not in _DTYPES:
             raise ValueError(f"dtype {dtype} not supported (float32 or bfloat16)")
         self._lib = _lib.load()
@@ -77,9 +82,21 @@ class KVCache:
         shape = (batch, kv_heads, max_len, head_dim)
         if fp8_scales is not None and (dtype != torch.bfloat16 or window is not None):
             raise ValueError("an E4M3 cache takes bfloat16 inputs and has no window")
-        store = torch.uint8 if fp8_scales is not None else dtype
-        self.k = torch.zeros(shape, dtype=store, device=device)
-        self.v = torch.zeros(shape, dtype=store, device=device)
+        self.paged = page_size is not None
+        if self.paged:
+            if num_pages is None or window is not None or fp8_scales is not None:
+                raise ValueError("a paged cache needs num_pages and has no window or E4M3 storage")
+            if max_len % page_size != 0:
+                raise ValueError("max_len must be a multiple of page_size")
+            pool = (int(num_pages), kv_heads, int(page_size), head_dim)
+            self.page_size, self.num_pages, self.max_blocks = int(page_size), int(num_pages), max_len // page_size
+            self.k = torch.zeros(pool, dtype=dtype, device=device)
+            self.v = torch.zeros(pool, dtype=dtype, device=device)
+            self.block_table_dev = torch.empty((max(batch, 1), self.max_blocks), dtype=torch.int32, device=device)
+        else:
+            store = torch.uint8 if fp8_scales is not None else dtype
+            self.k = torch.zeros(shape, dtype=store, device=device)
+            self.v = torch.zeros(shape, dtype=store, device=device)
         self.lens_dev = torch.zeros(max(batch, 1), dtype=torch.int32, device=device) if device_lens else None
         self.dtype = dtype
         self.batch, self.kv_heads, self.max_len, self.head_dim = shape
@@ -98,6 +115,11 @@ class KVCache:
                                                    (ctypes.c_float * max(kv_heads, 1))(*ks),
                                                    (ctypes.c_float * max(kv_heads, 1))(*vs), *bufs,
                                                    _stream_ptr(), ctypes.byref(h))
+            elif self.paged:
+                st = self._lib.kv_cache_create_paged(batch, kv_heads, self.num_pages, self.page_size,
+                                                     self.max_blocks, head_dim, _DTYPES[dtype], *bufs[:2],
+                                                     ctypes.c_void_p(self.block_table_dev.data_ptr()), bufs[2],
+                                                     _stream_ptr(), ctypes.byref(h))
             elif window is None:
                 st = self._lib.kv_cache_create(batch, kv_heads, max_len, head_dim, _DTYPES[dtype], *bufs,
                                                _stream_ptr(), ctypes.byref(h))
@@ -126,6 +148,18 @@ class KVCache:
         arr = (ctypes.c_int32 * max(1, self.batch))()
         _lib.check(self._lib.kv_get_lens(self._h, arr), self._lib)
         return list(arr)[: self.batch]
+
+    @property
+    def block_table(self):
+        """Host copy of a paged cache's block table [B][max_blocks] (-1: no page)."""
+        arr = (ctypes.c_int32 * max(1, self.batch * self.max_blocks))()
+        _lib.check(self._lib.kv_get_block_table(self._h, arr), self._lib)
+        flat = list(arr)
+        return [flat[b * self.max_blocks:(b + 1) * self.max_blocks] for b in range(self.batch)]
+
+    @property
+    def free_pages(self):
+        return int(self._lib.kv_free_pages(self._h))
 
     @property
     def bytes(self):

@@ -26,7 +26,7 @@ EXPORTED = (
     "kv_cache_create", "kv_cache_destroy", "kv_append", "gqa_attention_workspace_size",
     "gqa_attention", "kv_truncate", "kv_get_lens", "kv_cache_bytes", "kv_live_bytes",
     "kv_last_error", "kv_cache_set_policy", "kv_cache_create_ring", "kv_cache_create_fp8",
-    "gqa_attention_tree",
+    "gqa_attention_tree", "kv_cache_create_paged", "kv_get_block_table", "kv_free_pages",
 )
 
 _lib = None
@@ -53,6 +53,13 @@ def load():
     FP = ctypes.POINTER(ctypes.c_float)
     lib.kv_cache_create_fp8.argtypes = [I32, I32, I32, I32, FP, FP, P, P, P, P, ctypes.POINTER(P)]
     lib.kv_cache_create_fp8.restype = ctypes.c_int
+    lib.kv_cache_create_paged.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.c_int, P, P, P, P, P,
+                                          ctypes.POINTER(P)]
+    lib.kv_cache_create_paged.restype = ctypes.c_int
+    lib.kv_get_block_table.argtypes = [P, I32P]
+    lib.kv_get_block_table.restype = ctypes.c_int
+    lib.kv_free_pages.argtypes = [P]
+    lib.kv_free_pages.restype = I32
     lib.kv_cache_destroy.argtypes = [P]
     lib.kv_cache_destroy.restype = None
     lib.kv_append.argtypes = [P, P, P, I32, I32P, P]

@@ -16,8 +16,10 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <new>
 #include <numeric>
+#include <queue>
 #include <string>
 #include <vector>
 
@@ -40,6 +42,13 @@ struct kv_cache {
     int32_t keys_per_split = 0;  // 0 auto
     bool ring = false;           // token p in slot p mod max_len; lens are absolute positions
     int32_t window = kNoWindow;  // a query at p sees keys p - window < j <= p
+    // paged: k and v are a pool [num_pages, Hkv, page_size, d]; logical block
+    // i of row b is page table[b * max_blocks + i]; max_len = max_blocks * page_size
+    bool paged = false;
+    int32_t num_pages = 0, page_size = 0, page_shift = 0, max_blocks = 0;
+    int32_t *table_dev = nullptr;                 // caller's device copy, kept in stream order
+    std::vector<int32_t> table;                   // host copy, authoritative (-1: no page)
+    std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_pages;
     SideStream side;             // created on the first mixed decode + prefill call
 };
 
@@ -274,9 +283,36 @@ void fill_attn_rows(const std::vector<RowPlan> &rows, size_t lo, size_t hi, int 
     t.total_items = item;
 }
 
+struct PagedSpec {
+    int32_t num_pages, page_size, max_blocks;
+    int32_t *table_dev;
+};
+
 kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim, kv_dtype dtype,
                        void *k_buf, void *v_buf, int32_t *lens_dev, void *stream, bool ring, int32_t window,
-                       const float *k_scale, const float *v_scale, kv_cache **out);
+                       const float *k_scale, const float *v_scale, const PagedSpec *pg, kv_cache **out);
+
+// Paged caches: blocks a row of `len` tokens occupies.
+int64_t blocks_of(const kv_cache *c, int64_t len) { return ceil_div(len, c->page_size); }
+
+// Enqueue device block-table updates (index, page) in chunks that fit the
+// kernel arguments.
+kv_status push_table_updates(kv_cache *c, const std::vector<std::pair<int32_t, int32_t>> &upd, hipStream_t st,
+                             const char *what) {
+    for (size_t lo = 0; lo < upd.size(); lo += kMaxTableUpdates) {
+        TableArgs t{};
+        t.table = c->table_dev;
+        const size_t hi = std::min(upd.size(), lo + kMaxTableUpdates);
+        t.n = (int32_t)(hi - lo);
+        for (size_t i = lo; i < hi; ++i) {
+            t.idx[i - lo] = upd[i].first;
+            t.page[i - lo] = upd[i].second;
+        }
+        hipError_t e = launch_table_set(t, st);
+        if (e != hipSuccess) return device_fail(e, what);
+    }
+    return KV_OK;
+}
 
 kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
                          const int32_t *parents, void *out, void *workspace, size_t workspace_bytes, void *stream);
@@ -297,7 +333,7 @@ kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int3
     if (dtype == KV_DTYPE_FP8_E4M3)
         return fail(KV_ERR_UNSUPPORTED, "an E4M3 cache needs its scales: use kv_cache_create_fp8");
     return create_cache(batch, kv_heads, max_len, head_dim, dtype, k_buf, v_buf, lens_dev, stream, false,
-                        kNoWindow, nullptr, nullptr, out);
+                        kNoWindow, nullptr, nullptr, nullptr, out);
 }
 
 kv_status kv_cache_create_fp8(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim,
@@ -313,7 +349,7 @@ kv_status kv_cache_create_fp8(int32_t batch, int32_t kv_heads, int32_t max_len, 
         if (!(std::isfinite(k_scale[h]) && k_scale[h] > 0.f && std::isfinite(v_scale[h]) && v_scale[h] > 0.f))
             return fail(KV_ERR_INVALID_ARG, "kv head %d: scales must be finite and positive", h);
     return create_cache(batch, kv_heads, max_len, head_dim, KV_DTYPE_FP8_E4M3, k_buf, v_buf, lens_dev, stream,
-                        false, kNoWindow, k_scale, v_scale, out);
+                        false, kNoWindow, k_scale, v_scale, nullptr, out);
 }
 
 kv_status kv_cache_create_ring(int32_t batch, int32_t kv_heads, int32_t capacity, int32_t head_dim,
@@ -327,7 +363,30 @@ kv_status kv_cache_create_ring(int32_t batch, int32_t kv_heads, int32_t capacity
         return fail(KV_ERR_INVALID_ARG, "window %d outside 1..capacity %d", window, capacity);
     if (dtype == KV_DTYPE_FP8_E4M3) return fail(KV_ERR_UNSUPPORTED, "ring caches hold float32 or bfloat16");
     return create_cache(batch, kv_heads, capacity, head_dim, dtype, k_buf, v_buf, lens_dev, stream, true, window,
-                        nullptr, nullptr, out);
+                        nullptr, nullptr, nullptr, out);
+}
+
+kv_status kv_cache_create_paged(int32_t batch, int32_t kv_heads, int32_t num_pages, int32_t page_size,
+                                int32_t max_blocks, int32_t head_dim, kv_dtype dtype, void *k_pool, void *v_pool,
+                                int32_t *block_table, int32_t *lens_dev, void *stream, kv_cache **out) {
+    if (out == nullptr) return fail(KV_ERR_INVALID_ARG, "out is null");
+    *out = nullptr;
+    if (page_size < kMinPage || page_size > kMaxPage || (page_size & (page_size - 1)) != 0)
+        return fail(KV_ERR_INVALID_ARG, "page_size %d is not a power of two in %d..%d", page_size, kMinPage,
+                    kMaxPage);
+    if (num_pages <= 0 || max_blocks <= 0)
+        return fail(KV_ERR_INVALID_ARG, "bad pool num_pages=%d max_blocks=%d", num_pages, max_blocks);
+    if ((int64_t)max_blocks * page_size > INT32_MAX - kRingAlign)
+        return fail(KV_ERR_INVALID_ARG, "max_blocks * page_size out of range");
+    if ((int64_t)batch * max_blocks > INT32_MAX) return fail(KV_ERR_INVALID_ARG, "block table too large");
+    if ((int64_t)num_pages * kv_heads * page_size * head_dim >= (int64_t(1) << 40))
+        return fail(KV_ERR_INVALID_ARG, "page pool too large");
+    if (dtype == KV_DTYPE_FP8_E4M3) return fail(KV_ERR_UNSUPPORTED, "paged caches hold float32 or bfloat16");
+    if (batch > 0 && block_table == nullptr) return fail(KV_ERR_INVALID_ARG, "block_table is null");
+    if (!aligned16(block_table)) return fail(KV_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+    const PagedSpec pg{num_pages, page_size, max_blocks, block_table};
+    return create_cache(batch, kv_heads, max_blocks * page_size, head_dim, dtype, k_pool, v_pool, lens_dev, stream,
+                        false, kNoWindow, nullptr, nullptr, &pg, out);
 }
 
 }  // extern "C"
@@ -335,7 +394,7 @@ kv_status kv_cache_create_ring(int32_t batch, int32_t kv_heads, int32_t capacity
 namespace {
 kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t head_dim, kv_dtype dtype,
                        void *k_buf, void *v_buf, int32_t *lens_dev, void *stream, bool ring, int32_t window,
-                       const float *k_scale, const float *v_scale, kv_cache **out) {
+                       const float *k_scale, const float *v_scale, const PagedSpec *pg, kv_cache **out) {
     if (out == nullptr) return fail(KV_ERR_INVALID_ARG, "out is null");
     *out = nullptr;
     if (dtype != KV_DTYPE_F32 && dtype != KV_DTYPE_BF16 && dtype != KV_DTYPE_FP8_E4M3)
@@ -348,7 +407,7 @@ kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t
         return fail(KV_ERR_INVALID_ARG, "k_buf/v_buf is null");
     if (!aligned16(k_buf) || !aligned16(v_buf) || !aligned16(lens_dev))
         return fail(KV_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
-    if ((int64_t)batch * kv_heads * max_len * head_dim >= (int64_t(1) << 40))
+    if (pg == nullptr && (int64_t)batch * kv_heads * max_len * head_dim >= (int64_t(1) << 40))
         return fail(KV_ERR_INVALID_ARG, "cache too large");
     kv_cache *c = new (std::nothrow) kv_cache;
     if (c == nullptr) return fail(KV_ERR_DEVICE, "out of host memory");
@@ -373,6 +432,21 @@ kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t
     c->lens.assign(batch, 0);
     c->ring = ring;
     c->window = window;
+    if (pg != nullptr) {
+        c->paged = true;
+        c->num_pages = pg->num_pages;
+        c->page_size = pg->page_size;
+        while ((1 << c->page_shift) < pg->page_size) ++c->page_shift;
+        c->max_blocks = pg->max_blocks;
+        c->table_dev = pg->table_dev;
+        c->table.assign((size_t)batch * pg->max_blocks, -1);
+        for (int32_t i = 0; i < pg->num_pages; ++i) c->free_pages.push(i);
+        hipError_t e = launch_table_fill(c->table_dev, (int64_t)batch * pg->max_blocks, -1, (hipStream_t)stream);
+        if (e != hipSuccess) {
+            delete c;
+            return device_fail(e, "kv_cache_create_paged");
+        }
+    }
     if (lens_dev != nullptr) {
         for (int lo = 0; lo < batch; lo += kMaxRows) {
             LensTable t{};
@@ -423,10 +497,35 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
             return fail(KV_ERR_CAPACITY, "row %d: position %lld out of range", b, (long long)(s + n));
         total += n;
     }
+    // a paged cache takes the pages the new tokens need from the pool; the
+    // call is refused whole if the pool cannot give them all
+    int64_t pages_needed = 0;
+    if (c->paged) {
+        for (int b = 0; b < c->batch; ++b)
+            pages_needed += blocks_of(c, (int64_t)c->lens[b] + n_new[b]) - blocks_of(c, c->lens[b]);
+        if (pages_needed > (int64_t)c->free_pages.size())
+            return fail(KV_ERR_CAPACITY, "%lld pages needed, %zu free in the pool", (long long)pages_needed,
+                        c->free_pages.size());
+    }
     if (total > 0) {
         if (k_new == nullptr || v_new == nullptr) return fail(KV_ERR_INVALID_ARG, "k_new/v_new is null");
         if (!aligned16(k_new) || !aligned16(v_new))
             return fail(KV_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+    }
+    if (pages_needed > 0) {
+        // row by row, each new block gets the lowest-numbered free page; the
+        // device table learns the entries before the copy kernel reads them
+        std::vector<std::pair<int32_t, int32_t>> upd;
+        for (int b = 0; b < c->batch; ++b)
+            for (int64_t i = blocks_of(c, c->lens[b]); i < blocks_of(c, (int64_t)c->lens[b] + n_new[b]); ++i) {
+                const int32_t page = c->free_pages.top();
+                c->free_pages.pop();
+                const int32_t idx = (int32_t)((int64_t)b * c->max_blocks + i);
+                c->table[idx] = page;
+                upd.push_back({idx, page});
+            }
+        kv_status st = push_table_updates(c, upd, (hipStream_t)stream, "kv_append (block table)");
+        if (st != KV_OK) return st;
     }
     std::vector<int> rows;
     for (int b = 0; b < c->batch; ++b)
@@ -451,6 +550,9 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
         a.hkv = c->kv_heads;
         a.max_len = c->max_len;
         a.T = T;
+        a.table = c->paged ? c->table_dev : nullptr;
+        a.page_shift = c->page_shift;
+        a.max_blocks = c->max_blocks;
         const size_t hi = std::min(rows.size(), lo + kMaxRows);
         a.t.n_rows = (int32_t)(hi - lo);
         int32_t blocks = 0;
@@ -584,6 +686,9 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
     a.max_len = c->max_len;
     a.head_dim = c->head_dim;
     a.window = c->window;
+    a.table = c->paged ? c->table_dev : nullptr;
+    a.page_shift = c->page_shift;
+    a.max_blocks = c->max_blocks;
     for (size_t h = 0; h < c->k_scale.size(); ++h) {
         a.k_scale[h] = c->k_scale[h];
         a.v_scale[h] = c->v_scale[h];
@@ -681,9 +786,32 @@ kv_status kv_truncate(kv_cache *c, const int32_t *new_lens, void *stream) {
             if (e != hipSuccess) return device_fail(e, "kv_truncate");
         }
     }
+    if (c->paged) {
+        // blocks that no longer hold a token give their pages back to the pool
+        std::vector<std::pair<int32_t, int32_t>> upd;
+        for (int b = 0; b < c->batch; ++b)
+            for (int64_t i = blocks_of(c, new_lens[b]); i < blocks_of(c, c->lens[b]); ++i)
+                upd.push_back({(int32_t)((int64_t)b * c->max_blocks + i), -1});
+        kv_status st = push_table_updates(c, upd, (hipStream_t)stream, "kv_truncate (block table)");
+        if (st != KV_OK) return st;
+        for (auto &u : upd) {
+            c->free_pages.push(c->table[u.first]);
+            c->table[u.first] = -1;
+        }
+    }
     for (int b = 0; b < c->batch; ++b) c->lens[b] = new_lens[b];
     return ok();
 }
+
+kv_status kv_get_block_table(const kv_cache *c, int32_t *table_host) {
+    if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
+    if (!c->paged) return fail(KV_ERR_INVALID_ARG, "not a paged cache");
+    if (!c->table.empty() && table_host == nullptr) return fail(KV_ERR_INVALID_ARG, "table_host is null");
+    std::copy(c->table.begin(), c->table.end(), table_host);
+    return ok();
+}
+
+int32_t kv_free_pages(const kv_cache *c) { return (c != nullptr && c->paged) ? (int32_t)c->free_pages.size() : 0; }
 
 kv_status kv_get_lens(const kv_cache *c, int32_t *lens_host) {
     if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
@@ -694,6 +822,7 @@ kv_status kv_get_lens(const kv_cache *c, int32_t *lens_host) {
 
 uint64_t kv_cache_bytes(const kv_cache *c) {
     if (c == nullptr) return 0;
+    if (c->paged) return 2ull * (uint64_t)c->num_pages * c->kv_heads * c->page_size * c->head_dim * c->elem_bytes;
     return 2ull * (uint64_t)c->batch * c->kv_heads * c->max_len * c->head_dim * c->elem_bytes;
 }
 

@@ -29,7 +29,7 @@ constexpr int kMaxScaleHeads = 64;
 constexpr int kMaxTreeNodes = 16;
 
 struct AppendArgs {
-    void *k;                   // cache K [B, Hkv, max_len, d]
+    void *k;                   // cache K [B, Hkv, max_len, d], or the page pool [pages, Hkv, page, d]
     void *v;
     const void *k_new;         // [B, Hkv, T, d]
     const void *v_new;
@@ -39,7 +39,20 @@ struct AppendArgs {
     int32_t batch, hkv, max_len, T;
     int32_t quant;             // 1: bfloat16 inputs stored as E4M3 codes of x * inv scale
     float k_inv[kMaxScaleHeads], v_inv[kMaxScaleHeads];   // float32 1 / scale per KV head
+    const int32_t *table;      // paged cache: block table [B, max_blocks] (null: linear or ring)
+    int32_t page_shift;        // log2(page size)
+    int32_t max_blocks;
     AppendTable t;
+};
+
+// Paged caches: entries of the device block table set in stream order, carried
+// in the kernel arguments (no host-to-device copy).
+constexpr int kMaxTableUpdates = 480;
+struct TableArgs {
+    int32_t *table;
+    int32_t n;
+    int32_t idx[kMaxTableUpdates];    // b * max_blocks + block
+    int32_t page[kMaxTableUpdates];   // page, or -1
 };
 
 struct LensTable {
@@ -67,7 +80,7 @@ struct AttnRows {
 struct AttnArgs {
     const void *q;             // [B, Hq, T, d]
     void *out;                 // [B, Hq, T, d]
-    const void *k;             // cache [B, Hkv, max_len, d]
+    const void *k;             // cache [B, Hkv, max_len, d], or the page pool [pages, Hkv, page, d]
     const void *v;
     float *ws_acc;             // partial records: unnormalised acc [rec][d]
     float *ws_ml;              // partial records: (running max in log2 units, sum) [rec][2]
@@ -76,6 +89,9 @@ struct AttnArgs {
     int64_t records;           // partial records available in the workspace
     float scale_log2;          // log2(e) / sqrt(d)
     float k_scale[kMaxScaleHeads], v_scale[kMaxScaleHeads];   // E4M3 caches: code x scale per KV head
+    const int32_t *table;      // paged cache: block table [B, max_blocks] (null: linear or ring)
+    int32_t page_shift;        // log2(page size)
+    int32_t max_blocks;
     int32_t tree;              // 1: the new tokens of each row form a tree (parent below)
     int8_t parent[kMaxRows][kMaxTreeNodes];   // per launch row: parent node of node u, -1 = the committed prefix
     AttnRows rows;
@@ -120,7 +136,10 @@ struct ZeroArgs {
 // element type codes match kv_dtype
 hipError_t launch_append(const AppendArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t s);
-// nsub: 16-column subtiles per decode work item (1, 2 or 4)
+hipError_t launch_table_set(const TableArgs &a, hipStream_t s);
+hipError_t launch_table_fill(int32_t *table, int64_t n, int32_t value, hipStream_t s);
+// nsub: 16-column subtiles per decode work item (1, 2 or 4); a.table selects
+// the paged kernels (float32 and bfloat16 caches)
 hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t s);
 hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t s);
 hipError_t launch_combine(int dtype, int head_dim, const CombineArgs &a, hipStream_t s);
@@ -150,5 +169,10 @@ constexpr int32_t kNoWindow = 0x7fffffff;
 constexpr int32_t kRingAlign = 64;
 constexpr int kZeroSlice = 16384;   // bytes of output one zero-fill block clears
 constexpr int kAppendChunk = 4096;
+// Pages of a paged cache hold a power of two of tokens in this range: a key
+// tile of either kernel (32 or 64 keys from a multiple of its size) never
+// crosses a page.
+constexpr int32_t kMinPage = 64;
+constexpr int32_t kMaxPage = 65536;
 
 }  // namespace gqakv

@@ -34,7 +34,7 @@ namespace gqakv {
 
 // every launch passes its tables by value: keep them inside the kernel-argument space
 static_assert(sizeof(AttnArgs) <= 4096 && sizeof(AppendArgs) <= 4096 && sizeof(CombineArgs) <= 4096 &&
-              sizeof(ZeroArgs) <= 4096, "kernel arguments too large");
+              sizeof(ZeroArgs) <= 4096 && sizeof(TableArgs) <= 4096, "kernel arguments too large");
 
 typedef __bf16 bf16_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -276,20 +276,31 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         // token i of the row goes to slot slot0 + i, wrapping at max_len (a
         // ring; a linear cache never reaches the wrap)
         const int tok = (int)(off >> a.row_shift);
-        int slot = a.t.slot0[r] + tok;
-        if (slot >= a.max_len) slot -= a.max_len;
+        int64_t crow;                             // cache row of the token
+        if (a.table == nullptr) {
+            int slot = a.t.slot0[r] + tok;
+            if (slot >= a.max_len) slot -= a.max_len;
+            crow = head * a.max_len + slot;
+        } else {
+            // paged: position p sits in row p mod page of (page, kv head) in the
+            // pool, page = block_table[b][p / page] ([GQA] reversal); the table
+            // entries were set earlier on the stream
+            const int p = a.t.start[r] + tok;
+            const int page = a.table[(int64_t)b * a.max_blocks + (p >> a.page_shift)];
+            crow = (((int64_t)page * a.hkv + kvh) << a.page_shift) + (p & ((1 << a.page_shift) - 1));
+        }
         const int64_t src = head * a.T * a.row_bytes + off;
         const uint4 kx = *reinterpret_cast<const uint4 *>((const char *)a.k_new + src);
         const uint4 vx = *reinterpret_cast<const uint4 *>((const char *)a.v_new + src);
         if (!a.quant) {
-            const int64_t dst = ((head * a.max_len + slot) << a.row_shift) + (off & (a.row_bytes - 1));
+            const int64_t dst = (crow << a.row_shift) + (off & (a.row_bytes - 1));
             *reinterpret_cast<uint4 *>((char *)a.k + dst) = kx;
             *reinterpret_cast<uint4 *>((char *)a.v + dst) = vx;
         } else {
             // E4M3 cache ([CH16] exercise 4): 8 bfloat16 in, 8 codes out, each
             // the code of x * (1 / scale) in float32, saturated to +-448,
             // rounded to the nearest code (ties to even)
-            const int64_t dst = ((head * a.max_len + slot) << (a.row_shift - 1)) + ((off & (a.row_bytes - 1)) >> 1);
+            const int64_t dst = (crow << (a.row_shift - 1)) + ((off & (a.row_bytes - 1)) >> 1);
             *reinterpret_cast<uint2 *>((char *)a.k + dst) = quant8(kx, a.k_inv[kvh]);
             *reinterpret_cast<uint2 *>((char *)a.v + dst) = quant8(vx, a.v_inv[kvh]);
         }
@@ -301,6 +312,17 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 __global__ __launch_bounds__(64) void set_lens_kernel(int32_t *lens_dev, LensTable t) {
     const int i = threadIdx.x;
     if (i < t.n_rows) lens_dev[t.b[i]] = t.len[i];
+}
+
+// paged caches: block-table entries set by the host's page assignment
+__global__ __launch_bounds__(256) void table_set_kernel(TableArgs a) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < a.n) a.table[a.idx[i]] = a.page[i];
+}
+
+__global__ __launch_bounds__(256) void table_fill_kernel(int32_t *table, int64_t n, int32_t value) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) table[i] = value;
 }
 
 // ---------------------------------------------------------------------------
@@ -319,6 +341,47 @@ __device__ inline E *column_out(const AttnArgs &a, const Item &it, int col, int 
     const int t = column_t(it, col, a.group), h = column_head(it, col, a.group);
     return reinterpret_cast<E *>(a.out) + (((int64_t)it.b * a.hq + h) * a.T + t) * D;
 }
+
+// Where the keys of a work item live. Key position j of (row b, kv head h): a
+// linear or ring cache holds it in slot j mod max_len of the head's
+// [max_len, d] block; a paged cache in row j mod page of block (page, h) of
+// the pool, page = block_table[b][j / page] ([GQA] reversal: a block table
+// and a paged kernel). row(tile) is the cache row of a tile's first key; no
+// tile crosses a page or the end of a ring. A paged lookup keeps 64
+// consecutive table entries of the row, one per lane, and reads the one it
+// needs across lanes; tiles are asked for in increasing order, so the entries
+// are reloaded once per 64 blocks.
+template <bool PG> struct KeyRows;
+
+template <> struct KeyRows<false> {
+    int64_t head_row;
+    int max_len;
+    __device__ KeyRows(const AttnArgs &a, const Item &it, int)
+        : head_row(((int64_t)it.b * a.hkv + it.kvh) * a.max_len), max_len(a.max_len) {}
+    __device__ int64_t row(int tile) const { return head_row + tile % max_len; }
+};
+
+template <> struct KeyRows<true> {
+    const int32_t *tbl;
+    int nblk, shift, kvh, hkv;
+    int blk0, ent;
+    __device__ KeyRows(const AttnArgs &a, const Item &it, int first_key)
+        : tbl(a.table + (int64_t)it.b * a.max_blocks), nblk(a.max_blocks), shift(a.page_shift), kvh(it.kvh),
+          hkv(a.hkv) {
+        refill(__builtin_amdgcn_readfirstlane(first_key >> shift));
+    }
+    __device__ void refill(int blk) {
+        blk0 = blk;
+        const int i = blk + (int)(threadIdx.x & 63);
+        ent = i < nblk ? tbl[i] : 0;
+    }
+    __device__ int64_t row(int tile) {
+        const int blk = __builtin_amdgcn_readfirstlane(tile >> shift);
+        if (blk - blk0 >= 64) refill(blk);
+        const int page = __builtin_amdgcn_readlane(ent, blk - blk0);
+        return (((int64_t)page * hkv + kvh) << shift) + (tile & ((1 << shift) - 1));
+    }
+};
 
 // One online-softmax step for the 8 scores a lane holds for its column
 // (two 16-key blocks: s0 = keys 4g..4g+3, s1 = keys 16+4g..16+4g+3 of a
@@ -397,7 +460,7 @@ __device__ inline void softmax_tile(const float (&v)[N], float c, ColState &st, 
 // merge their partial results through LDS (reusing the V staging space), so a
 // split-free row needs no second pass.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int NSUB, int W, bool F8>
+template <typename E, int D, int NSUB, int W, bool F8, bool PG>
 __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     using O = Op<E>;
     using S = Stor<E, F8>;
@@ -453,9 +516,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         }
     }
 
-    const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
-    const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k) + head * a.max_len * CROWB;
-    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v) + head * a.max_len * CROWB;
+    const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k);
+    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v);
+    KeyRows<PG> km(a, it, w_begin);
     // an E4M3 cache stands for code x scale of the head: the K scale joins the
     // score scale, the V scale multiplies the output
     const float score_c = F8 ? a.scale_log2 * a.k_scale[it.kvh] : a.scale_log2;
@@ -479,10 +542,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     constexpr int PF = (F8 && NSUB <= 2) ? 2 : 1;
     kraw kA[2][KC], kB[2][KC];
     uint4 vA[VCH], vB[VCH];
-    // key position j lives in slot j mod max_len; a tile never wraps (ring
-    // capacities are multiples of kRingAlign, tiles start at multiples of KT)
+    // a tile's keys are consecutive cache rows from km.row(tile): no tile
+    // wraps (ring capacities are multiples of kRingAlign, pages of kMinPage,
+    // and tiles start at multiples of KT)
     auto load_tile = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
-        const int slot = tile % a.max_len;
+        const int64_t row0 = km.row(tile);
+        const unsigned char *kt = kbase + row0 * CROWB;
+        const unsigned char *vt = vbase + row0 * CROWB;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int key = ks * 16 + lr;
@@ -490,7 +556,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
             if constexpr (KPAIR) {
 #pragma unroll
                 for (int j = 0; j < KC / 2; ++j) {
-                    const uint4 w = ok ? load_stream(kbase + (int64_t)(slot + key) * CROWB + dmap(2 * j))
+                    const uint4 w = ok ? load_stream(kt + key * CROWB + dmap(2 * j))
                                        : make_uint4(0, 0, 0, 0);
                     kop[ks][2 * j] = make_uint2(w.x, w.y);
                     kop[ks][2 * j + 1] = make_uint2(w.z, w.w);
@@ -499,7 +565,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
                     const int d0 = dmap(kc);
-                    kop[ks][kc] = (ok && d0 < D) ? S::load_k(kbase + (int64_t)(slot + key) * CROWB + d0 * S::kBytes)
+                    kop[ks][kc] = (ok && d0 < D) ? S::load_k(kt + key * CROWB + d0 * S::kBytes)
                                                  : S::zero_k();
                 }
             }
@@ -509,7 +575,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
             const int c = lane + 64 * i;
             const int key = c / CPK, part = c % CPK;
             const bool ok = (c < KT * CPK) && (tile + key < w_end);
-            vreg[i] = ok ? load_stream(vbase + (int64_t)(slot + key) * CROWB + part * 16) : make_uint4(0, 0, 0, 0);
+            vreg[i] = ok ? load_stream(vt + key * CROWB + part * 16) : make_uint4(0, 0, 0, 0);
         }
     };
 
@@ -672,7 +738,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 // or below the first query's position are not masked; only tiles straddling
 // the diagonal compare indices ([MASK] "A strong answer", tiled-kernel rule).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool F8>
+template <typename E, int D, bool F8, bool PG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(AttnArgs a) {
     using O = Op<E>;
     using S = Stor<E, F8>;
@@ -724,9 +790,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
     }
 
-    const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
-    const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k) + head * a.max_len * CROWB;
-    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v) + head * a.max_len * CROWB;
+    const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k);
+    const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v);
+    KeyRows<PG> km(a, it, it.k_begin);
     // an E4M3 cache: the K scale joins the score scale, the V scale the output
     const float score_c = F8 ? a.scale_log2 * a.k_scale[it.kvh] : a.scale_log2;
     const float out_c = F8 ? a.v_scale[it.kvh] : 1.f;
@@ -748,10 +814,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // thread chunk c = tid + 256 i is key c / CPK, bytes (c % CPK) * 16.. of the
     // tile: byte offset c * 16 from the tile's first key. Keys at or past
     // k_end (and chunks past the tile) fall outside the view and read as zero.
-    // key position j lives in slot j mod max_len; no tile wraps (see decode)
-    auto load = [&](uint4 (&reg)[PCH], const unsigned char *base, int tile) {
-        const __amdgpu_buffer_rsrc_t r =
-            buffer_view(base + (int64_t)(tile % a.max_len) * CROWB, imin(it.k_end - tile, KT) * CROWB);
+    // a tile's keys are consecutive cache rows from km.row(tile), which the
+    // K load of a tile looks up and the V load of the same tile reuses (no
+    // tile wraps or crosses a page: see decode)
+    auto load = [&](uint4 (&reg)[PCH], const unsigned char *base, int64_t row0, int tile) {
+        const __amdgpu_buffer_rsrc_t r = buffer_view(base + row0 * CROWB, imin(it.k_end - tile, KT) * CROWB);
 #pragma unroll
         for (int i = 0; i < PCH; ++i) reg[i] = buffer_load_stream(r, (tid + 256 * i) * 16);
     };
@@ -933,12 +1000,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
     };
 
+    int64_t row_cur = 0, row_next = 0;                 // cache rows of tiles i and i + 1
     if (ntiles > 0) {
-        load(kreg, kbase, it.k_begin);
+        row_cur = km.row(it.k_begin);
+        load(kreg, kbase, row_cur, it.k_begin);
         store(kreg, lds_k[0]);
         __syncthreads();
-        if (ntiles > 1) load(kreg, kbase, it.k_begin + KT);
-        load(vreg, vbase, it.k_begin);
+        if (ntiles > 1) {
+            row_next = km.row(it.k_begin + KT);
+            load(kreg, kbase, row_next, it.k_begin + KT);
+        }
+        load(vreg, vbase, row_cur, it.k_begin);
         if (wave_last >= 0) scores(lds_k[0], sc);
     }
     for (int i = 0; i < ntiles; ++i) {
@@ -949,8 +1021,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         if (has_next) store(kreg, lds_k[(i + 1) & 1]);
         if (i > 0) store(vreg, lds_v[(i + 1) & 1]);
         __syncthreads();
-        if (i + 2 < ntiles) load(kreg, kbase, tile + 2 * KT);
-        if (i > 0) load(vreg, vbase, tile);              // V(0) came with the prologue
+        int64_t row_k2 = 0;
+        if (i + 2 < ntiles) {
+            row_k2 = km.row(tile + 2 * KT);
+            load(kreg, kbase, row_k2, tile + 2 * KT);
+        }
+        if (i > 0) load(vreg, vbase, row_cur, tile);     // V(0) came with the prologue
+        row_cur = row_next;
+        row_next = row_k2;
         if (i > wave_last) {
             if (i == wave_last + 1 && wave_last >= 0) pv(vp, pb);   // the last tile this wave computed
             continue;
@@ -1107,49 +1185,65 @@ hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t s)
     return hipGetLastError();
 }
 
+hipError_t launch_table_set(const TableArgs &a, hipStream_t s) {
+    if (a.n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(table_set_kernel, dim3((a.n + 255) / 256), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_table_fill(int32_t *table, int64_t n, int32_t value, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(table_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, table, n, value);
+    return hipGetLastError();
+}
+
 // dtype codes (kv_dtype): 0 float32, 1 bfloat16, 2 E4M3 cache with bfloat16 q/out
-template <typename E, int D, bool F8>
+template <typename E, int D, bool F8, bool PG>
 static hipError_t decode_d(int nsub, const AttnArgs &a, hipStream_t s) {
     constexpr int W = kDecodeWaves;
     const dim3 grid(a.rows.total_items), block(64 * W);
     switch (nsub) {
-        case 1: hipLaunchKernelGGL((decode_kernel<E, D, 1, W, F8>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<E, D, 2, W, F8>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<E, D, 4, W, F8>), grid, block, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<E, D, 1, W, F8, PG>), grid, block, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<E, D, 2, W, F8, PG>), grid, block, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<E, D, 4, W, F8, PG>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <typename E, bool F8>
+template <typename E, bool F8, bool PG>
 static hipError_t decode_e(int head_dim, int nsub, const AttnArgs &a, hipStream_t s) {
     switch (head_dim) {
-        case 16: return decode_d<E, 16, F8>(nsub, a, s);
-        case 32: return decode_d<E, 32, F8>(nsub, a, s);
-        case 64: return decode_d<E, 64, F8>(nsub, a, s);
-        case 128: return decode_d<E, 128, F8>(nsub, a, s);
+        case 16: return decode_d<E, 16, F8, PG>(nsub, a, s);
+        case 32: return decode_d<E, 32, F8, PG>(nsub, a, s);
+        case 64: return decode_d<E, 64, F8, PG>(nsub, a, s);
+        case 128: return decode_d<E, 128, F8, PG>(nsub, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
+// paged caches hold float32 or bfloat16 (dtype 0 or 1)
 hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t s) {
     if (a.rows.total_items <= 0) return hipSuccess;
+    const bool pg = a.table != nullptr;
     switch (dtype) {
-        case 0: return decode_e<float, false>(head_dim, nsub, a, s);
-        case 1: return decode_e<bf16_t, false>(head_dim, nsub, a, s);
-        case 2: return decode_e<bf16_t, true>(head_dim, nsub, a, s);
+        case 0: return pg ? decode_e<float, false, true>(head_dim, nsub, a, s)
+                          : decode_e<float, false, false>(head_dim, nsub, a, s);
+        case 1: return pg ? decode_e<bf16_t, false, true>(head_dim, nsub, a, s)
+                          : decode_e<bf16_t, false, false>(head_dim, nsub, a, s);
+        case 2: return pg ? hipErrorInvalidValue : decode_e<bf16_t, true, false>(head_dim, nsub, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename E, bool F8>
+template <typename E, bool F8, bool PG>
 static hipError_t prefill_e(int head_dim, const AttnArgs &a, hipStream_t s) {
     const dim3 grid(a.rows.total_items), block(256);
     switch (head_dim) {
-        case 16: hipLaunchKernelGGL((prefill_kernel<E, 16, F8>), grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((prefill_kernel<E, 32, F8>), grid, block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((prefill_kernel<E, 64, F8>), grid, block, 0, s, a); break;
-        case 128: hipLaunchKernelGGL((prefill_kernel<E, 128, F8>), grid, block, 0, s, a); break;
+        case 16: hipLaunchKernelGGL((prefill_kernel<E, 16, F8, PG>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((prefill_kernel<E, 32, F8, PG>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((prefill_kernel<E, 64, F8, PG>), grid, block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((prefill_kernel<E, 128, F8, PG>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1157,10 +1251,12 @@ static hipError_t prefill_e(int head_dim, const AttnArgs &a, hipStream_t s) {
 
 hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t s) {
     if (a.rows.total_items <= 0) return hipSuccess;
+    const bool pg = a.table != nullptr;
     switch (dtype) {
-        case 0: return prefill_e<float, false>(head_dim, a, s);
-        case 1: return prefill_e<bf16_t, false>(head_dim, a, s);
-        case 2: return prefill_e<bf16_t, true>(head_dim, a, s);
+        case 0: return pg ? prefill_e<float, false, true>(head_dim, a, s) : prefill_e<float, false, false>(head_dim, a, s);
+        case 1: return pg ? prefill_e<bf16_t, false, true>(head_dim, a, s)
+                          : prefill_e<bf16_t, false, false>(head_dim, a, s);
+        case 2: return pg ? hipErrorInvalidValue : prefill_e<bf16_t, true, false>(head_dim, a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -11,8 +11,9 @@
  *
  * Ownership. The caller owns every device buffer (K, V, the optional device
  * copy of the lengths, q, out, k_new, v_new, the workspace) and every stream.
- * The library owns only the opaque handle and its host copy of the per-row
- * lengths; it never allocates device memory.
+ * The library owns only the opaque handle and its host copies of the per-row
+ * lengths (and of a paged cache's block table); it never allocates device
+ * memory.
  *
  * Layout. All device arrays are dense and row-major:
  *   K, V            [B, Hkv, max_len, d]   ([GQA] "A strong answer")
@@ -132,6 +133,51 @@ kv_status kv_cache_create_fp8(int32_t batch, int32_t kv_heads, int32_t max_len, 
                               const float *k_scale, const float *v_scale, void *k_buf, void *v_buf,
                               int32_t *lens_dev, void *stream, kv_cache **out);
 
+/*
+ * Paged cache: one pool of fixed-size pages shared by every row, and a block
+ * table per row that maps the row's logical blocks to pages, so memory is held
+ * in proportion to the tokens stored instead of max_len per row. [GQA] "A
+ * strong answer" (preallocating max_len per row is the waste a paged cache
+ * removes) and the reversal (rows of wildly different lengths call for a block
+ * table and a paged kernel); [CH16] "16. Prefill, decode and the KV cache",
+ * design choices (a paged cache keeps the in-place O(1) write without
+ * reserving the maximum up front).
+ *   num_pages     pages in the pool; k_pool and v_pool are device arrays of
+ *                 num_pages * Hkv * page_size * d elements each, laid out
+ *                 [num_pages, Hkv, page_size, d].
+ *   page_size     tokens per page: a power of two, 64 <= page_size <= 65536.
+ *   max_blocks    table entries per row: a row holds at most
+ *                 max_blocks * page_size tokens (its max_len).
+ *   block_table   device int32[B * max_blocks], caller-allocated, written only
+ *                 by the library, in stream order: entry b * max_blocks + i is
+ *                 the page holding tokens i * page_size .. (i + 1) *
+ *                 page_size - 1 of row b, or -1. Set to -1 here on `stream`.
+ * kv_append gives each row the pages its new tokens need, row by row, each
+ * time the lowest-numbered free page; if the pool cannot give them all it
+ * returns KV_ERR_CAPACITY ("{n} pages needed, {m} free in the pool") and
+ * changes nothing. kv_truncate returns to the pool the pages of blocks that
+ * no longer hold a token. gqa_attention and gqa_attention_tree compute what
+ * they compute on a linear cache with max_len = max_blocks * page_size, the
+ * keys gathered through the table. float32 and bfloat16 only
+ * (KV_ERR_UNSUPPORTED for E4M3); KV_ERR_INVALID_ARG for a page_size, num_pages
+ * or max_blocks outside the ranges above; other arguments and errors as
+ * kv_cache_create.
+ */
+kv_status kv_cache_create_paged(int32_t batch, int32_t kv_heads, int32_t num_pages, int32_t page_size,
+                                int32_t max_blocks, int32_t head_dim, kv_dtype dtype, void *k_pool,
+                                void *v_pool, int32_t *block_table, int32_t *lens_dev, void *stream,
+                                kv_cache **out);
+
+/*
+ * Copy a paged cache's host block table (B * max_blocks entries, as of the
+ * last enqueued call; -1 = no page) into table_host. KV_ERR_INVALID_ARG for a
+ * cache that is not paged.
+ */
+kv_status kv_get_block_table(const kv_cache *c, int32_t *table_host);
+
+/* Pages of a paged cache's pool that hold no token (0 for other caches). */
+int32_t kv_free_pages(const kv_cache *c);
+
 /* Release the handle (never the caller's buffers). NULL is ignored. */
 void kv_cache_destroy(kv_cache *c);
 
@@ -231,7 +277,8 @@ kv_status kv_get_lens(const kv_cache *c, int32_t *lens_host);
 
 /*
  * Bytes of the reservation, 2 * B * Hkv * max_len * d * element size
- * ([CH16] "Layout and validity", the bytes property).
+ * ([CH16] "Layout and validity", the bytes property); for a paged cache the
+ * pool, 2 * num_pages * Hkv * page_size * d * element size.
  */
 uint64_t kv_cache_bytes(const kv_cache *c);
 

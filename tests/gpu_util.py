@@ -61,3 +61,32 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
 def same_bytes(a: np.ndarray, b: np.ndarray) -> bool:
     return a.shape == b.shape and np.array_equal(np.ascontiguousarray(a).view(np.uint8),
                                                  np.ascontiguousarray(b).view(np.uint8))
+
+
+def fill_rows(cache, shape, seed, lens, chunk=2048):
+    """Append each row's seeded history (prefix_kv) until row b holds lens[b]
+    tokens (into each cache of a list, when given one)."""
+    caches = cache if isinstance(cache, (list, tuple)) else [cache]
+    lens = np.asarray(lens)
+    B, hk, d = shape.batch, shape.kv_heads, shape.head_dim
+    start = 0
+    while start < lens.max():
+        n = np.clip(lens - start, 0, chunk)
+        T = int(n.max())
+        k = np.zeros((B, hk, T, d), W.storage_np_dtype(shape.dtype))
+        v = np.zeros_like(k)
+        for b in range(B):
+            if n[b] > 0:
+                k[b, :, :n[b]], v[b, :, :n[b]] = W.prefix_kv(shape, seed, b, start, int(n[b]))
+        kd, vd = to_dev(k, shape.dtype), to_dev(v, shape.dtype)
+        for c in caches:
+            c.append(kd, vd, n.tolist())
+        start += chunk
+
+
+def row_history(shape, seed, b, length, extra_k=None, extra_v=None):
+    k, v = W.prefix_kv(shape, seed, b, 0, length)
+    if extra_k is not None:
+        k = np.concatenate([k, extra_k], axis=1)
+        v = np.concatenate([v, extra_v], axis=1)
+    return k, v

@@ -36,6 +36,7 @@ std::map<uintptr_t, int> g_out_rows;   // start address of an output row -> writ
 std::map<int64_t, int> g_records;      // partial record -> writes
 std::map<uintptr_t, int> g_appended;   // 16-byte chunk of K -> writes
 std::vector<int32_t> g_lens_dev;
+std::vector<int32_t> g_table;          // the device block table of a paged cache, as the kernels see it
 int64_t g_launches = 0;
 
 void err(const std::string &m) {
@@ -68,6 +69,7 @@ void hostcheck_reset() {
     g_records.clear();
     g_appended.clear();
     g_lens_dev.clear();
+    g_table.clear();
     g_launches = 0;
 }
 
@@ -107,6 +109,9 @@ int64_t hostcheck_appended_dupes() {
 
 int32_t hostcheck_lens_dev(int b) { return (b >= 0 && b < (int)g_lens_dev.size()) ? g_lens_dev[b] : -1; }
 
+// entry i of the simulated device block table (-2 when never written)
+int32_t hostcheck_table(int64_t i) { return (i >= 0 && i < (int64_t)g_table.size()) ? g_table[i] : -2; }
+
 }  // extern "C"
 
 namespace gqakv {
@@ -128,14 +133,26 @@ hipError_t launch_append(const AppendArgs &a, int n_blocks, hipStream_t) {
             if (off >= span) continue;
             if ((int64_t(1) << a.row_shift) != a.row_bytes) err("append: row_shift does not match row_bytes");
             if (a.t.slot0[r] != a.t.start[r] % a.max_len) err("append: slot0 is not start mod max_len");
-            // the kernel's mapping: token i -> slot slot0 + i, wrapped once at max_len
+            // the kernel's mapping: token i -> slot slot0 + i, wrapped once at
+            // max_len; in a paged cache position p -> row p mod page of
+            // (block_table[b][p / page], kv head) in the pool
             const int tok = (int)(off >> a.row_shift);
             int slot = a.t.slot0[r] + tok;
             if (slot >= a.max_len) slot -= a.max_len;
+            int64_t crow = head * a.max_len + slot;
+            if (a.table != nullptr) {
+                const int p = a.t.start[r] + tok;
+                const int64_t ti = (int64_t)b * a.max_blocks + (p >> a.page_shift);
+                access(a.table + ti, 4, "table", "append block table");
+                const int page = ti < (int64_t)g_table.size() ? g_table[ti] : -1;
+                if (page < 0) err("append: block without a page");
+                crow = (((int64_t)page * a.hkv + kvh) << a.page_shift) + (p & ((1 << a.page_shift) - 1));
+                slot = p % a.max_len;                // the logical slot, for the check below
+            }
             const int64_t src = head * a.T * a.row_bytes + off;
             // a quantizing append writes one code byte per two input bytes
             const int sh = a.quant ? a.row_shift - 1 : a.row_shift;
-            const int64_t dst = ((head * a.max_len + slot) << sh) + ((off & (a.row_bytes - 1)) >> (a.quant ? 1 : 0));
+            const int64_t dst = (crow << sh) + ((off & (a.row_bytes - 1)) >> (a.quant ? 1 : 0));
             const int wbytes = a.quant ? 8 : 16;
             access((const char *)a.k_new + src, 16, "k_new", "append read k_new");
             access((const char *)a.v_new + src, 16, "v_new", "append read v_new");
@@ -151,6 +168,24 @@ hipError_t launch_append(const AppendArgs &a, int n_blocks, hipStream_t) {
             access(a.lens_dev + b, 4, "lens", "append lens_dev");
             g_lens_dev[b] = a.t.start[r] + a.t.n[r];
         }
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_table_fill(int32_t *table, int64_t n, int32_t value, hipStream_t) {
+    ++g_launches;
+    access(table, (size_t)n * 4, "table", "table fill");
+    g_table.assign((size_t)n, value);
+    return hipSuccess;
+}
+
+hipError_t launch_table_set(const TableArgs &a, hipStream_t) {
+    ++g_launches;
+    if (a.n <= 0 || a.n > kMaxTableUpdates) err("table set: bad update count");
+    for (int i = 0; i < a.n; ++i) {
+        access(a.table + a.idx[i], 4, "table", "table set");
+        if (a.idx[i] < 0 || a.idx[i] >= (int64_t)g_table.size()) err("table set: index outside the table");
+        else g_table[a.idx[i]] = a.page[i];
     }
     return hipSuccess;
 }
@@ -180,6 +215,20 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
             err("attention: bad row table entry");
         if (R.lsplit[r] % key_tile != 0 || R.nsplit[r] <= 0) err("attention: bad split");
     }
+    const bool paged = a.table != nullptr;
+    if (paged) {
+        // no page is held by two blocks, and every block below a row's length has one
+        std::map<int32_t, int> owners;
+        for (int32_t e : g_table)
+            if (e >= 0 && ++owners[e] > 1) err("attention: a page is held twice");
+        if (windowed || (1 << a.page_shift) < kMinPage || a.max_len != a.max_blocks << a.page_shift)
+            err("attention: bad paged geometry");
+        for (int r = 0; r < R.n_rows; ++r)
+            for (int i = 0; i < (R.len[r] + (1 << a.page_shift) - 1) >> a.page_shift; ++i) {
+                const int64_t ti = (int64_t)R.b[r] * a.max_blocks + i;
+                if (ti >= (int64_t)g_table.size() || g_table[ti] < 0) err("attention: block of a row without a page");
+            }
+    }
     for (int item = 0; item < R.total_items; ++item) {
         const Item it = decode_item(R, item, a.hkv, a.group, cols, a.window);
         const int r = find_row(R.item0, R.n_rows, item);
@@ -204,9 +253,19 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
             const int n = std::min(key_tile, it.k_end - t0);
             const int slot = t0 % a.max_len;
             if (slot + n > a.max_len) err("attention: key tile wraps");
-            for (int key : {slot, slot + n - 1}) {
-                access((const char *)a.k + (head * a.max_len + key) * cache_row, cache_row, "k", "attention K");
-                access((const char *)a.v + (head * a.max_len + key) * cache_row, cache_row, "v", "attention V");
+            int64_t row0 = head * a.max_len + slot;   // cache row of the tile's first key (the kernels' KeyRows)
+            if (paged) {
+                const int psz = 1 << a.page_shift;
+                const int64_t ti = (int64_t)it.b * a.max_blocks + (t0 >> a.page_shift);
+                access(a.table + ti, 4, "table", "attention block table");
+                const int page = ti < (int64_t)g_table.size() ? g_table[ti] : -1;
+                if (page < 0) err("attention: tile in a block without a page");
+                if ((t0 & (psz - 1)) + n > psz) err("attention: key tile crosses a page");
+                row0 = (((int64_t)page * a.hkv + it.kvh) << a.page_shift) + (t0 & (psz - 1));
+            }
+            for (int64_t key : {row0, row0 + n - 1}) {
+                access((const char *)a.k + key * cache_row, cache_row, "k", "attention K");
+                access((const char *)a.v + key * cache_row, cache_row, "v", "attention V");
             }
         }
         for (int col = 0; col < cols; ++col) {

@@ -12,7 +12,7 @@ import torch
 
 from oracle import direct
 import workloads as W
-from gpu_util import assert_close, from_dev, out_f64, to_dev
+from gpu_util import assert_close, fill_rows, from_dev, out_f64, row_history, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -21,31 +21,6 @@ def _lib():
     from gqa_attention_preallocated_amd import KVCache, gqa_attention
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     return KVCache, gqa_attention
-
-
-def fill_rows(cache, shape, seed, lens, chunk=2048):
-    """Append each row's seeded history (prefix_kv) until row b holds lens[b] tokens."""
-    lens = np.asarray(lens)
-    B, hk, d = shape.batch, shape.kv_heads, shape.head_dim
-    start = 0
-    while start < lens.max():
-        n = np.clip(lens - start, 0, chunk)
-        T = int(n.max())
-        k = np.zeros((B, hk, T, d), W.storage_np_dtype(shape.dtype))
-        v = np.zeros_like(k)
-        for b in range(B):
-            if n[b] > 0:
-                k[b, :, :n[b]], v[b, :, :n[b]] = W.prefix_kv(shape, seed, b, start, int(n[b]))
-        cache.append(to_dev(k, shape.dtype), to_dev(v, shape.dtype), n.tolist())
-        start += chunk
-
-
-def row_history(shape, seed, b, length, extra_k=None, extra_v=None):
-    k, v = W.prefix_kv(shape, seed, b, 0, length)
-    if extra_k is not None:
-        k = np.concatenate([k, extra_k], axis=1)
-        v = np.concatenate([v, extra_v], axis=1)
-    return k, v
 
 
 def test_zero_output_fails_the_gate():

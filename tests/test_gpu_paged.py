@@ -1,0 +1,169 @@
+"""GPU parity of the paged KV cache (kv_cache_create_paged).
+
+The HIP path (KVCache(page_size=..., num_pages=...) -> kv_cache_create_paged,
+kv_append, gqa_attention through the C ABI) against oracle/paged.py on the
+same seeded bits: the block table bit for bit (host copy, device copy and the
+oracle's page assignment), every page's bytes after every append, outputs
+within the contract tolerances, and, against the linear cache on the same
+inputs, the same output bits. [GQA] "Implement grouped-query attention over a
+preallocated KV cache, with no torch.cat, for both prefill chunks and decode",
+the reversal (a block table and a paged kernel for wildly ragged rows).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import direct, paged
+import workloads as W
+from gpu_util import TORCH_DTYPE, assert_close, fill_rows, from_dev, out_f64, row_history, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return KVCache, gqa_attention
+
+
+def _tables_agree(cache, ref):
+    host = np.array(cache.block_table, np.int64)
+    dev = cache.block_table_dev.cpu().numpy().astype(np.int64)[: cache.batch]
+    assert np.array_equal(host, dev), "device block table differs from the host copy"
+    assert np.array_equal(host, ref.table), "page assignment differs from the oracle"
+    assert cache.free_pages == len(ref.free)
+
+
+def _pages_agree(cache, ref, dt):
+    """Every page a row holds has the oracle's bytes (the valid rows of it)."""
+    k, v = from_dev(cache.k, dt), from_dev(cache.v, dt)
+    for b in range(cache.batch):
+        L = int(ref.lens[b])
+        for i in range(ref.blocks(L)):
+            page = int(ref.table[b, i])
+            n = min(ref.page_size, L - i * ref.page_size)
+            assert np.array_equal(k[page, :, :n], ref.k[page, :, :n]), f"row {b} block {i}: K bytes"
+            assert np.array_equal(v[page, :, :n], ref.v[page, :, :n]), f"row {b} block {i}: V bytes"
+
+
+CALLS = [(70, [70, 33, 0]), (1, [1, 1, 1]), (5, [5, 2, 5]), (130, [3, 130, 64]), (1, [1, 0, 1]),
+         "rollback", (64, [64, 64, 64]), (4, [4, 4, 1]), (200, [200, 7, 199])]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("d,P", [(16, 64), (64, 128), (128, 64), (128, 256)])
+def test_paged_schedule(dt, d, P):
+    """Prefill chunks, decode and verify steps, empty rows and a rollback on a
+    paged cache, under each kernel selection."""
+    KVCache, gqa_attention = _lib()
+    B, hk, G = 3, 2, 4
+    S = 768
+    pages = 2 * B * S // P // 3            # fewer pages than the dense reservation
+    shape = W.Shape("paged", dt, B, hk * G, hk, d, S)
+    for policy in [(0, 0), (1, 0), (2, 0), (1, 32), (2, 64)]:
+        cache = KVCache(B, hk, S, d, dtype=TORCH_DTYPE[dt], page_size=P, num_pages=pages)
+        cache.set_policy(*policy)
+        ref = paged.PagedCache(B, hk, pages, P, S // P, d, dt)
+        for i, call in enumerate(CALLS):
+            if call == "rollback":
+                new = [L - L // 3 for L in cache.lens]
+                cache.truncate(new)
+                ref.truncate(new)
+                _tables_agree(cache, ref)
+                continue
+            T, n = call
+            q, k, v = W.step_inputs(shape, 51, i, T, n, pad="nan")
+            cache.append(to_dev(k, dt), to_dev(v, dt), n)
+            ref.append(k, v, n)
+            _tables_agree(cache, ref)
+            _pages_agree(cache, ref, dt)
+            out = gqa_attention(to_dev(q, dt), cache, n)
+            assert_close(out_f64(out, dt), paged.attention(ref, q, n), dt, f"call {i} policy {policy}")
+            raw = from_dev(out, dt)
+            for b in range(B):
+                assert not raw[b, :, n[b]:].view(np.uint8).any(), "padded slot not +0.0"
+
+
+def test_paged_gives_the_bits_of_the_linear_cache():
+    """Same inputs into a linear and a paged cache (rows interleaved in the
+    pool): decode, verify, prefill and tree-verify outputs agree bit for bit."""
+    KVCache, gqa_attention = _lib()
+    B, hk, G, d, S = 4, 8, 4, 128, 4096
+    shape = W.Shape("paged_bits", "bf16", B, hk * G, hk, d, S)
+    lin = KVCache(B, hk, S, d)
+    pgd = KVCache(B, hk, S, d, page_size=64, num_pages=B * S // 64)
+    for i, (T, n) in enumerate([(64, [64, 64, 64, 64])] * 4 + [(1500, [1500, 900, 1200, 64])]):
+        _, k, v = W.step_inputs(shape, 8, i, T, n, pad="normal")
+        for c in (lin, pgd):
+            c.append(to_dev(k, "bf16"), to_dev(v, "bf16"), n)
+    assert pgd.block_table[0][:4] == [0, 4, 8, 12]          # rows alternate in the pool
+    for step, (T, n) in enumerate([(1, [1] * B), (4, [4, 4, 4, 4]), (512, [512, 17, 300, 1]), (3, [3, 0, 2, 3])]):
+        q, k, v = W.step_inputs(shape, 8, 100 + step, T, n, pad="normal")
+        outs = []
+        for c in (lin, pgd):
+            c.append(to_dev(k, "bf16"), to_dev(v, "bf16"), n)
+            outs.append(from_dev(gqa_attention(to_dev(q, "bf16"), c, n), "bf16"))
+        assert np.array_equal(outs[0], outs[1]), f"step {step}"
+    q, k, v = W.step_inputs(shape, 8, 200, 8, [8] * B, pad="normal")
+    par = [[-1, 0, 1, 2, 0, 4, -1, 6]] * B
+    outs = []
+    for c in (lin, pgd):
+        c.append(to_dev(k, "bf16"), to_dev(v, "bf16"), [8] * B)
+        outs.append(from_dev(gqa_attention(to_dev(q, "bf16"), c, [8] * B, parents=par), "bf16"))
+    assert np.array_equal(outs[0], outs[1]), "tree verify"
+
+
+def test_paged_pool_refusals():
+    KVCache, gqa_attention = _lib()
+    cache = KVCache(2, 1, 256, 16, dtype=torch.float32, page_size=64, num_pages=3)
+    k = torch.randn(2, 1, 128, 16, device="cuda")
+    cache.append(k, k, [64, 64])
+    before = (cache.block_table, cache.lens, cache.free_pages)
+    with pytest.raises(ValueError, match="pages needed"):
+        cache.append(k, k, [65, 1])
+    assert (cache.block_table, cache.lens, cache.free_pages) == before
+    with pytest.raises(ValueError):
+        KVCache(2, 1, 256, 16, dtype=torch.float32, page_size=48, num_pages=3)
+    with pytest.raises(ValueError):
+        KVCache(2, 1, 256, 16, page_size=64, num_pages=3, fp8_scales=([1.0], [1.0]))
+
+
+@pytest.mark.parametrize("seed", [4, 5])
+def test_llama_paged_ragged(seed):
+    """The 64 ragged Llama-shaped rows (1 .. 32,000 cached, 0 to 256 new) in a
+    pool of exactly the pages their lengths need (page 256): sampled outputs
+    against the oracle, padding +0.0, and far less memory than the dense cache."""
+    KVCache, gqa_attention = _lib()
+    sh = W.LLAMA8B_RAGGED
+    lens, n_new = W.ragged_rows(seed)
+    P = 256
+    pages = int(sum(-(-int(L + n) // P) for L, n in zip(lens, n_new)))
+    cache = KVCache(sh.batch, sh.kv_heads, sh.max_len, sh.head_dim, page_size=P, num_pages=pages)
+    fill_rows(cache, sh, seed, lens)
+    q, k, v = W.step_inputs(sh, seed, 10_000, 256, n_new, pad="nan")
+    cache.append(to_dev(k, "bf16"), to_dev(v, "bf16"), n_new.tolist())
+    assert cache.free_pages == 0
+    assert cache.bytes < 0.6 * 2 * sh.batch * sh.kv_heads * sh.max_len * sh.head_dim * 2
+    out = gqa_attention(to_dev(q, "bf16"), cache, n_new.tolist())
+    raw = from_dev(out, "bf16")
+    got = out_f64(out, "bf16")
+    assert np.isfinite(got).all()
+    for b in range(sh.batch):
+        assert not raw[b, :, n_new[b]:].view(np.uint8).any(), f"row {b}: padding not +0.0"
+    picks = []
+    for cls in (1, 4, 256):
+        idx = np.flatnonzero(n_new == cls)
+        if idx.size:
+            picks.append(int(idx[np.argmax(lens[idx])]))
+    picks.append(int(np.argmax(lens + (n_new > 0) * 10**6)))
+    rng = np.random.default_rng(7)
+    for b in sorted(set(picks)):
+        nb = int(n_new[b])
+        L = int(lens[b]) + nb
+        kr, vr = row_history(sh, seed, b, int(lens[b]), k[b, :, :nb], v[b, :, :nb])
+        ts = sorted({0, nb - 1, *rng.integers(0, nb, 3).tolist()})
+        pairs = [(h, t) for h in (0, 5, 31) for t in ts]
+        ref = direct.attention_row(kr, vr, L, nb, q[b], "bf16", pairs)
+        for h, t in pairs:
+            assert_close(got[b, h, t], ref[h, t], "bf16", f"paged ragged row {b} (len {L}) head {h} t {t}")

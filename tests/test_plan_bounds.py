@@ -37,6 +37,10 @@ def sim(tmp_path_factory):
     lib.kv_cache_create_ring.argtypes = [I32, I32, I32, I32, ctypes.c_int, I32, P, P, P, P, ctypes.POINTER(P)]
     FP = ctypes.POINTER(ctypes.c_float)
     lib.kv_cache_create_fp8.argtypes = [I32, I32, I32, I32, FP, FP, P, P, P, P, ctypes.POINTER(P)]
+    lib.kv_cache_create_paged.argtypes = [I32, I32, I32, I32, I32, I32, ctypes.c_int, P, P, P, P, P,
+                                          ctypes.POINTER(P)]
+    lib.kv_get_block_table.argtypes = [P, I32P]
+    lib.kv_free_pages.argtypes = [P]
     lib.kv_append.argtypes = [P, P, P, I32, I32P, P]
     lib.gqa_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]
     lib.gqa_attention.argtypes = [P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
@@ -52,6 +56,7 @@ def sim(tmp_path_factory):
     lib.hostcheck_appended_chunks.restype = ctypes.c_int64
     lib.hostcheck_appended_dupes.restype = ctypes.c_int64
     lib.hostcheck_launches.restype = ctypes.c_int64
+    lib.hostcheck_table.argtypes = [ctypes.c_int64]
     return lib
 
 
@@ -65,14 +70,19 @@ class SimCache:
 
     GAP = 1 << 44
 
-    def __init__(self, lib, B, hk, max_len, d, dtype, hq, t_max, window=None):
+    def __init__(self, lib, B, hk, max_len, d, dtype, hq, t_max, window=None, paged=None):
         self.lib, self.B, self.hk, self.max_len, self.d, self.hq = lib, B, hk, max_len, d, hq
         self.elem = 4 if dtype == "f32" else 2                  # q, out, k_new, v_new
         cache_elem = {"f32": 4, "bf16": 2, "fp8": 1}[dtype]       # K, V
         lib.hostcheck_reset()
         self.addr = {}
+        # paged = (page_size, num_pages): K and V are one pool, plus a block table
+        self.paged = paged
+        rows = B * max_len if paged is None else paged[1] * paged[0]
+        self.max_blocks = 0 if paged is None else max_len // paged[0]
         sizes = {
-            "k": B * hk * max_len * d * cache_elem, "v": B * hk * max_len * d * cache_elem,
+            "k": rows * hk * d * cache_elem, "v": rows * hk * d * cache_elem,
+            "table": 4 * max(B * self.max_blocks, 1),
             "lens": 4 * max(B, 1),
             "k_new": B * hk * t_max * d * self.elem, "v_new": B * hk * t_max * d * self.elem,
             "q": B * hq * t_max * d * self.elem, "out": B * hq * t_max * d * self.elem,
@@ -84,7 +94,11 @@ class SimCache:
             lib.hostcheck_region(base, max(size, 1), name.encode())
         h = ctypes.c_void_p()
         bufs = (ctypes.c_void_p(self.addr["k"]), ctypes.c_void_p(self.addr["v"]), ctypes.c_void_p(self.addr["lens"]))
-        if dtype == "fp8":
+        if paged is not None:
+            st = lib.kv_cache_create_paged(B, hk, paged[1], paged[0], self.max_blocks, d, 0 if dtype == "f32" else 1,
+                                           *bufs[:2], ctypes.c_void_p(self.addr["table"]), bufs[2], None,
+                                           ctypes.byref(h))
+        elif dtype == "fp8":
             sc = (ctypes.c_float * max(hk, 1))(*([0.05] * hk))
             st = lib.kv_cache_create_fp8(B, hk, max_len, d, sc, sc, *bufs, None, ctypes.byref(h))
         elif window is None:
@@ -119,6 +133,11 @@ class SimCache:
         assert st == 0, self.lib.kv_last_error()
         return size.value
 
+    def block_table(self):
+        arr = (ctypes.c_int32 * max(1, self.B * self.max_blocks))()
+        assert self.lib.kv_get_block_table(self.h, arr) == 0
+        return np.array(list(arr)[: self.B * self.max_blocks], np.int64).reshape(self.B, self.max_blocks)
+
     def check(self, T=None):
         lib = self.lib
         errs = [lib.hostcheck_error(i).decode() for i in range(lib.hostcheck_error_count())]
@@ -128,6 +147,11 @@ class SimCache:
             assert lib.hostcheck_appended_chunks() == self.appended
         for b in range(self.B):
             assert lib.hostcheck_lens_dev(b) == self.lens[b]
+        if self.paged is not None:
+            # the device table the kernels read equals the library's host table
+            host = self.block_table()
+            dev = [lib.hostcheck_table(i) for i in range(self.B * self.max_blocks)]
+            assert host.reshape(-1).tolist() == dev
         if T is not None and self.B > 0 and T > 0:
             rows = self.B * self.hq * T
             row_bytes = self.d * self.elem
@@ -339,3 +363,100 @@ def test_tree_verify_launches_and_rules(sim):
     assert call([-1] * (sh.batch * 17), 17, [0] * sh.batch) == 3       # more than 16 nodes
     sim.kv_cache_set_policy(c.h, 2, 0)
     assert call(parents) == 3
+
+
+def _paged_pair(sim, B, hk, G, d, max_len, dtype, t_max, P, pages):
+    """A simulated paged cache and the oracle's page bookkeeping (K/V of width 1)."""
+    from oracle import paged as opaged
+    c = SimCache(sim, B, hk, max_len, d, dtype, hk * G, t_max, paged=(P, pages))
+    ref = opaged.PagedCache(B, 1, pages, P, max_len // P, 1)
+    return c, ref
+
+
+def _ref_append(ref, n_new):
+    n = np.asarray(n_new)
+    T = max(int(n.max()), 1) if len(n) else 1
+    z = np.zeros((len(n), 1, T, 1), np.float32)
+    ref.append(z, z, n)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_paged_random_trials(sim, seed):
+    """Paged caches: every append writes through pages the block table gives the
+    row, every attention tile reads one page of the row, and the table the
+    kernels see equals the host table and the oracle's page assignment (lowest
+    free page first), under every kernel selection, with rollbacks freeing
+    pages along the way."""
+    shape, calls = W.trial_spec(seed, head_dims=(16, 32, 64, 128))
+    P = (64, 128, 256)[seed % 3]
+    S = -(-shape.max_len // P) * P
+    pages = shape.batch * (S // P)            # enough for every row at once
+    t_max = max([c["T"] for c in calls] + [1])
+    for policy in [(0, 0), (1, 32), (2, 64)]:
+        c, ref = _paged_pair(sim, shape.batch, shape.kv_heads, shape.group, shape.head_dim, S,
+                             "bf16" if seed % 2 else "f32", t_max, P, pages)
+        sim.kv_cache_set_policy(c.h, *policy)
+        for i, call in enumerate(calls):
+            c.append(call["T"], call["n_new"])
+            _ref_append(ref, call["n_new"])
+            c.attention(call["T"], call["n_new"])
+            c.check(call["T"])
+            assert np.array_equal(c.block_table(), ref.table)
+            assert sim.kv_free_pages(c.h) == len(ref.free)
+            if i % 3 == 2:                     # roll every row back by a third
+                new = c.lens - c.lens // 3
+                assert sim.kv_truncate(c.h, _i32(new), None) == 0
+                ref.truncate(new)
+                c.lens = new.copy()
+                c.rewrote = True
+                c.check()
+                assert np.array_equal(c.block_table(), ref.table)
+
+
+def test_paged_pool_rules(sim):
+    """A pool that cannot give a call all its pages refuses it and changes
+    nothing; so does a row past max_blocks; page sizes outside the rules and
+    E4M3 storage are refused at creation."""
+    c, ref = _paged_pair(sim, 2, 1, 4, 64, 256, "bf16", 256, 64, 5)
+    c.append(130, [130, 64])                   # 3 + 1 pages
+    _ref_append(ref, [130, 64])
+    before = (c.block_table().copy(), sim.kv_free_pages(c.h))
+    k = ctypes.c_void_p(c.addr["k_new"])
+    assert sim.kv_append(c.h, k, k, 70, _i32([70, 70]), None) == 2      # 1 + 2 pages > 1 free
+    assert b"pages needed" in sim.kv_last_error()
+    assert sim.kv_append(c.h, k, k, 130, _i32([127, 0]), None) == 2     # 257 > 4 blocks of 64
+    assert np.array_equal(c.block_table(), before[0]) and sim.kv_free_pages(c.h) == before[1]
+    c.check()
+    assert sim.kv_truncate(c.h, _i32([64, 64]), None) == 0             # row 0 frees 2 pages
+    ref.truncate([64, 64])
+    c.lens[:] = [64, 64]
+    c.rewrote = True
+    c.append(70, [70, 60])                     # 2 + 1 pages: the pool's last three
+    _ref_append(ref, [70, 60])
+    assert np.array_equal(c.block_table(), ref.table) and sim.kv_free_pages(c.h) == 0
+    c.attention(70, [70, 60])
+    c.check(70)
+    h = ctypes.c_void_p()
+    a = ctypes.c_void_p(c.addr["k"])
+    t = ctypes.c_void_p(c.addr["table"])
+    for P, pages, blocks, dt in [(32, 4, 4, 1), (96, 4, 4, 1), (64, 0, 4, 1), (64, 4, 0, 1), (64, 4, 4, 2)]:
+        st = sim.kv_cache_create_paged(2, 1, pages, P, blocks, 64, dt, a, a, t, None, None, ctypes.byref(h))
+        assert st in (1, 3), (P, pages, blocks, dt)
+
+
+def test_paged_llama_ragged(sim):
+    """The 64 ragged Llama-shaped rows (1 .. 32,000 cached, 0 to 256 new) in a
+    pool of exactly the pages their lengths need: decode and prefill launches
+    stay inside the pool, and the pool is a fraction of the dense reservation."""
+    sh = W.LLAMA8B_RAGGED
+    lens, n_new = W.ragged_rows(4)
+    P = 256
+    pages = int(sum(-(-int(L + n) // P) for L, n in zip(lens, n_new)))
+    c = SimCache(sim, sh.batch, sh.kv_heads, sh.max_len, sh.head_dim, "bf16", sh.q_heads, 4096, paged=(P, pages))
+    for call in _prefix_calls(lens):
+        c.append(call["T"], call["n_new"])
+    c.append(int(max(n_new)), n_new)
+    assert sim.kv_free_pages(c.h) == 0
+    c.attention(int(max(n_new)), n_new)
+    c.check(int(max(n_new)))
+    assert pages * P < 0.6 * sh.batch * sh.max_len
