@@ -385,6 +385,67 @@ def run_ragged(torch, seed=4, reps=20):
             "config": {"workload": sh.name, "seed": seed, "batch": B, "T": T, "sum_lens": int(sum(after))}}
 
 
+def run_paged(torch, reps=30):
+    """Paged cache ([GQA] reversal: a block table and a paged kernel): the Llama
+    decode step (B=32, 4,096 cached + 1) with rows interleaved page by page in
+    the pool, at page sizes 64 and 256, against the same step on the linear
+    cache; and the three ragged batches in a pool of exactly the pages their
+    lengths need, against the dense cache, with the bytes each holds."""
+    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    import workloads as W
+    sh = W.LLAMA8B_DECODE
+    B, hq, hkv, d = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim
+    g = torch.Generator(device="cuda").manual_seed(9)
+    q = torch.randn(B, hq, 1, d, device="cuda", generator=g).to(torch.bfloat16)
+    kn = torch.randn(B, hkv, 1, d, device="cuda", generator=g).to(torch.bfloat16)
+    n = [1] * B
+    nbytes = attention_bytes([DECODE_CACHED + 1] * B, n, hq, hkv, d, 1)
+    decode = {}
+    for name, P in (("linear", None), ("page64", 64), ("page256", 256)):
+        if P is None:
+            cache = KVCache(B, hkv, sh.max_len, d, device_lens=False)
+            _fill_gpu_random(torch, cache, [DECODE_CACHED] * B, 31)
+        else:
+            cache = KVCache(B, hkv, sh.max_len, d, device_lens=False, page_size=P,
+                            num_pages=B * -(-(DECODE_CACHED + 1) // P))
+            _fill_gpu_random(torch, cache, [DECODE_CACHED] * B, 31, chunk=P)     # rows alternate page by page
+        cache.append(kn, kn, n)
+        out = torch.empty_like(q)
+        t = _time_calls(torch, lambda i: gqa_attention(q, cache, n, out=out), reps)
+        decode[name] = {"ms": round(t * 1e3, 5), "GB/s": round(nbytes / t / 1e9, 1),
+                        "cache_bytes": cache.bytes}
+        del cache
+    ragged = []
+    rs = W.LLAMA8B_RAGGED
+    for seed in (4, 5, 6):
+        lens, n_new = W.ragged_rows(seed)
+        nl = [int(x) for x in n_new]
+        after = [int(l) + x for l, x in zip(lens, nl)]
+        T = 256
+        qr = torch.randn(rs.batch, rs.q_heads, T, d, device="cuda", generator=g).to(torch.bfloat16)
+        kr = torch.randn(rs.batch, hkv, T, d, device="cuda", generator=g).to(torch.bfloat16)
+        row = {"seed": seed}
+        for name, P in (("dense", None), ("page256", 256)):
+            if P is None:
+                cache = KVCache(rs.batch, hkv, rs.max_len, d, device_lens=False)
+            else:
+                cache = KVCache(rs.batch, hkv, rs.max_len, d, device_lens=False, page_size=P,
+                                num_pages=sum(-(-a // P) for a in after))
+            _fill_gpu_random(torch, cache, lens, 30)
+            cache.append(kr, kr, nl)
+            out = torch.empty_like(qr)
+            ws = torch.zeros(max(cache.workspace_bytes(rs.q_heads, T, nl), 256), dtype=torch.uint8, device="cuda")
+            t = _time_calls(torch, lambda i: gqa_attention(qr, cache, nl, out=out, workspace=ws), 20)
+            row[name] = {"ms": round(t * 1e3, 5), "cache_bytes": cache.bytes}
+            del cache
+        row["time_ratio"] = round(row["page256"]["ms"] / row["dense"]["ms"], 4)
+        row["bytes_ratio"] = round(row["page256"]["cache_bytes"] / row["dense"]["cache_bytes"], 4)
+        ragged.append(row)
+    return {"metric": "paged decode attention HBM GB/s", "value": decode["page256"]["GB/s"], "unit": "GB/s",
+            "decode": decode, "ragged": ragged,
+            "config": {"workload": sh.name + " / " + rs.name, "batch": B, "keys": DECODE_CACHED + 1}}
+
+
 DECODE_SEED, DECODE_CACHED = 1, 4096
 
 
@@ -485,7 +546,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "window", "fp8", "tree",
-                                       "cpu"],
+                                       "paged", "cpu"],
                     default=None,
                     help="time one workload only (for profiling); prints its own JSON line")
     ap.add_argument("--copy-probe", action="store_true",
@@ -519,9 +580,9 @@ def main():
     if args.only == "ragged":
         print(json.dumps({"ragged": [run_ragged(torch, seed) for seed in (4, 5, 6)]}), flush=True)
         return
-    if args.only in ("prefill", "verify", "append", "window", "fp8", "tree"):
+    if args.only in ("prefill", "verify", "append", "window", "fp8", "tree", "paged"):
         fn = {"prefill": run_prefill, "verify": run_verify, "append": run_append, "window": run_window,
-              "fp8": run_fp8, "tree": run_tree}[args.only]
+              "fp8": run_fp8, "tree": run_tree, "paged": run_paged}[args.only]
         print(json.dumps({args.only: fn(torch)}), flush=True)
         return
     res = run_decode(torch, args.steps, args.warmup)
