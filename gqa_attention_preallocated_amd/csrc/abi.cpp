@@ -111,8 +111,9 @@ int64_t tile_span(int32_t len, int32_t n, int tq, int qt, int32_t window) {
 // Decode work groups (kDecodeWaves waves each) the chip runs at once: one per
 // CU. Rows are split across work groups only as far as needed to fill them.
 constexpr int64_t kDecodeSlots = 256;
-// Prefill work-group slots on the chip (256 CUs x 2 resident work groups).
-constexpr int64_t kPrefillSlots = 512;
+// Prefill work-group slots on the chip: 256 CUs x one resident work group
+// (8 waves, or 4 at one wave per SIMD; prefill_waves).
+constexpr int64_t kPrefillSlots = 256;
 
 void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new, Plan &p) {
     const int G = q_heads / c->kv_heads;
@@ -175,7 +176,7 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
     }
     // ---- prefill rows: split only rows whose longest item would dominate
     {
-        const int tq = kPrefillCols / G;
+        const int tq = prefill_cols(c->dtype, c->head_dim) / G;
         int64_t total = 0;
         for (int b : pre_rows)
             for (int qt = 0; qt < ceil_div(n_new[b], tq); ++qt)
@@ -221,7 +222,7 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
         }
     };
     for (auto &r : p.dec) assign(r, p.dec_cols);
-    for (auto &r : p.pre) assign(r, kPrefillCols);
+    for (auto &r : p.pre) assign(r, prefill_cols(c->dtype, c->head_dim));
     for (int b = 0; b < c->batch; ++b)
         if (n_new[b] < T) p.pad_rows.push_back(b);
 }
@@ -720,7 +721,7 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
     // rows split across work groups: merge their partials
     std::vector<std::pair<const RowPlan *, int>> split_rows;
     for (auto &r : p.pre)
-        if (r.nsplit > 1) split_rows.push_back({&r, kPrefillCols});
+        if (r.nsplit > 1) split_rows.push_back({&r, prefill_cols(c->dtype, c->head_dim)});
     for (auto &r : p.dec)
         if (r.nsplit > 1) split_rows.push_back({&r, p.dec_cols});
     for (size_t lo = 0; lo < split_rows.size(); lo += kMaxRows) {

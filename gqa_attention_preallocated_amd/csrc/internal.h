@@ -161,7 +161,12 @@ hipError_t launch_zero_fill(const ZeroArgs &a, hipStream_t s);
 constexpr int kDecodeKeyTile = 32;
 constexpr int kDecodeWaves = 8;       // waves per decode work group (they split the keys)
 constexpr int kPrefillKeyTile = 64;
-constexpr int kPrefillCols = 128;
+// Waves per prefill work group (32 columns each): 8, one work group per CU;
+// float32 at d = 128 keeps 4 (its accumulators need the full register file
+// of one wave per SIMD). The planner and the kernels take the count from here.
+inline constexpr int prefill_waves(int dtype, int head_dim) { return (dtype == 0 && head_dim == 128) ? 4 : 8; }
+inline constexpr int prefill_cols(int dtype, int head_dim) { return 32 * prefill_waves(dtype, head_dim); }
+constexpr int kPrefillColsMax = 256;
 // Window of a linear cache: pos - kNoWindow < 0 <= every key, so no lower bound.
 constexpr int32_t kNoWindow = 0x7fffffff;
 // Ring caches hold a multiple of this many slots, and key ranges start at a

@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "indexing.h"
 #include "internal.h"
 
@@ -732,28 +734,32 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// chunked-prefill kernel: 4 waves x 32 columns = 128 columns per work item,
-// 64-key tiles of K and V shared by the 4 waves through double-buffered LDS.
+// chunked-prefill kernel: PW waves x 32 columns per work item, 64-key tiles
+// of K and V shared by the waves through double-buffered LDS. With PW = 8 one
+// work group fills a CU at two waves per SIMD; eight waves rather than four
+// halve the staging (global loads, LDS stores, their registers) per FLOP.
+// float32 at d = 128 runs PW = 4 at one wave per SIMD (prefill_waves).
 // Key tiles past the last query's position are never loaded; tiles wholly at
 // or below the first query's position are not masked; only tiles straddling
 // the diagonal compare indices ([MASK] "A strong answer", tiled-kernel rule).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool F8, bool PG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(AttnArgs a) {
+template <typename E, int D, bool F8, bool PG, int PW>
+__global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8 ? 2 : 1))) void prefill_kernel(AttnArgs a) {
     using O = Op<E>;
     using S = Stor<E, F8>;
     using vec = typename O::vec;
     constexpr int KT = kPrefillKeyTile;           // 64 keys per tile
     constexpr int KC = D >= 32 ? D / 32 : 1;
     constexpr int NB = D / 16;
-    constexpr int C = kPrefillCols;               // 128 columns per item
+    constexpr int C = 32 * PW;                    // columns per item
+    constexpr int NT = 64 * PW;                   // threads per work group
     constexpr int NS = 2;                         // 16-column subtiles per wave
     constexpr int ROWB = D * O::kBytes;           // LDS bytes of a K or V row (compute type)
     constexpr int RS = ROWB + O::kPad;
     constexpr int CROWB = D * S::kBytes;          // cache bytes of a row
     constexpr int CPK = CROWB / 16;               // 16-byte cache chunks per row
     constexpr int TILE_BYTES = KT * RS;
-    constexpr int PCH = (KT * CPK + 255) / 256;   // 16-byte chunks per thread per tensor
+    constexpr int PCH = (KT * CPK + NT - 1) / NT; // 16-byte chunks per thread per tensor
     __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE_BYTES];
     __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][TILE_BYTES];
 
@@ -820,14 +826,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     auto load = [&](uint4 (&reg)[PCH], const unsigned char *base, int64_t row0, int tile) {
         const __amdgpu_buffer_rsrc_t r = buffer_view(base + row0 * CROWB, imin(it.k_end - tile, KT) * CROWB);
 #pragma unroll
-        for (int i = 0; i < PCH; ++i) reg[i] = buffer_load_stream(r, (tid + 256 * i) * 16);
+        for (int i = 0; i < PCH; ++i) reg[i] = buffer_load_stream(r, (tid + NT * i) * 16);
     };
     // into LDS in the compute type (an E4M3 chunk of 16 codes becomes 32 bytes)
     auto store = [&](const uint4 (&reg)[PCH], unsigned char *dst) {
 #pragma unroll
         for (int i = 0; i < PCH; ++i) {
-            const int c = tid + 256 * i;
-            if ((KT * CPK) % 256 == 0 || c < KT * CPK) S::stage(dst + (c / CPK) * RS + (c % CPK) * S::kLdsPerChunk, reg[i]);
+            const int c = tid + NT * i;
+            if ((KT * CPK) % NT == 0 || c < KT * CPK) S::stage(dst + (c / CPK) * RS + (c % CPK) * S::kLdsPerChunk, reg[i]);
         }
     };
     // S^T of one 64-key tile for the wave's 32 columns (32 MFMAs)
@@ -907,8 +913,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // Staging: iteration i writes K(i+1) and V(i-1) to LDS, then one barrier.
     // Its stores run before that barrier, so a slower wave may still be in
     // iteration i-1, which reads K(i) and V(i-2); the slots written hold
-    // K(i-1) and V(i-3), last read in iteration i-2. The tile loads for those
-    // stores (K(i+2), V(i)) are issued right after the barrier. V(last) is
+    // K(i-1) and V(i-3), last read in iteration i-2. The tile loads for the
+    // next stores (K(i+2), V(i)) are issued right after this iteration's
+    // stores, before the barrier, into the registers just stored. V(last) is
     // staged after the loop behind its own barrier. A wave computes tiles
     // 0..wave_last only (tiles past its last query are skipped; it still
     // takes part in staging and barriers).
@@ -917,48 +924,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     f32x4 sc[2][NS][2];
     vec pb[2][NS];
 
-    // phase X: 2*NB steps of PV (ch = g / NB, nb = g % NB, both subtiles), then
-    // the two all-ones MFMAs per chunk; VALU: the max tree of tile i as ten
-    // tasks (per subtile: four quarter maxima, then the column max), task t
-    // at step t * NSX / 10 so every task runs after the ones it needs
+    // probability pair u (0..7) of chunk ch of tile i: subtile u / 4, elements
+    // 2 (u % 4) and 2 (u % 4) + 1, packed into the PV operand
+    auto prob_pair = [&](int ch, int u, float m) {
+        const int ps = u >> 2, j = (u & 3) * 2;
+        O::set_pair(pb[ch][ps], j, fast_exp2(fmaf(sc[ch][ps][j >> 2][j & 3], score_c, -m)),
+                    fast_exp2(fmaf(sc[ch][ps][(j + 1) >> 2][(j + 1) & 3], score_c, -m)));
+    };
+    // the reference max as it stands before tile i's rescale decision
+    auto ref_max = [&](float (&m)[NS]) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) m[s] = (st[s].m == -INFINITY) ? 0.f : st[s].m;
+    };
+
+    // phase X: 2*NB steps of PV (ch = g / NB, nb = g % NB, both subtiles), the
+    // all-ones MFMAs of chunk 0 after step NB-1 and of chunk 1 at the end.
+    // VALU, first NB steps: the max tree of tile i as ten tasks (per subtile:
+    // four quarter maxima, then the column max), task t at step t * NB / 10 so
+    // every task runs after the ones it needs. VALU, last NB steps (chunk 0's
+    // operands are consumed by then): the probabilities of chunk 0 of tile i
+    // against the current reference max, task u at step NB + u * NB / 8. The
+    // reference only moves when a column's max outgrows it by more than
+    // kRescaleLog2; finish_max then recomputes chunk 0 for those columns, so
+    // every probability of the tile uses one reference, as if computed after
+    // the decision.
     auto phase_x = [&](const unsigned char *vp, float (&tmax)[NS]) {
         constexpr int NSX = 2 * NB;
-        vec vt[2];
+        float m0[NS];
+        ref_max(m0);
+        // V^T operands are read from LDS two steps ahead of their MFMAs
+        vec vt[3];
         vt[0] = O::vt_operand(vp, RS, 0, 0, lane);
+        if (NSX > 1) vt[1] = O::vt_operand(vp, RS, (1 / NB) * 32, (1 % NB) * 16, lane);
         float part[NS][4];
 #pragma unroll
         for (int g = 0; g < NSX; ++g) {
             const int ch = g / NB, nb = g % NB;
-            if (g + 1 < NSX) vt[(g + 1) & 1] = O::vt_operand(vp, RS, ((g + 1) / NB) * 32, ((g + 1) % NB) * 16, lane);
+            if (g + 2 < NSX) vt[(g + 2) % 3] = O::vt_operand(vp, RS, ((g + 2) / NB) * 32, ((g + 2) % NB) * 16, lane);
 #pragma unroll
-            for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt[g & 1], pb[ch][s], acc[s][nb]);
+            for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt[g % 3], pb[ch][s], acc[s][nb]);
+            if (g == NB - 1) {
 #pragma unroll
-            for (int t = 0; t < 10; ++t) {
-                if (t * NSX / 10 != g) continue;
-                if (t < 8) {
-                    const int s = t >> 2, q = t & 3;      // quarter q = (ch, ks) block
-                    const f32x4 x = sc[q >> 1][s][q & 1];
-                    part[s][q] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-                } else {
-                    const int s = t - 8;
-                    const float m4 = fmaxf(fmaxf(part[s][0], part[s][1]), fmaxf(part[s][2], part[s][3]));
-                    tmax[s] = wave_max_across_groups(m4) * score_c;
+                for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, pb[0][s], acc[s][NB]);
+            }
+            if (g < NB) {
+#pragma unroll
+                for (int t = 0; t < 10; ++t) {
+                    if (t * NB / 10 != g) continue;
+                    if (t < 8) {
+                        const int s = t >> 2, q = t & 3;      // quarter q = (ch, ks) block
+                        const f32x4 x = sc[q >> 1][s][q & 1];
+                        part[s][q] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+                    } else {
+                        const int s = t - 8;
+                        const float m4 = fmaxf(fmaxf(part[s][0], part[s][1]), fmaxf(part[s][2], part[s][3]));
+                        tmax[s] = wave_max_across_groups(m4) * score_c;
+                    }
                 }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (NB + u * NB / 8 == g) prob_pair(0, u, m0[u >> 2]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-            for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, pb[ch][s], acc[s][NB]);
+        for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, pb[1][s], acc[s][NB]);
     };
-    // phase Y: 16 steps of scores for tile i+1 (ch = g / 8, ks = (g / 4) % 2,
-    // kc = g % 4, both subtiles; steps with kc >= KC issue no MFMA); VALU: 2
-    // of the 32 probabilities of tile i per step, packed into the operand
+    // phase Y: 16 steps of scores for tile i+1 (ch = g / 8, kc = (g / 2) % 4,
+    // ks = g % 2, both subtiles; steps with kc >= KC issue no MFMA): an
+    // accumulator is updated every fourth MFMA, and only the four of one
+    // chunk are live while the probabilities of chunk 1 of tile i, one pair
+    // in each of the first 8 steps, free their scores
     auto phase_y = [&](const unsigned char *kn, const float (&m_use)[NS], f32x4 (&scn)[2][NS][2]) {
         auto kop = [&](int g) {
-            const int krow = (g >> 3) * 32 + ((g >> 2) & 1) * 16 + lr;
-            const int d0 = (g & 3) * 32 + lg * 8;
+            const int krow = (g >> 3) * 32 + (g & 1) * 16 + lr;
+            const int d0 = ((g >> 1) & 3) * 32 + lg * 8;
             return (d0 < D) ? O::lds_load(kn + krow * RS + d0 * O::kBytes) : O::zero();
         };
         vec kv[3];
@@ -966,7 +1007,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         kv[1] = kop(1);
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
-            const int ch = g >> 3, ks = (g >> 2) & 1, kc = g & 3;
+            const int ch = g >> 3, kc = (g >> 1) & 3, ks = g & 1;
             if (g + 2 < 16) kv[(g + 2) % 3] = kop(g + 2);
             if (kc < KC) {
 #pragma unroll
@@ -975,19 +1016,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                     scn[ch][s][ks] = O::mma(kv[g % 3], qop[s][kc], c0);
                 }
             }
-            // probabilities: step g covers (ch', s') = (g / 8, (g / 4) % 2), elements 2 (g % 4) .. +1
-            {
-                const int pc = g >> 3, ps = (g >> 2) & 1, j = (g & 3) * 2;
-                O::set_pair(pb[pc][ps], j, fast_exp2(fmaf(sc[pc][ps][j >> 2][j & 3], score_c, -m_use[ps])),
-                            fast_exp2(fmaf(sc[pc][ps][(j + 1) >> 2][(j + 1) & 3], score_c, -m_use[ps])));
-            }
+            if (g < 8) prob_pair(1, g, m_use[g >> 2]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto finish_max = [&](const float (&tmax)[NS], float (&m_use)[NS]) {
-        // move the reference max where a column's max outgrew it by more than
-        // kRescaleLog2 (st.m = -inf: the first visible key sets it; alpha is
-        // then 0 and acc is still 0)
+    // move the reference max where a column's max outgrew it by more than
+    // kRescaleLog2 (st.m = -inf: the first visible key sets it; alpha is then
+    // 0 and acc is still 0), and give those columns chunk 0 again against the
+    // new reference; with chunk0_done false, chunk 0 is computed here for all
+    auto finish_max = [&](const float (&tmax)[NS], float (&m_use)[NS], bool chunk0_done) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             if (tmax[s] > st[s].m + kRescaleLog2) {
@@ -995,8 +1032,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
                 for (int nb = 0; nb <= NB; ++nb) acc[s][nb] *= alpha;
                 st[s].m = tmax[s];
+                if (chunk0_done) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) prob_pair(0, s * 4 + u, tmax[s]);
+                }
             }
             m_use[s] = (st[s].m == -INFINITY) ? 0.f : st[s].m;    // no key seen yet: every p is 0
+        }
+        if (!chunk0_done) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) prob_pair(0, u, m_use[u >> 2]);
         }
     };
 
@@ -1020,7 +1065,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         const unsigned char *vp = lds_v[(i + 1) & 1];  // V(i-1)
         if (has_next) store(kreg, lds_k[(i + 1) & 1]);
         if (i > 0) store(vreg, lds_v[(i + 1) & 1]);
-        __syncthreads();
+        // the registers are free again: the next loads go out before the
+        // barrier, so they have the barrier wait as well as one iteration
         int64_t row_k2 = 0;
         if (i + 2 < ntiles) {
             row_k2 = km.row(tile + 2 * KT);
@@ -1029,6 +1075,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         if (i > 0) load(vreg, vbase, row_cur, tile);     // V(0) came with the prologue
         row_cur = row_next;
         row_next = row_k2;
+        __syncthreads();
         if (i > wave_last) {
             if (i == wave_last + 1 && wave_last >= 0) pv(vp, pb);   // the last tile this wave computed
             continue;
@@ -1040,7 +1087,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         __builtin_amdgcn_s_setprio(1);
         if (i > 0) phase_x(vp, tmax);
         else tile_max(sc, tmax);
-        finish_max(tmax, m_use);
+        finish_max(tmax, m_use, i > 0);
         // on the last tile the K slot holds an older tile: those scores are never used
         f32x4 scn[2][NS][2];
         phase_y(kn, m_use, scn);
@@ -1236,14 +1283,19 @@ hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, h
     }
 }
 
+template <typename E, int D, bool F8, bool PG>
+static void prefill_d(const AttnArgs &a, hipStream_t s) {
+    constexpr int PW = prefill_waves(std::is_same<E, float>::value ? 0 : 1, D);
+    hipLaunchKernelGGL((prefill_kernel<E, D, F8, PG, PW>), dim3(a.rows.total_items), dim3(64 * PW), 0, s, a);
+}
+
 template <typename E, bool F8, bool PG>
 static hipError_t prefill_e(int head_dim, const AttnArgs &a, hipStream_t s) {
-    const dim3 grid(a.rows.total_items), block(256);
     switch (head_dim) {
-        case 16: hipLaunchKernelGGL((prefill_kernel<E, 16, F8, PG>), grid, block, 0, s, a); break;
-        case 32: hipLaunchKernelGGL((prefill_kernel<E, 32, F8, PG>), grid, block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((prefill_kernel<E, 64, F8, PG>), grid, block, 0, s, a); break;
-        case 128: hipLaunchKernelGGL((prefill_kernel<E, 128, F8, PG>), grid, block, 0, s, a); break;
+        case 16: prefill_d<E, 16, F8, PG>(a, s); break;
+        case 32: prefill_d<E, 32, F8, PG>(a, s); break;
+        case 64: prefill_d<E, 64, F8, PG>(a, s); break;
+        case 128: prefill_d<E, 128, F8, PG>(a, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -299,7 +299,8 @@ hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, h
 
 hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t) {
     if (head_dim != a.head_dim) err("prefill: head_dim mismatch");
-    sim_attention(a, kPrefillCols, kPrefillKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
+    sim_attention(a, prefill_cols(dtype, head_dim), kPrefillKeyTile, dtype == 0 ? 4 : 2,
+                  dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
     return hipSuccess;
 }
 
