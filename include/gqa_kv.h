@@ -30,10 +30,13 @@
  * host thread at a time and kept in stream order by the caller.
  *
  * Errors. Every call validates all of its arguments on the host before it
- * enqueues anything. A status other than KV_OK means nothing was enqueued and
- * no state changed: not the host lengths, not the device lengths, not a byte
- * of K or V. kv_last_error() returns the message of the last failing call on
- * the calling thread.
+ * enqueues anything. KV_ERR_INVALID_ARG, KV_ERR_CAPACITY, KV_ERR_UNSUPPORTED
+ * and KV_ERR_WORKSPACE mean nothing was enqueued and no state changed: not
+ * the host lengths, not the device lengths, not a byte of K or V, not a page
+ * of a paged cache. KV_ERR_DEVICE means a HIP launch failed part way through
+ * a call that enqueues several kernels; the handle's state is then
+ * unspecified and it should be destroyed. kv_last_error() returns the message
+ * of the last failing call on the calling thread.
  */
 #ifndef GQA_KV_H
 #define GQA_KV_H

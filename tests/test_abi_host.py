@@ -103,6 +103,31 @@ def test_truncate_rules_and_bytes(lib):
     lib.kv_cache_destroy(h)
 
 
+def test_paged_create_validation(lib):
+    """kv_cache_create_paged refuses bad pool geometry and E4M3 storage before
+    enqueueing anything; the block-table query refuses a linear cache."""
+    h = ctypes.c_void_p()
+    a, t = ctypes.c_void_p(1 << 20), ctypes.c_void_p(3 << 20)
+    bad = [
+        (64 - 16, 8, 4, 1, 1),      # page size not a power of two
+        (32, 8, 4, 1, 1),           # below 64
+        (1 << 17, 8, 4, 1, 1),      # above 65,536
+        (64, 0, 4, 1, 1),           # no pages
+        (64, 8, 0, 1, 1),           # no blocks
+        (64, 8, 4, 2, 3),           # E4M3
+    ]
+    for P, pages, blocks, dt, code in bad:
+        st = lib.kv_cache_create_paged(2, 2, pages, P, blocks, 64, dt, a, a, t, None, None, ctypes.byref(h))
+        assert st == code, (P, pages, blocks, dt, lib.kv_last_error())
+    st = lib.kv_cache_create_paged(2, 2, 8, 64, 4, 64, 1, a, a, ctypes.c_void_p((3 << 20) + 4), None, None,
+                                   ctypes.byref(h))
+    assert st == 1                  # misaligned block table
+    lin = _fake_cache(lib)
+    assert lib.kv_get_block_table(lin, _arr([0] * 8)) == 1
+    assert lib.kv_free_pages(lin) == 0
+    lib.kv_cache_destroy(lin)
+
+
 def test_python_layer_refuses_without_gpu_buffers():
     import torch
     from gqa_attention_preallocated_amd import KVCache

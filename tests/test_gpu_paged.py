@@ -167,3 +167,36 @@ def test_llama_paged_ragged(seed):
         ref = direct.attention_row(kr, vr, L, nb, q[b], "bf16", pairs)
         for h, t in pairs:
             assert_close(got[b, h, t], ref[h, t], "bf16", f"paged ragged row {b} (len {L}) head {h} t {t}")
+
+
+def test_paged_edges():
+    """Empty batches and calls, rows filled exactly to max_blocks, a reset that
+    returns every page, and a refill that takes pages lowest first again."""
+    KVCache, gqa_attention = _lib()
+    c0 = KVCache(0, 2, 256, 32, dtype=torch.float32, page_size=64, num_pages=4)
+    assert gqa_attention(torch.zeros((0, 4, 3, 32), device="cuda"), c0, []).shape == (0, 4, 3, 32)
+    B, hk, d, P, S = 2, 1, 32, 64, 256
+    cache = KVCache(B, hk, S, d, dtype=torch.float32, page_size=P, num_pages=8)
+    q = torch.full((B, 2, 3, d), float("nan"), device="cuda")
+    out = gqa_attention(q, cache, [0, 0])                 # empty cache, no new tokens
+    assert torch.equal(out, torch.zeros_like(out))
+    assert gqa_attention(torch.zeros((B, 2, 0, d), device="cuda"), cache, [0, 0]).shape == (B, 2, 0, d)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    k = torch.randn(B, hk, S, d, device="cuda", generator=g)
+    cache.append(k, k, [S, S])                            # both rows full: all 8 pages
+    assert cache.free_pages == 0 and cache.lens == [S, S]
+    with pytest.raises(ValueError):
+        cache.append(k[:, :, :1].contiguous(), k[:, :, :1].contiguous(), [1, 0])
+    qq = torch.randn(B, 2, 1, d, device="cuda", generator=g)
+    cache.truncate([S - 1, S - 1])
+    cache.append(k[:, :, -1:].contiguous(), k[:, :, -1:].contiguous(), [1, 1])
+    ref = paged.PagedCache(B, hk, 8, P, S // P, d, "f32")
+    kk = k.cpu().numpy()
+    ref.append(kk, kk, [S, S])
+    got = out_f64(gqa_attention(qq, cache, [1, 1]), "f32")
+    assert_close(got, paged.attention(ref, qq.cpu().numpy(), [1, 1]), "f32", "full rows")
+    cache.reset()
+    assert cache.free_pages == 8 and all(e == -1 for row in cache.block_table for e in row)
+    assert (cache.block_table_dev.cpu() == -1).all()
+    cache.append(k[:, :, :65].contiguous(), k[:, :, :65].contiguous(), [65, 1])
+    assert cache.block_table[0][:2] == [0, 1] and cache.block_table[1][0] == 2
