@@ -166,7 +166,6 @@ constexpr int kPrefillKeyTile = 64;
 // of one wave per SIMD). The planner and the kernels take the count from here.
 inline constexpr int prefill_waves(int dtype, int head_dim) { return (dtype == 0 && head_dim == 128) ? 4 : 8; }
 inline constexpr int prefill_cols(int dtype, int head_dim) { return 32 * prefill_waves(dtype, head_dim); }
-constexpr int kPrefillColsMax = 256;
 // Window of a linear cache: pos - kNoWindow < 0 <= every key, so no lower bound.
 constexpr int32_t kNoWindow = 0x7fffffff;
 // Ring caches hold a multiple of this many slots, and key ranges start at a
