@@ -639,37 +639,18 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
     const WsLayout w = ws_layout(c, p);
     char *ws = (char *)workspace;
 
-    // A batch with both decode and prefill rows runs the decode kernel on a
-    // side stream forked from (and later joined back to) the caller's stream,
-    // beside the zero fill and the prefill kernel, so no kernel's ramp and
-    // tail idles the chip. The three write disjoint output slots.
-    const bool mixed = !p.pre.empty() && !p.dec.empty();
+    // A call with prefill rows runs the decode kernel and the zero fill on a
+    // side stream forked from (and later joined back to) the caller's
+    // stream, beside the prefill kernel: the MFMA-bound prefill then starts
+    // at once and the HBM-bound work fills the chip around it. The three
+    // write disjoint output slots.
+    const bool mixed = !p.pre.empty() && (!p.dec.empty() || !p.pad_rows.empty());
     hipStream_t dec_stream = st;
     if (mixed) {
         hipError_t e = side_stream_init(c->side);
         if (e == hipSuccess) e = side_stream_fork(c->side, st);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (side stream)");
         dec_stream = c->side.side;
-    }
-
-    // padded slots: independent of the attention kernels
-    for (size_t lo = 0; lo < p.pad_rows.size(); lo += kMaxRows) {
-        ZeroArgs z{};
-        z.out = out;
-        z.batch = c->batch;
-        z.T = T;
-        z.hq = q_heads;
-        z.head_dim = c->head_dim;
-        z.row_bytes = (int64_t)c->head_dim * c->io_bytes;
-        z.slices = (int32_t)ceil_div((int64_t)T * z.row_bytes, kZeroSlice);
-        const size_t hi = std::min(p.pad_rows.size(), lo + kMaxRows);
-        z.rows.n_rows = (int32_t)(hi - lo);
-        for (size_t i = lo; i < hi; ++i) {
-            z.rows.b[i - lo] = p.pad_rows[i];
-            z.rows.nnew[i - lo] = n_new[p.pad_rows[i]];
-        }
-        hipError_t e = launch_zero_fill(z, st);
-        if (e != hipSuccess) return device_fail(e, "gqa_attention (zero fill)");
     }
 
     AttnArgs a{};
@@ -708,6 +689,26 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
         }
         hipError_t e = launch_decode((int)c->dtype, c->head_dim, p.nsub, a, dec_stream);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (decode kernel)");
+    }
+
+    // padded slots: independent of the attention kernels
+    for (size_t lo = 0; lo < p.pad_rows.size(); lo += kMaxRows) {
+        ZeroArgs z{};
+        z.out = out;
+        z.batch = c->batch;
+        z.T = T;
+        z.hq = q_heads;
+        z.head_dim = c->head_dim;
+        z.row_bytes = (int64_t)c->head_dim * c->io_bytes;
+        z.slices = (int32_t)ceil_div((int64_t)T * z.row_bytes, kZeroSlice);
+        const size_t hi = std::min(p.pad_rows.size(), lo + kMaxRows);
+        z.rows.n_rows = (int32_t)(hi - lo);
+        for (size_t i = lo; i < hi; ++i) {
+            z.rows.b[i - lo] = p.pad_rows[i];
+            z.rows.nnew[i - lo] = n_new[p.pad_rows[i]];
+        }
+        hipError_t e = launch_zero_fill(z, dec_stream);
+        if (e != hipSuccess) return device_fail(e, "gqa_attention (zero fill)");
     }
     for (size_t lo = 0; lo < p.pre.size(); lo += kMaxRows) {
         fill_attn_rows(p.pre, lo, std::min(p.pre.size(), lo + kMaxRows), c->kv_heads, a.rows);

@@ -231,10 +231,10 @@ kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32
  *                 before it is read in the same call, so the contents need no
  *                 initialisation. Two calls in flight at once must not share a
  *                 workspace.
- * A batch that holds both decode rows and prefill rows runs the decode kernel
- * on a stream the handle owns, forked from `stream` by an event before any of
- * the call's work and joined back to it before the call's last kernel, so the
- * call as a whole stays in `stream` order.
+ * A call with prefill-kernel rows runs its decode kernel and its zero fill of
+ * padded slots on a stream the handle owns, forked from `stream` by an event
+ * before any of the call's work and joined back to it before the call's last
+ * kernel, so the call as a whole stays in `stream` order.
  * Returns KV_ERR_INVALID_ARG for a bad shape, a q_heads that is not a positive
  * multiple of kv_heads, or a bad n_new; KV_ERR_UNSUPPORTED when G > 128;
  * KV_ERR_WORKSPACE when the workspace is too small.
