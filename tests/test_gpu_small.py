@@ -120,6 +120,41 @@ def test_prefill_many_key_tiles(dt, d):
     _run_schedule(shape, calls, 11, (2, 4096), check_bytes=False)
 
 
+@pytest.mark.parametrize("policy", [(0, 0), (1, 32), (2, 64)])
+def test_more_rows_than_one_launch(policy):
+    """150 rows: every kernel (append, decode, prefill, combine, zero fill)
+    is split over several launches of at most 64 rows, with decode, verify,
+    prefill and idle rows mixed in each call and a rollback between calls."""
+    B = 150
+    shape = W.Shape("rows150", "bf16", B, 8, 2, 32, 512)
+    rng = np.random.default_rng(12)
+    first = rng.integers(1, 300, B)
+    calls = [{"T": int(first.max()), "n_new": first.tolist()}]
+    for _ in range(2):
+        n = rng.choice([0, 1, 3, 40], B)
+        calls.append({"T": 40, "n_new": n.tolist()})
+    KVCache, gqa_attention = _lib()
+    cache = KVCache(B, 2, 512, 32)
+    cache.set_policy(*policy)
+    ref = direct.Cache(B, 2, 512, 32, "bf16")
+    for i, call in enumerate(calls):
+        T, n = call["T"], call["n_new"]
+        q, k, v = W.step_inputs(shape, 13, i, T, n, pad="nan")
+        cache.append(to_dev(k, "bf16"), to_dev(v, "bf16"), n)
+        ref.append(k, v, n)
+        out = gqa_attention(to_dev(q, "bf16"), cache, n)
+        assert_close(out_f64(out, "bf16"), direct.attention(ref, q, n), "bf16", f"call {i} policy {policy}")
+        raw = from_dev(out, "bf16")
+        for b in range(B):
+            assert not raw[b, :, n[b]:].view(np.uint8).any(), "padded slot not +0.0"
+        assert same_bytes(from_dev(cache.k, "bf16"), ref.k) and same_bytes(from_dev(cache.v, "bf16"), ref.v)
+        if i == 1:
+            back = [max(0, L - 2) for L in cache.lens]
+            cache.truncate(back)
+            ref.truncate(back)
+        assert cache.lens_dev.cpu().tolist()[:B] == ref.lens.tolist()
+
+
 def test_nan_in_padding_and_stale_tail_never_leaks():
     """NaN in padded q/k/v slots and in the cache past each row's length must not
     reach the output (stale slots are never read)."""
