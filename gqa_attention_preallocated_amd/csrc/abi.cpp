@@ -679,6 +679,7 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c->head_dim));
 
     a.tree = parents != nullptr;
+    a.cols = p.dec_cols;
     for (size_t lo = 0; lo < p.dec.size(); lo += kMaxRows) {
         fill_attn_rows(p.dec, lo, std::min(p.dec.size(), lo + kMaxRows), c->kv_heads, a.rows);
         if (a.tree) {
@@ -710,6 +711,8 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
         hipError_t e = launch_zero_fill(z, dec_stream);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (zero fill)");
     }
+    a.cols = prefill_cols(c->dtype, c->head_dim);
+    a.tree = 0;
     for (size_t lo = 0; lo < p.pre.size(); lo += kMaxRows) {
         fill_attn_rows(p.pre, lo, std::min(p.pre.size(), lo + kMaxRows), c->kv_heads, a.rows);
         hipError_t e = launch_prefill((int)c->dtype, c->head_dim, a, st);

@@ -85,6 +85,7 @@ struct AttnArgs {
     float *ws_acc;             // partial records: unnormalised acc [rec][d]
     float *ws_ml;              // partial records: (running max in log2 units, sum) [rec][2]
     int32_t batch, T, hq, hkv, group, max_len, head_dim;
+    int32_t cols;              // columns (query, head pairs) per work item of this launch
     int32_t window;            // keys a query sees: pos - window < key <= pos (kNoWindow: no lower bound)
     int64_t records;           // partial records available in the workspace
     float scale_log2;          // log2(e) / sqrt(d)

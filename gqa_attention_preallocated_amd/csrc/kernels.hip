@@ -471,7 +471,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     constexpr int KT = kDecodeKeyTile;            // 32 keys per tile
     constexpr int KC = D >= 32 ? D / 32 : 1;      // 32-wide chunks of d
     constexpr int NB = D / 16;                    // 16-row blocks of O^T
-    constexpr int C = 16 * NSUB;
+    // columns per work item: a.cols (the planner's choice, at most 16 * NSUB;
+    // columns past it are padding and see no key)
     constexpr int ROWB = D * O::kBytes;           // LDS bytes of one V row (compute type)
     constexpr int RS = ROWB + O::kPad;            // padded LDS row: conflict-free transposed reads
     constexpr int CROWB = D * S::kBytes;          // cache bytes of one K or V row
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     const int wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     unsigned char *lds = lds_all + wave * STAGE;
-    const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, C, a.window);
+    const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, a.cols, a.window);
 
     // this wave's share of the item's keys: every W-th 32-key tile from its
     // own, so at any time the work group streams one contiguous run of K and
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
         const int col = s * 16 + lr;
-        pos[s] = column_position(it, col, a.group, C);
+        pos[s] = column_position(it, col, a.group, a.cols);
         const E *qp = pos[s] >= 0 ? column_q<E>(a, it, col, D) : nullptr;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
@@ -705,7 +706,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         for (int task = tid; task < 16 * DC; task += 64 * W) {
             const int c16 = task / DC, d = (task % DC) * 4;
             const int col = s * 16 + c16;
-            if (column_position(it, col, a.group, C) < 0) continue;
+            if (column_position(it, col, a.group, a.cols) < 0) continue;
             float M = -INFINITY;
 #pragma unroll
             for (int w = 0; w < W; ++w) M = fmaxf(M, pml[(w * 16 + c16) * 2]);

@@ -293,14 +293,18 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
 
 hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t) {
     if (head_dim != a.head_dim) err("decode: head_dim mismatch");
-    sim_attention(a, 16 * nsub, kDecodeKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
+    // the kernel's register tiling holds 16 * nsub columns; the items use a.cols of them
+    if (nsub != 1 && nsub != 2 && nsub != 4) err("decode: bad subtile count");
+    if (a.cols < a.group || a.cols > 16 * nsub || (nsub > 1 && a.cols <= 8 * nsub))
+        err("decode: item columns do not fit the kernel's tiling");
+    sim_attention(a, a.cols, kDecodeKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
     return hipSuccess;
 }
 
 hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t) {
     if (head_dim != a.head_dim) err("prefill: head_dim mismatch");
-    sim_attention(a, prefill_cols(dtype, head_dim), kPrefillKeyTile, dtype == 0 ? 4 : 2,
-                  dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
+    if (a.cols != prefill_cols(dtype, head_dim)) err("prefill: columns differ from the kernel's");
+    sim_attention(a, a.cols, kPrefillKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
     return hipSuccess;
 }
 
