@@ -446,6 +446,49 @@ def run_paged(torch, reps=30):
             "config": {"workload": sh.name + " / " + rs.name, "batch": B, "keys": DECODE_CACHED + 1}}
 
 
+def run_probe(torch, reps=10):
+    """Streaming-read probe (bench_probe.hip, built beside the library): the HBM
+    read rate of a plain 16-byte-load kernel, plain and non-temporal, over two
+    alternating 1 GiB buffers (four times the MALL). The attention kernels'
+    rates are quoted against it as the practical ceiling."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbench_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.probe_stream_read.restype = ctypes.c_int
+    nbytes = 1 << 30
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda"), torch.full((nbytes,), 2, dtype=torch.uint8,
+                                                                             device="cuda")]
+    sink = torch.empty(32768 * 256, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = {}
+    for nt in (0, 1):
+        for blocks in (2048, 4096, 8192, 16384):
+            ts = []
+            for r in range(reps + 2):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                rc = lib.probe_stream_read(ctypes.c_void_p(bufs[r & 1].data_ptr()), nbytes, blocks, nt,
+                                           ctypes.c_void_p(sink.data_ptr()), stream)
+                e1.record()
+                torch.cuda.synchronize()
+                if rc != 0:
+                    raise RuntimeError(f"probe_stream_read returned {rc}")
+                if r >= 2:
+                    ts.append(e0.elapsed_time(e1) * 1e-3)
+            gbs = nbytes / sorted(ts)[len(ts) // 2] / 1e9
+            key = "nontemporal" if nt else "plain"
+            if gbs > best.get(key, (0, 0))[0]:
+                best[key] = (gbs, blocks)
+    del bufs, sink
+    return {"plain_GB/s": round(best["plain"][0], 1), "plain_blocks": best["plain"][1],
+            "nontemporal_GB/s": round(best["nontemporal"][0], 1), "nontemporal_blocks": best["nontemporal"][1],
+            "bytes": nbytes, "note": "median of %d reads per launch shape; best shape reported" % reps}
+
+
 DECODE_SEED, DECODE_CACHED = 1, 4096
 
 
@@ -546,7 +589,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "window", "fp8", "tree",
-                                       "paged", "cpu"],
+                                       "paged", "probe", "cpu"],
                     default=None,
                     help="time one workload only (for profiling); prints its own JSON line")
     ap.add_argument("--copy-probe", action="store_true",
@@ -580,9 +623,9 @@ def main():
     if args.only == "ragged":
         print(json.dumps({"ragged": [run_ragged(torch, seed) for seed in (4, 5, 6)]}), flush=True)
         return
-    if args.only in ("prefill", "verify", "append", "window", "fp8", "tree", "paged"):
+    if args.only in ("prefill", "verify", "append", "window", "fp8", "tree", "paged", "probe"):
         fn = {"prefill": run_prefill, "verify": run_verify, "append": run_append, "window": run_window,
-              "fp8": run_fp8, "tree": run_tree, "paged": run_paged}[args.only]
+              "fp8": run_fp8, "tree": run_tree, "paged": run_paged, "probe": run_probe}[args.only]
         print(json.dumps({args.only: fn(torch)}), flush=True)
         return
     res = run_decode(torch, args.steps, args.warmup)
@@ -618,6 +661,10 @@ def main():
     }
     if not args.no_prefill:
         line["prefill"] = run_prefill(torch)
+        probe = run_probe(torch)
+        if probe is not None:
+            probe["decode_kernel_frac"] = round(achieved / probe["nontemporal_GB/s"], 4)
+            line["read_probe"] = probe
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
