@@ -83,6 +83,8 @@ class KVCache:
         if fp8_scales is not None and (dtype != torch.bfloat16 or window is not None):
             raise ValueError("an E4M3 cache takes bfloat16 inputs and has no window")
         self.paged = page_size is not None
+        self.page_size = self.num_pages = None
+        self.max_blocks = 0
         if self.paged:
             if num_pages is None or window is not None or fp8_scales is not None:
                 raise ValueError("a paged cache needs num_pages and has no window or E4M3 storage")

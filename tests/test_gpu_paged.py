@@ -127,6 +127,10 @@ def test_paged_pool_refusals():
         KVCache(2, 1, 256, 16, dtype=torch.float32, page_size=48, num_pages=3)
     with pytest.raises(ValueError):
         KVCache(2, 1, 256, 16, page_size=64, num_pages=3, fp8_scales=([1.0], [1.0]))
+    linear = KVCache(2, 1, 256, 16, dtype=torch.float32)
+    with pytest.raises(ValueError, match="not a paged cache"):
+        linear.block_table
+    assert linear.free_pages == 0
 
 
 @pytest.mark.parametrize("seed", [4, 5])
