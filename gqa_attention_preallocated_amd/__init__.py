@@ -23,7 +23,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["KVCache", "gqa_attention", "library_path"]
+__all__ = ["KVCache", "gqa_attention", "append_attention", "library_path"]
 
 _DTYPES = {torch.float32: _lib.KV_DTYPE_F32, torch.bfloat16: _lib.KV_DTYPE_BF16}
 
@@ -265,5 +265,46 @@ def gqa_attention(q, cache: KVCache, n_new, out=None, workspace=None, parents=No
         st = lib.gqa_attention_tree(cache.handle, ctypes.c_void_p(q.data_ptr()), hq, T, arr,
                                     _lib.int32_array(flat), ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_len,
                                     _stream_ptr())
+    _lib.check(st, lib)
+    return out
+
+
+def append_attention(cache: KVCache, k_new, v_new, q, n_new, out=None, workspace=None):
+    """``cache.append(k_new, v_new, n_new)`` then ``gqa_attention(q, cache, n_new)``
+    in one library call (kv_append_attention): rows on the decode kernel are
+    appended by that kernel, so a decode step is one launch. Same bits as the
+    two calls."""
+    cache._check_tensor(k_new, "k_new", cache.kv_heads)
+    cache._check_tensor(v_new, "v_new", cache.kv_heads)
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new differ in shape")
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-d tensor [B, Hq, T, d]")
+    cache._check_tensor(q, "q", q.shape[1])
+    B, hq, T, d = q.shape
+    if k_new.shape[2] != T:
+        raise ValueError("k_new and q differ in T")
+    n = _row_counts(n_new, B)
+    arr = _lib.int32_array(n)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        cache._check_tensor(out, "out", hq)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    lib = cache._lib
+    size = ctypes.c_size_t()
+    _lib.check(lib.kv_append_attention_workspace_size(cache.handle, hq, T, arr, ctypes.byref(size)), lib)
+    need = int(size.value)
+    if workspace is None:
+        ws = cache._workspace(need)
+    else:
+        if workspace.device != cache.device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the cache's device")
+        ws = workspace
+    st = lib.kv_append_attention(cache.handle, ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
+                                 ctypes.c_void_p(q.data_ptr()), hq, T, arr, ctypes.c_void_p(out.data_ptr()),
+                                 ctypes.c_void_p(ws.data_ptr() if ws is not None else 0),
+                                 ws.numel() if ws is not None else 0, _stream_ptr())
     _lib.check(st, lib)
     return out

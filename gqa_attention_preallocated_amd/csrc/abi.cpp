@@ -115,7 +115,10 @@ constexpr int64_t kDecodeSlots = 256;
 // (8 waves, or 4 at one wave per SIMD; prefill_waves).
 constexpr int64_t kPrefillSlots = 256;
 
-void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new, Plan &p) {
+// `lens`: the row lengths the call sees (the host lengths, or those after a
+// fused append)
+void plan_attention(const kv_cache *c, const int32_t *lens, int32_t q_heads, int32_t T, const int32_t *n_new,
+                    Plan &p) {
     const int G = q_heads / c->kv_heads;
     p.group = G;
     std::vector<int> dec_rows, pre_rows;
@@ -149,7 +152,7 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
         int64_t total = 0;
         for (int b : dec_rows)
             for (int qt = 0; qt < ceil_div(n_new[b], tq); ++qt)
-                total += (int64_t)c->kv_heads * ceil_div(tile_span(c->lens[b], n_new[b], tq, qt, c->window),
+                total += (int64_t)c->kv_heads * ceil_div(tile_span(lens[b], n_new[b], tq, qt, c->window),
                                                          kDecodeKeyTile);
         // tiles per work group: the whole job spread over the slots, never
         // fewer than one tile per wave
@@ -157,7 +160,7 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
         for (int b : dec_rows) {
             RowPlan r{};
             r.b = b;
-            r.len = c->lens[b];
+            r.len = lens[b];
             r.nnew = n_new[b];
             r.nq = (int)ceil_div(r.nnew, tq);
             int64_t span = 0;                      // the longest query tile's key range
@@ -180,7 +183,7 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
         int64_t total = 0;
         for (int b : pre_rows)
             for (int qt = 0; qt < ceil_div(n_new[b], tq); ++qt)
-                total += (int64_t)c->kv_heads * ceil_div(tile_span(c->lens[b], n_new[b], tq, qt, c->window),
+                total += (int64_t)c->kv_heads * ceil_div(tile_span(lens[b], n_new[b], tq, qt, c->window),
                                                          kPrefillKeyTile);
         // a row is split only when its longest item would run well past the
         // per-slot share of the whole launch (the launch lasts as long as its
@@ -189,7 +192,7 @@ void plan_attention(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t
         for (int b : pre_rows) {
             RowPlan r{};
             r.b = b;
-            r.len = c->lens[b];
+            r.len = lens[b];
             r.nnew = n_new[b];
             r.nq = (int)ceil_div(r.nnew, tq);
             int64_t span = 0;
@@ -245,7 +248,8 @@ WsLayout ws_layout(const kv_cache *c, const Plan &p) {
 
 size_t workspace_bytes_for(const kv_cache *c, const Plan &p) { return ws_layout(c, p).total; }
 
-kv_status check_attention_args(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new) {
+kv_status check_attention_args(const kv_cache *c, const int32_t *lens, int32_t q_heads, int32_t T,
+                               const int32_t *n_new) {
     if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
     if (q_heads <= 0 || q_heads % c->kv_heads != 0)
         return fail(KV_ERR_INVALID_ARG, "q_heads %d is not a positive multiple of kv_heads %d", q_heads,
@@ -257,9 +261,9 @@ kv_status check_attention_args(const kv_cache *c, int32_t q_heads, int32_t T, co
     for (int b = 0; b < c->batch; ++b) {
         if (n_new[b] < 0 || n_new[b] > T)
             return fail(KV_ERR_INVALID_ARG, "row %d: n_new %d outside 0..%d", b, n_new[b], T);
-        if (n_new[b] > c->lens[b])
+        if (n_new[b] > lens[b])
             return fail(KV_ERR_INVALID_ARG, "row %d: n_new %d > length %d (append before attention)", b,
-                        n_new[b], c->lens[b]);
+                        n_new[b], lens[b]);
     }
     return KV_OK;
 }
@@ -317,6 +321,25 @@ kv_status push_table_updates(kv_cache *c, const std::vector<std::pair<int32_t, i
 
 kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
                          const int32_t *parents, void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+// An attention call's checks and plan, against `lens`, before anything is enqueued.
+kv_status attention_prepare(const kv_cache *c, const int32_t *lens, const void *q, int32_t q_heads, int32_t T,
+                            const int32_t *n_new, void *out, void *workspace, size_t workspace_bytes, Plan &p);
+// New tokens a decode kernel appends itself (kv_append_attention): read from
+// k_new / v_new [B, Hkv, T, d] and written to the cache by the kernel.
+struct Fused {
+    const void *k_new = nullptr, *v_new = nullptr;
+};
+kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_heads, int32_t T,
+                           const int32_t *n_new, const int32_t *parents, void *out, void *workspace,
+                           const Fused *fused, void *stream);
+// An append's checks (all rows, the pool), before anything is enqueued.
+kv_status append_check(const kv_cache *c, const void *k_new, const void *v_new, int32_t T, const int32_t *n_new,
+                       int64_t *pages_needed, bool check_pointers = true);
+// Enqueue an append that append_check accepted: pages, the copy kernel for
+// every row with skip[b] == 0 (all rows when skip is null), then the lengths.
+kv_status append_commit(kv_cache *c, const void *k_new, const void *v_new, int32_t T, const int32_t *n_new,
+                        int64_t pages_needed, const std::vector<char> *skip, void *stream);
 
 // Ring caches: the lowest position a row of this length still holds, and the
 // lowest key a query at position pos sees ([MASK] "A strong answer", reversal).
@@ -478,6 +501,102 @@ void kv_cache_destroy(kv_cache *c) {
 
 kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T, const int32_t *n_new,
                     void *stream) {
+    int64_t pages = 0;
+    kv_status s = append_check(c, k_new, v_new, T, n_new, &pages);
+    if (s != KV_OK) return s;
+    s = append_commit(c, k_new, v_new, T, n_new, pages, nullptr, stream);
+    return s == KV_OK ? ok() : s;
+}
+
+kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new,
+                                       size_t *bytes) {
+    if (bytes == nullptr) return fail(KV_ERR_INVALID_ARG, "bytes is null");
+    *bytes = 0;
+    kv_status s = check_attention_args(c, c == nullptr ? nullptr : c->lens.data(), q_heads, T, n_new);
+    if (s != KV_OK) return s;
+    if (c->batch == 0 || T == 0) return ok();
+    Plan p;
+    plan_attention(c, c->lens.data(), q_heads, T, n_new, p);
+    *bytes = workspace_bytes_for(c, p);
+    return ok();
+}
+
+kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
+                        void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    return attention_call(c, q, q_heads, T, n_new, nullptr, out, workspace, workspace_bytes, stream);
+}
+
+kv_status gqa_attention_tree(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
+                             const int32_t *parents, void *out, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    kv_status s = check_attention_args(c, c == nullptr ? nullptr : c->lens.data(), q_heads, T, n_new);
+    if (s != KV_OK) return s;
+    if (T > kMaxTreeNodes || (int64_t)(q_heads / c->kv_heads) * T > 64)
+        return fail(KV_ERR_UNSUPPORTED, "tree verify takes at most %d nodes and G * T <= 64", kMaxTreeNodes);
+    if (c->ring) return fail(KV_ERR_UNSUPPORTED, "tree verify runs on linear caches");
+    if (c->path_policy == 2) return fail(KV_ERR_UNSUPPORTED, "tree verify runs on the split-K decode kernel");
+    if (c->batch > 0 && T > 0 && parents == nullptr) return fail(KV_ERR_INVALID_ARG, "parents is null");
+    // [MASK] "What interviewers probe next": parent pointers; here every parent
+    // is -1 (the committed prefix) or an earlier node of the same row
+    for (int b = 0; b < c->batch; ++b)
+        for (int u = 0; u < n_new[b]; ++u) {
+            const int p = parents[(int64_t)b * T + u];
+            if (p < -1 || p >= u)
+                return fail(KV_ERR_INVALID_ARG, "row %d node %d: parent %d is not -1 or an earlier node", b, u, p);
+        }
+    return attention_call(c, q, q_heads, T, n_new, parents, out, workspace, workspace_bytes, stream);
+}
+
+kv_status kv_append_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new,
+                                             size_t *bytes) {
+    if (bytes == nullptr) return fail(KV_ERR_INVALID_ARG, "bytes is null");
+    *bytes = 0;
+    int64_t pages = 0;
+    kv_status s = append_check(c, nullptr, nullptr, T, n_new, &pages, false);
+    if (s != KV_OK) return s;
+    std::vector<int32_t> after(c->lens);
+    for (int b = 0; b < c->batch; ++b) after[b] += n_new[b];
+    s = check_attention_args(c, after.data(), q_heads, T, n_new);
+    if (s != KV_OK) return s;
+    if (c->batch == 0 || T == 0) return ok();
+    Plan p;
+    plan_attention(c, after.data(), q_heads, T, n_new, p);
+    *bytes = workspace_bytes_for(c, p);
+    return ok();
+}
+
+kv_status kv_append_attention(kv_cache *c, const void *k_new, const void *v_new, const void *q, int32_t q_heads,
+                              int32_t T, const int32_t *n_new, void *out, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    // every check of both halves first, against the lengths after the append
+    int64_t pages = 0;
+    kv_status s = append_check(c, k_new, v_new, T, n_new, &pages);
+    if (s != KV_OK) return s;
+    std::vector<int32_t> after(c->lens);
+    for (int b = 0; b < c->batch; ++b) after[b] += n_new[b];
+    Plan p;
+    s = attention_prepare(c, after.data(), q, q_heads, T, n_new, out, workspace, workspace_bytes, p);
+    if (s != KV_OK) return s;
+    // rows of the decode kernel append themselves (an E4M3 cache quantizes in
+    // the copy kernel, so its rows are all appended there)
+    const bool fuse = c->dtype != KV_DTYPE_FP8_E4M3 && !p.dec.empty();
+    std::vector<char> skip(c->batch, 0);
+    if (fuse)
+        for (const RowPlan &r : p.dec) skip[r.b] = 1;
+    s = append_commit(c, k_new, v_new, T, n_new, pages, &skip, stream);
+    if (s != KV_OK) return s;
+    Fused f;
+    f.k_new = k_new;
+    f.v_new = v_new;
+    s = attention_launch(c, p, q, q_heads, T, n_new, nullptr, out, workspace, fuse ? &f : nullptr, stream);
+    return s == KV_OK ? ok() : s;
+}
+
+}  // extern "C"
+
+namespace {
+kv_status append_check(const kv_cache *c, const void *k_new, const void *v_new, int32_t T, const int32_t *n_new,
+                       int64_t *pages_out, bool check_pointers) {
     if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
     if (T < 0) return fail(KV_ERR_INVALID_ARG, "T %d < 0", T);
     if (c->batch > 0 && n_new == nullptr) return fail(KV_ERR_INVALID_ARG, "n_new is null");
@@ -508,11 +627,17 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
             return fail(KV_ERR_CAPACITY, "%lld pages needed, %zu free in the pool", (long long)pages_needed,
                         c->free_pages.size());
     }
-    if (total > 0) {
+    if (total > 0 && check_pointers) {
         if (k_new == nullptr || v_new == nullptr) return fail(KV_ERR_INVALID_ARG, "k_new/v_new is null");
         if (!aligned16(k_new) || !aligned16(v_new))
             return fail(KV_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
     }
+    *pages_out = pages_needed;
+    return KV_OK;
+}
+
+kv_status append_commit(kv_cache *c, const void *k_new, const void *v_new, int32_t T, const int32_t *n_new,
+                        int64_t pages_needed, const std::vector<char> *skip, void *stream) {
     if (pages_needed > 0) {
         // row by row, each new block gets the lowest-numbered free page; the
         // device table learns the entries before the copy kernel reads them
@@ -530,7 +655,7 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
     }
     std::vector<int> rows;
     for (int b = 0; b < c->batch; ++b)
-        if (n_new[b] > 0) rows.push_back(b);
+        if (n_new[b] > 0 && (skip == nullptr || !(*skip)[b])) rows.push_back(b);
     const int64_t row_bytes = (int64_t)c->head_dim * c->io_bytes;      // of k_new / v_new
     for (size_t lo = 0; lo < rows.size(); lo += kMaxRows) {
         AppendArgs a{};
@@ -573,68 +698,40 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
     }
     // the length moves only after the write is enqueued ([GQA] "Common mistakes")
     for (int b = 0; b < c->batch; ++b) c->lens[b] += n_new[b];
-    return ok();
+    return KV_OK;
 }
 
-kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new,
-                                       size_t *bytes) {
-    if (bytes == nullptr) return fail(KV_ERR_INVALID_ARG, "bytes is null");
-    *bytes = 0;
-    kv_status s = check_attention_args(c, q_heads, T, n_new);
+kv_status attention_prepare(const kv_cache *c, const int32_t *lens, const void *q, int32_t q_heads, int32_t T,
+                            const int32_t *n_new, void *out, void *workspace, size_t workspace_bytes, Plan &p) {
+    kv_status s = check_attention_args(c, lens, q_heads, T, n_new);
     if (s != KV_OK) return s;
-    if (c->batch == 0 || T == 0) return ok();
-    Plan p;
-    plan_attention(c, q_heads, T, n_new, p);
-    *bytes = workspace_bytes_for(c, p);
-    return ok();
-}
-
-kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
-                        void *out, void *workspace, size_t workspace_bytes, void *stream) {
-    return attention_call(c, q, q_heads, T, n_new, nullptr, out, workspace, workspace_bytes, stream);
-}
-
-kv_status gqa_attention_tree(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
-                             const int32_t *parents, void *out, void *workspace, size_t workspace_bytes,
-                             void *stream) {
-    kv_status s = check_attention_args(c, q_heads, T, n_new);
-    if (s != KV_OK) return s;
-    if (T > kMaxTreeNodes || (int64_t)(q_heads / c->kv_heads) * T > 64)
-        return fail(KV_ERR_UNSUPPORTED, "tree verify takes at most %d nodes and G * T <= 64", kMaxTreeNodes);
-    if (c->ring) return fail(KV_ERR_UNSUPPORTED, "tree verify runs on linear caches");
-    if (c->path_policy == 2) return fail(KV_ERR_UNSUPPORTED, "tree verify runs on the split-K decode kernel");
-    if (c->batch > 0 && T > 0 && parents == nullptr) return fail(KV_ERR_INVALID_ARG, "parents is null");
-    // [MASK] "What interviewers probe next": parent pointers; here every parent
-    // is -1 (the committed prefix) or an earlier node of the same row
-    for (int b = 0; b < c->batch; ++b)
-        for (int u = 0; u < n_new[b]; ++u) {
-            const int p = parents[(int64_t)b * T + u];
-            if (p < -1 || p >= u)
-                return fail(KV_ERR_INVALID_ARG, "row %d node %d: parent %d is not -1 or an earlier node", b, u, p);
-        }
-    return attention_call(c, q, q_heads, T, n_new, parents, out, workspace, workspace_bytes, stream);
-}
-
-}  // extern "C"
-
-namespace {
-kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
-                         const int32_t *parents, void *out, void *workspace, size_t workspace_bytes,
-                         void *stream) {
-    kv_status s = check_attention_args(c, q_heads, T, n_new);
-    if (s != KV_OK) return s;
-    if (c->batch == 0 || T == 0) return ok();
+    if (c->batch == 0 || T == 0) return KV_OK;           // an empty plan: nothing to launch
     if (q == nullptr || out == nullptr) return fail(KV_ERR_INVALID_ARG, "q/out is null");
     if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
         return fail(KV_ERR_INVALID_ARG, "q/out/workspace must be 16-byte aligned");
-    Plan p;
-    plan_attention(c, q_heads, T, n_new, p);
+    plan_attention(c, lens, q_heads, T, n_new, p);
     const size_t need = workspace_bytes_for(c, p);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
     if (p.records > INT32_MAX / 2)
         return fail(KV_ERR_UNSUPPORTED, "too many split partials");
+    return KV_OK;
+}
 
+kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T, const int32_t *n_new,
+                         const int32_t *parents, void *out, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    Plan p;
+    kv_status s = attention_prepare(c, c->lens.data(), q, q_heads, T, n_new, out, workspace, workspace_bytes, p);
+    if (s != KV_OK) return s;
+    s = attention_launch(c, p, q, q_heads, T, n_new, parents, out, workspace, nullptr, stream);
+    return s == KV_OK ? ok() : s;
+}
+
+kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_heads, int32_t T,
+                           const int32_t *n_new, const int32_t *parents, void *out, void *workspace,
+                           const Fused *fused, void *stream) {
+    if (p.dec.empty() && p.pre.empty() && p.pad_rows.empty()) return KV_OK;
     hipStream_t st = (hipStream_t)stream;
     const WsLayout w = ws_layout(c, p);
     char *ws = (char *)workspace;
@@ -680,6 +777,12 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
 
     a.tree = parents != nullptr;
     a.cols = p.dec_cols;
+    if (fused != nullptr) {
+        a.fuse = 1;
+        a.k_new = fused->k_new;
+        a.v_new = fused->v_new;
+        a.lens_dev = c->lens_dev;
+    }
     for (size_t lo = 0; lo < p.dec.size(); lo += kMaxRows) {
         fill_attn_rows(p.dec, lo, std::min(p.dec.size(), lo + kMaxRows), c->kv_heads, a.rows);
         if (a.tree) {
@@ -713,6 +816,7 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
     }
     a.cols = prefill_cols(c->dtype, c->head_dim);
     a.tree = 0;
+    a.fuse = 0;                // prefill rows were appended by the copy kernel
     for (size_t lo = 0; lo < p.pre.size(); lo += kMaxRows) {
         fill_attn_rows(p.pre, lo, std::min(p.pre.size(), lo + kMaxRows), c->kv_heads, a.rows);
         hipError_t e = launch_prefill((int)c->dtype, c->head_dim, a, st);
@@ -760,7 +864,7 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
         hipError_t e = launch_combine((int)c->dtype, c->head_dim, m, st);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (combine kernel)");
     }
-    return ok();
+    return KV_OK;
 }
 }  // namespace
 

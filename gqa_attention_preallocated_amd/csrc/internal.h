@@ -93,6 +93,13 @@ struct AttnArgs {
     const int32_t *table;      // paged cache: block table [B, max_blocks] (null: linear or ring)
     int32_t page_shift;        // log2(page size)
     int32_t max_blocks;
+    // kv_append_attention on decode-kernel rows: the kernel writes each row's
+    // new tokens from k_new / v_new ([B, Hkv, T, d]) into the cache and reads
+    // those keys from k_new / v_new; one work group per row sets lens_dev
+    int32_t fuse;
+    const void *k_new;
+    const void *v_new;
+    int32_t *lens_dev;         // optional
     int32_t tree;              // 1: the new tokens of each row form a tree (parent below)
     int8_t parent[kMaxRows][kMaxTreeNodes];   // per launch row: parent node of node u, -1 = the committed prefix
     AttnRows rows;

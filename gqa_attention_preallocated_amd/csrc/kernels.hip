@@ -385,6 +385,19 @@ template <> struct KeyRows<true> {
     }
 };
 
+// Cache row (in units of one K or V row) of key position p of (row b, kv head
+// h), for the few keys a fused append writes: linear and ring caches use slot
+// p mod max_len, paged caches the block table.
+template <bool PG>
+__device__ inline int64_t cache_row(const AttnArgs &a, int b, int h, int p) {
+    if constexpr (PG) {
+        const int page = a.table[(int64_t)b * a.max_blocks + (p >> a.page_shift)];
+        return (((int64_t)page * a.hkv + h) << a.page_shift) + (p & ((1 << a.page_shift) - 1));
+    } else {
+        return ((int64_t)b * a.hkv + h) * a.max_len + p % a.max_len;
+    }
+}
+
 // One online-softmax step for the 8 scores a lane holds for its column
 // (two 16-key blocks: s0 = keys 4g..4g+3, s1 = keys 16+4g..16+4g+3 of a
 // 32-key chunk, g = lane/16). Scores arrive unscaled; `pos` is the column's
@@ -522,6 +535,29 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k);
     const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v);
     KeyRows<PG> km(a, it, w_begin);
+    if constexpr (!F8) {
+        if (a.fuse) {
+            // kv_append_attention: the new tokens in this item's key range go
+            // into the cache here, 16 bytes per thread per step. Items of one
+            // row that hold the same token write the same bytes, and every new
+            // token lies in some item's range. The attention below reads these
+            // keys from k_new / v_new, so nothing waits for the writes.
+            const int lo = it.k_begin > it.base ? it.k_begin : it.base, n_tok = it.k_end - lo;
+            const int64_t knew_row0 = ((int64_t)it.b * a.hkv + it.kvh) * a.T + (lo - it.base);
+            for (int task = tid; task < 2 * n_tok * CPK; task += 64 * W) {
+                const int tv = task / (n_tok * CPK), rem = task % (n_tok * CPK);
+                const int tok = rem / CPK, part = rem % CPK;
+                const int64_t src = (knew_row0 + tok) * CROWB + part * 16;
+                const int64_t dst = cache_row<PG>(a, it.b, it.kvh, lo + tok) * CROWB + part * 16;
+                const unsigned char *sb = reinterpret_cast<const unsigned char *>(tv ? a.v_new : a.k_new);
+                unsigned char *db = reinterpret_cast<unsigned char *>(const_cast<void *>(tv ? a.v : a.k));
+                *reinterpret_cast<uint4 *>(db + dst) = *reinterpret_cast<const uint4 *>(sb + src);
+            }
+            // the first item of a row sets the row's device length
+            if (a.lens_dev != nullptr && tid == 0 && blockIdx.x == a.rows.item0[it.r])
+                a.lens_dev[it.b] = a.rows.len[it.r];
+        }
+    }
     // an E4M3 cache stands for code x scale of the head: the K scale joins the
     // score scale, the V scale multiplies the output
     const float score_c = F8 ? a.scale_log2 * a.k_scale[it.kvh] : a.scale_log2;
@@ -548,10 +584,31 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     // a tile's keys are consecutive cache rows from km.row(tile): no tile
     // wraps (ring capacities are multiples of kRingAlign, pages of kMinPage,
     // and tiles start at multiples of KT)
-    auto load_tile = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
+    // kv_append_attention (never for E4M3 caches): keys at or past the row's
+    // first new position come from k_new / v_new [B, Hkv, T, d] (FRESH tiles)
+    const unsigned char *knew = nullptr, *vnew = nullptr;
+    if constexpr (!F8) {
+        if (a.fuse) {
+            const int64_t r0 = ((int64_t)it.b * a.hkv + it.kvh) * a.T;
+            knew = reinterpret_cast<const unsigned char *>(a.k_new) + r0 * CROWB;
+            vnew = reinterpret_cast<const unsigned char *>(a.v_new) + r0 * CROWB;
+        }
+    }
+    auto load_tile_as = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile, auto fresh) {
+        constexpr bool FRESH = decltype(fresh)::value;
         const int64_t row0 = km.row(tile);
         const unsigned char *kt = kbase + row0 * CROWB;
         const unsigned char *vt = vbase + row0 * CROWB;
+        auto krow = [&](int key) -> const unsigned char * {
+            if constexpr (FRESH)
+                if (tile + key >= it.base) return knew + (int64_t)(tile + key - it.base) * CROWB;
+            return kt + key * CROWB;
+        };
+        auto vrow = [&](int key) -> const unsigned char * {
+            if constexpr (FRESH)
+                if (tile + key >= it.base) return vnew + (int64_t)(tile + key - it.base) * CROWB;
+            return vt + key * CROWB;
+        };
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int key = ks * 16 + lr;
@@ -559,8 +616,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
             if constexpr (KPAIR) {
 #pragma unroll
                 for (int j = 0; j < KC / 2; ++j) {
-                    const uint4 w = ok ? load_stream(kt + key * CROWB + dmap(2 * j))
-                                       : make_uint4(0, 0, 0, 0);
+                    const uint4 w = ok ? load_stream(krow(key) + dmap(2 * j)) : make_uint4(0, 0, 0, 0);
                     kop[ks][2 * j] = make_uint2(w.x, w.y);
                     kop[ks][2 * j + 1] = make_uint2(w.z, w.w);
                 }
@@ -568,8 +624,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
                     const int d0 = dmap(kc);
-                    kop[ks][kc] = (ok && d0 < D) ? S::load_k(kt + key * CROWB + d0 * S::kBytes)
-                                                 : S::zero_k();
+                    kop[ks][kc] = (ok && d0 < D) ? S::load_k(krow(key) + d0 * S::kBytes) : S::zero_k();
                 }
             }
         }
@@ -578,8 +633,17 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
             const int c = lane + 64 * i;
             const int key = c / CPK, part = c % CPK;
             const bool ok = (c < KT * CPK) && (tile + key < w_end);
-            vreg[i] = ok ? load_stream(vt + key * CROWB + part * 16) : make_uint4(0, 0, 0, 0);
+            vreg[i] = ok ? load_stream(vrow(key) + part * 16) : make_uint4(0, 0, 0, 0);
         }
+    };
+    auto load_tile = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
+        if constexpr (!F8) {
+            if (a.fuse && tile + KT > it.base) {           // uniform over the wave
+                load_tile_as(kop, vreg, tile, std::true_type{});
+                return;
+            }
+        }
+        load_tile_as(kop, vreg, tile, std::false_type{});
     };
 
     // tree verify ([MASK] "What interviewers probe next"): the new tokens of

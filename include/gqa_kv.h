@@ -266,6 +266,34 @@ kv_status gqa_attention_tree(kv_cache *c, const void *q, int32_t q_heads, int32_
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Append and attention in one call: exactly kv_append(c, k_new, v_new, T,
+ * n_new) followed by gqa_attention(c, q, q_heads, T, n_new, out, ...), the
+ * cache bytes, lengths and outputs bit for bit the same. [GQA] "A strong
+ * answer" (each step writes the new tokens at the row's length, then attends
+ * over the cache) and [CH16] "Layout and validity" (append, then attend).
+ * Every check of both halves runs before anything is enqueued, with the
+ * lengths the append will leave; any error other than KV_ERR_DEVICE changes
+ * nothing. Rows that run on the split-K decode kernel are appended by that
+ * kernel, which reads those keys from k_new / v_new, so one launch does the
+ * append and the attention of a decode step; other rows, and every row of an
+ * E4M3 cache, are appended by the copy kernel first.
+ *   k_new, v_new  device [B, Hkv, T, d]; q, out device [B, q_heads, T, d]
+ *   n_new         HOST int32[B]
+ *   workspace     as gqa_attention, of at least
+ *                 kv_append_attention_workspace_size() bytes.
+ */
+kv_status kv_append_attention(kv_cache *c, const void *k_new, const void *v_new, const void *q,
+                              int32_t q_heads, int32_t T, const int32_t *n_new, void *out,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace kv_append_attention needs for these arguments (the
+ * gqa_attention workspace for the lengths after the append), in bytes.
+ */
+kv_status kv_append_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32_t T,
+                                             const int32_t *n_new, size_t *bytes);
+
+/*
  * Roll back: set lens[b] = new_lens[b] for every row, copying and clearing
  * nothing. [CH16] "Layout and validity" (truncate for speculative rollback;
  * stale slots stay and are never read). new_lens is a HOST int32[B] with

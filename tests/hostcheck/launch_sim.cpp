@@ -5,7 +5,9 @@
 // column, using the same indexing functions the kernels use (indexing.h), and
 // checks on the CPU that
 //   * every K/V/q/out/workspace/lens access lies inside a registered buffer,
-//   * append writes only the slots [lens, lens + n_new) of each row, once,
+//   * append writes only the slots [lens, lens + n_new) of each row, once
+//     (the copy kernel, or the decode kernel of kv_append_attention, whose
+//     items may write one token more than once within a launch),
 //   * each attention call writes every output row (b, h, t) exactly once,
 //   * each split partial is written once before the combine kernel reads it.
 // Buffers are fake addresses registered by the test; nothing is dereferenced.
@@ -16,6 +18,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <set>
 #include <string>
 #include <vector>
 
@@ -216,6 +219,17 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
         if (R.lsplit[r] % key_tile != 0 || R.nsplit[r] <= 0) err("attention: bad split");
     }
     const bool paged = a.table != nullptr;
+    // kv_append_attention: the kernel writes its key range's new tokens and
+    // reads keys at or past the row's first new position from k_new / v_new
+    const bool fuse = a.fuse != 0;
+    if (fuse && (cache_elem != elem || key_tile != kDecodeKeyTile || a.k_new == nullptr || a.v_new == nullptr))
+        err("attention: fused append outside the decode kernel of a float32 / bfloat16 cache");
+    std::set<uintptr_t> fused_chunks;    // 16-byte chunks of K written by this launch
+    auto new_row = [&](const Item &it, int r, int key) -> int64_t {   // k_new row of key `key`
+        const int t = key - it.base;
+        if (t < 0 || t >= R.nnew[r] || t >= a.T) err("attention: k_new row outside the row's new tokens");
+        return ((int64_t)it.b * a.hkv + it.kvh) * a.T + t;
+    };
     if (paged) {
         // no page is held by two blocks, and every block below a row's length has one
         std::map<int32_t, int> owners;
@@ -247,6 +261,29 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
         // every visible key is still held by the ring (positions >= len - max_len)
         if (windowed && lo_visible < std::max(0, R.len[r] - a.max_len)) err("attention: window key evicted");
         const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
+        if (fuse) {
+            for (int p = std::max(it.k_begin, it.base); p < it.k_end; ++p) {
+                const int64_t src = new_row(it, r, p) * cache_row;
+                int64_t dst = head * a.max_len + p % a.max_len;
+                if (paged) {
+                    const int64_t ti = (int64_t)it.b * a.max_blocks + (p >> a.page_shift);
+                    access(a.table + ti, 4, "table", "fused append block table");
+                    const int page = ti < (int64_t)g_table.size() ? g_table[ti] : -1;
+                    if (page < 0) err("fused append: block without a page");
+                    dst = (((int64_t)page * a.hkv + it.kvh) << a.page_shift) + (p & ((1 << a.page_shift) - 1));
+                }
+                access((const char *)a.k_new + src, cache_row, "k_new", "fused append read k_new");
+                access((const char *)a.v_new + src, cache_row, "v_new", "fused append read v_new");
+                access((const char *)a.k + dst * cache_row, cache_row, "k", "fused append write K");
+                access((const char *)a.v + dst * cache_row, cache_row, "v", "fused append write V");
+                for (int64_t o = 0; o < cache_row; o += 16) fused_chunks.insert((uintptr_t)a.k + dst * cache_row + o);
+            }
+            if (a.lens_dev != nullptr && item == R.item0[r]) {
+                access(a.lens_dev + it.b, 4, "lens", "fused append lens_dev");
+                if ((int)g_lens_dev.size() <= it.b) g_lens_dev.resize(it.b + 1, 0);
+                g_lens_dev[it.b] = R.len[r];
+            }
+        }
         // keys read: [k_begin, k_end) tile by tile; key j from slot j mod max_len,
         // and no tile may wrap inside the ring
         for (int t0 = it.k_begin; t0 < it.k_end; t0 += key_tile) {
@@ -267,6 +304,14 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
                 access((const char *)a.k + key * cache_row, cache_row, "k", "attention K");
                 access((const char *)a.v + key * cache_row, cache_row, "v", "attention V");
             }
+            // a tile holding new keys reads them from k_new / v_new
+            if (fuse && t0 + key_tile > it.base)
+                for (int key : {std::max(t0, it.base), t0 + n - 1}) {
+                    if (key < it.base) continue;
+                    const int64_t src = new_row(it, r, key) * cache_row;
+                    access((const char *)a.k_new + src, cache_row, "k_new", "fused attention k_new");
+                    access((const char *)a.v_new + src, cache_row, "v_new", "fused attention v_new");
+                }
         }
         for (int col = 0; col < cols; ++col) {
             const int pos = column_position(it, col, a.group, cols);
@@ -289,6 +334,7 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
             }
         }
     }
+    for (uintptr_t c : fused_chunks) g_appended[c]++;
 }
 
 hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t) {
@@ -304,6 +350,7 @@ hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, h
 hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_t) {
     if (head_dim != a.head_dim) err("prefill: head_dim mismatch");
     if (a.cols != prefill_cols(dtype, head_dim)) err("prefill: columns differ from the kernel's");
+    if (a.fuse) err("prefill: fused append requested");
     sim_attention(a, a.cols, kPrefillKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
     return hipSuccess;
 }

@@ -45,6 +45,8 @@ def sim(tmp_path_factory):
     lib.gqa_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]
     lib.gqa_attention.argtypes = [P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
     lib.gqa_attention_tree.argtypes = [P, P, I32, I32, I32P, I32P, P, P, ctypes.c_size_t, P]
+    lib.kv_append_attention.argtypes = [P, P, P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
+    lib.kv_append_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]
     lib.kv_truncate.argtypes = [P, I32P, P]
     lib.kv_cache_set_policy.argtypes = [P, I32, I32]
     lib.kv_cache_destroy.argtypes = [P]
@@ -131,6 +133,27 @@ class SimCache:
                                     ctypes.c_void_p(self.addr["out"]), ctypes.c_void_p(self.addr["ws"]),
                                     size.value, None)
         assert st == 0, self.lib.kv_last_error()
+        return size.value
+
+    def append_attention(self, T, n_new):
+        """kv_append_attention; returns its workspace size, which must equal
+        gqa_attention's for the lengths after the append."""
+        size = ctypes.c_size_t()
+        assert self.lib.kv_append_attention_workspace_size(self.h, self.hq, T, _i32(n_new), ctypes.byref(size)) == 0
+        assert size.value < (1 << 34)
+        self.lib.hostcheck_begin_call()
+        a = self.addr
+        st = self.lib.kv_append_attention(self.h, ctypes.c_void_p(a["k_new"]), ctypes.c_void_p(a["v_new"]),
+                                          ctypes.c_void_p(a["q"]), self.hq, T, _i32(n_new), ctypes.c_void_p(a["out"]),
+                                          ctypes.c_void_p(a["ws"]), size.value, None)
+        assert st == 0, self.lib.kv_last_error()
+        self.lens += np.asarray(n_new)
+        self.appended += int(np.sum(n_new)) * self.hk * self.d * self.elem // 16
+        if (self.lens > self.max_len).any():
+            self.rewrote = True
+        after = ctypes.c_size_t()
+        assert self.lib.gqa_attention_workspace_size(self.h, self.hq, T, _i32(n_new), ctypes.byref(after)) == 0
+        assert after.value == size.value
         return size.value
 
     def block_table(self):
@@ -460,3 +483,59 @@ def test_paged_llama_ragged(sim):
     c.attention(int(max(n_new)), n_new)
     c.check(int(max(n_new)))
     assert pages * P < 0.6 * sh.batch * sh.max_len
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_append_attention_trials(sim, seed):
+    """kv_append_attention: every new token written once (by the copy kernel or
+    by the decode kernel's items, never both), every k_new read inside the
+    row's new tokens, lens_dev and every output row set, under each policy and
+    cache kind."""
+    shape, calls = W.trial_spec(seed, head_dims=(16, 32, 64, 128))
+    kind = ["f32", "bf16", "ring", "paged", "fp8", "bf16"][seed % 6]
+    for policy in [(0, 0), (1, 32), (2, 64)]:
+        t_max = max([c["T"] for c in calls] + [1])
+        hq = shape.kv_heads * shape.group
+        if kind == "paged":
+            P = 64
+            max_len = -(-shape.max_len // P) * P
+            pages = shape.batch * (max_len // P)
+            c = SimCache(sim, shape.batch, shape.kv_heads, max_len, shape.head_dim, "bf16", hq, t_max,
+                         paged=(P, pages))
+        elif kind == "ring":
+            c = SimCache(sim, shape.batch, shape.kv_heads, 64, shape.head_dim, "bf16", hq, t_max,
+                         window=64 - t_max + 1)
+        else:
+            c = SimCache(sim, shape.batch, shape.kv_heads, shape.max_len, shape.head_dim, kind, hq, t_max)
+        sim.kv_cache_set_policy(c.h, policy[0], policy[1])
+        for call in calls:
+            c.append_attention(call["T"], call["n_new"])
+            c.check(call["T"])
+
+
+def test_append_attention_llama_decode_and_ragged(sim):
+    """Llama-3.1-8B shapes: a decode step over 32 rows of 8191 keys, and a
+    mixed batch (decode, verify and prefill rows) in one call, on linear and
+    paged caches."""
+    for paged in (None, (256, 32 * 34)):
+        c = SimCache(sim, 32, 8, 8704, 128, "bf16", 32, 4096, paged=paged)
+        for call in _prefix_calls([8191] * 32):
+            c.append(call["T"], call["n_new"])
+        c.append_attention(1, [1] * 32)
+        c.check(1)
+        n = [1, 4, 512, 0] * 8
+        c.append_attention(512, n)
+        c.check(512)
+
+
+@pytest.mark.parametrize("d,C,win", [(64, 128, 50), (128, 192, 64)])
+def test_append_attention_ring_wraps(sim, d, C, win):
+    """kv_append_attention on a sliding-window ring over many wraps."""
+    calls, lens = W.ring_schedule(d * 1000 + C + win + 1, 3, C, win, 200, min(40, C - win + 1))
+    assert lens.max() > C + 8
+    for policy in [(0, 0), (1, 32)]:
+        c = SimCache(sim, 3, 2, C, d, "bf16", 8, max(x["T"] for x in calls), window=win)
+        sim.kv_cache_set_policy(c.h, *policy)
+        for call in calls:
+            c.append_attention(call["T"], call["n_new"])
+            c.check(call["T"])
