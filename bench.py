@@ -283,6 +283,49 @@ def run_verify(torch, reps=30):
             "config": {"workload": sh.name, "batch": B, "T": 4, "keys": 4096}}
 
 
+def run_shard(torch, reps=40):
+    """One GPU's share of the decode step when tp GPUs split the heads (tp = 1,
+    2, 4, 8: Hkv = 8/tp and Hq = 32/tp, all 32 rows, 4,096 cached keys + 1):
+    kv_append_attention then a host-only rollback, over 2*tp caches in turn so
+    that each step reads 1/(2 tp) of 1.07 GB of K/V that the step before did
+    not touch."""
+    from gqa_attention_preallocated_amd import KVCache, append_attention
+    import workloads as W
+    shards = []
+    for tp in (1, 2, 4, 8):
+        sh = W.llama8b_decode_shard(tp)
+        B, hq, hkv, d = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim
+        nc = 2 * tp
+        caches = [KVCache(B, hkv, sh.max_len, d, device_lens=False) for _ in range(nc)]
+        for i, c in enumerate(caches):
+            _fill_gpu_random(torch, c, [4096] * B, 40 + i)
+        n = [1] * B
+        g = torch.Generator(device="cuda").manual_seed(13)
+        q = (torch.randn(B, hq, 1, d, device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+        kn = (torch.randn(B, hkv, 1, d, device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+        vn = (torch.randn(B, hkv, 1, d, device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        caches[0].append(kn, vn, n)
+        ws_bytes = caches[0].workspace_bytes(hq, 1, n)
+        caches[0].truncate([4096] * B)
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            c = caches[i % nc]
+            append_attention(c, kn, vn, q, n, out=out, workspace=ws)
+            c.truncate([4096] * B)
+
+        t = _time_calls(torch, step, reps)
+        nbytes = attention_bytes([4097] * B, n, hq, hkv, d, 1) + 2 * B * hkv * d * 2
+        shards.append({"tp": tp, "kv_heads": hkv, "q_heads": hq, "items": B * hkv, "ms": round(t * 1e3, 5),
+                       "bytes": nbytes, "GB/s": round(nbytes / t / 1e9, 2), "frac_of_8TBs": round(nbytes / t / 8e12, 4)})
+        del caches, ws
+        torch.cuda.empty_cache()
+    return {"metric": "decode step per GPU under head sharding, HBM GB/s", "value": shards[-1]["GB/s"], "unit": "GB/s",
+            "shards": shards,
+            "config": {"workload": "llama8b_decode_b32_s4096_tp{1,2,4,8}", "batch": 32, "keys": 4097, "T": 1}}
+
+
 def run_window(torch, reps=30):
     """Sliding-window decode: B=32 rows, a 4,096-key window over an 8,192-slot ring
     after 20,000 tokens (the ring has wrapped twice), T=1. Two caches in turn."""
@@ -595,7 +638,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "window", "fp8", "tree",
-                                       "paged", "probe", "cpu"],
+                                       "paged", "shard", "probe", "cpu"],
                     default=None,
                     help="time one workload only (for profiling); prints its own JSON line")
     ap.add_argument("--copy-probe", action="store_true",
@@ -629,9 +672,9 @@ def main():
     if args.only == "ragged":
         print(json.dumps({"ragged": [run_ragged(torch, seed) for seed in (4, 5, 6)]}), flush=True)
         return
-    if args.only in ("prefill", "verify", "append", "window", "fp8", "tree", "paged", "probe"):
+    if args.only in ("prefill", "verify", "append", "window", "fp8", "tree", "paged", "shard", "probe"):
         fn = {"prefill": run_prefill, "verify": run_verify, "append": run_append, "window": run_window,
-              "fp8": run_fp8, "tree": run_tree, "paged": run_paged, "probe": run_probe}[args.only]
+              "fp8": run_fp8, "tree": run_tree, "paged": run_paged, "shard": run_shard, "probe": run_probe}[args.only]
         print(json.dumps({args.only: fn(torch)}), flush=True)
         return
     res = run_decode(torch, args.steps, args.warmup)

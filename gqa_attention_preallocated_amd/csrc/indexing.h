@@ -18,14 +18,15 @@ namespace gqakv {
 
 GQAKV_HD inline int imin(int a, int b) { return a < b ? a : b; }
 
-// Largest r in [0, n_rows) with item0[r] <= item (item0 is nondecreasing).
+// Largest r in [0, n_rows) with item0[r] <= item (item0 is nondecreasing
+// from item0[0] = 0): the number of rows r >= 1 whose first item is <= item.
+// The kernels take the same count with one ballot over a wave whose lane l
+// holds item0[l] (all lanes load at once, so a block finds its row after one
+// round of loads); here it is a loop.
 GQAKV_HD inline int find_row(const int32_t *item0, int n_rows, int item) {
-    int lo = 0, hi = n_rows - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (item0[mid] <= item) lo = mid; else hi = mid - 1;
-    }
-    return lo;
+    int r = 0;
+    for (int i = 1; i < n_rows; ++i) r += item0[i] <= item;
+    return r;
 }
 
 // One work item of an attention launch (see AttnRows for the numbering).
@@ -45,32 +46,45 @@ GQAKV_HD inline int range_start(int first_pos, int window) {
     return lo <= 0 ? 0 : lo - lo % kRingAlign;
 }
 
-GQAKV_HD inline Item decode_item(const AttnRows &R, int item, int hkv, int group, int cols, int window) {
+// The row table entries of one row.
+struct RowFields {
+    int item0, nnew, nsplit, b, len, lsplit, pbase;
+};
+
+GQAKV_HD inline RowFields row_fields(const AttnRows &R, int r) {
+    return RowFields{R.item0[r], R.nnew[r], R.nsplit[r], R.b[r], R.len[r], R.lsplit[r], R.pbase[r]};
+}
+
+// Item `item` of row r, whose table entries are f.
+GQAKV_HD inline Item decode_item_at(const RowFields &f, int r, int item, int hkv, int group, int cols, int window) {
     Item it;
-    const int r = find_row(R.item0, R.n_rows, item);
     it.r = r;
-    const int n = R.nnew[r];
+    const int n = f.nnew;
     const int tq = cols / group;                  // queries per tile
     it.nq = (n + tq - 1) / tq;
-    it.nsplit = R.nsplit[r];
-    const int local = item - R.item0[r];
+    it.nsplit = f.nsplit;
+    const int local = item - f.item0;
     it.kvh = local % hkv;
     const int rest = local / hkv;
     it.split = rest % it.nsplit;
     it.qtile = it.nq - 1 - rest / it.nsplit;      // longest key range first
-    it.b = R.b[r];
-    it.base = R.len[r] - n;
+    it.b = f.b;
+    it.base = f.len - n;
     it.t0 = it.qtile * tq;
     it.t_end = imin(it.t0 + tq, n);
     // bottom-right rule: the tile's last query sits at base + t_end - 1 and sees
     // keys up to that position, never past the row's length; with a window the
     // tile's first query sees nothing below base + t0 - window + 1
     const int keys_hi = it.base + it.t_end;
-    it.k_begin = range_start(it.base + it.t0, window) + it.split * R.lsplit[r];
-    it.k_end = imin(it.k_begin + R.lsplit[r], keys_hi);
-    it.rec0 = R.pbase[r] < 0 ? -1
-            : R.pbase[r] + ((it.kvh * it.nq + it.qtile) * it.nsplit + it.split) * cols;
+    it.k_begin = range_start(it.base + it.t0, window) + it.split * f.lsplit;
+    it.k_end = imin(it.k_begin + f.lsplit, keys_hi);
+    it.rec0 = f.pbase < 0 ? -1 : f.pbase + ((it.kvh * it.nq + it.qtile) * it.nsplit + it.split) * cols;
     return it;
+}
+
+GQAKV_HD inline Item decode_item(const AttnRows &R, int item, int hkv, int group, int cols, int window) {
+    const int r = find_row(R.item0, R.n_rows, item);
+    return decode_item_at(row_fields(R, r), r, item, hkv, group, cols, window);
 }
 
 // Absolute position of the query in column `col` of the item, or -1 for a

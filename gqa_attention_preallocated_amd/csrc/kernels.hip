@@ -264,14 +264,92 @@ __device__ inline uint2 quant8(const uint4 &x, float inv) {
     return make_uint2(quant4(x.x, x.y, inv), quant4(x.z, x.w, inv));
 }
 
+// ---------------------------------------------------------------------------
+// Row lookup from the launch tables in the kernel arguments. Lane l of a wave
+// loads entry l of each table (at most kMaxRows rows: one wave holds them
+// all), so every entry arrives after one round of loads; the block's row is
+// the ballot count of find_row, and its entries are read from that row's lane.
+// (A search over the table would chain one dependent load per step before a
+// block could issue its first memory access.)
+// ---------------------------------------------------------------------------
+__device__ inline int lane_entry(const int32_t *table, int n, int pad) {
+    const int l = threadIdx.x & 63;
+    return l < n ? table[l] : pad;
+}
+
+// find_row over `first` (nondecreasing, first[0] = 0) with one ballot
+__device__ inline int wave_find_row(int first_mine, int idx) {
+    const int l = threadIdx.x & 63;
+    return (int)__builtin_popcountll(__ballot(l >= 1 && first_mine <= idx));
+}
+
+__device__ inline int row_entry(int mine, int r) { return __builtin_amdgcn_readlane(mine, r); }
+
+__device__ inline Item decode_item_wave(const AttnRows &R, int item, int hkv, int group, int cols, int window) {
+    const int n = R.n_rows;
+    const int i0 = lane_entry(R.item0, n, 0x7fffffff);
+    const int nn = lane_entry(R.nnew, n, 0), ns = lane_entry(R.nsplit, n, 1), bb = lane_entry(R.b, n, 0);
+    const int ln = lane_entry(R.len, n, 0), ls = lane_entry(R.lsplit, n, 0), pb = lane_entry(R.pbase, n, -1);
+    const int r = wave_find_row(i0, item);
+    const RowFields f{row_entry(i0, r), row_entry(nn, r), row_entry(ns, r), row_entry(bb, r),
+                      row_entry(ln, r), row_entry(ls, r), row_entry(pb, r)};
+    return decode_item_at(f, r, item, hkv, group, cols, window);
+}
+
+// Split partials: the nsplit partial records rec, rec + stride, ... of one
+// column hold unnormalised sums acc and (running max m in log2 units, sum l).
+// Their outputs d..d+3 are merged by log-sum-exp in split order, eight splits
+// per batch of loads, and normalised (0 when no split saw a key).
+template <int D>
+__device__ inline f32x4 merge_partials(const float *ws_acc, const float *ws_ml, int64_t rec, int64_t stride,
+                                       int nsplit, int d) {
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        float2 ml[8];
+        float4 x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t rs = rec + (int64_t)(s0 + j) * stride;
+            if (s0 + j < nsplit) {
+                ml[j] = *reinterpret_cast<const float2 *>(ws_ml + rs * 2);
+                x[j] = *reinterpret_cast<const float4 *>(ws_acc + rs * D + d);
+            } else {
+                ml[j] = make_float2(-INFINITY, 0.f);
+                x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        float bm = M;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bm = fmaxf(bm, ml[j].x);
+        if (bm == -INFINITY) continue;            // no split so far saw a key of this column
+        const float c = fast_exp2(M - bm);        // M = -inf: c = 0 (acc and L are still 0)
+        acc *= c;
+        L *= c;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float w = fast_exp2(ml[j].x - bm);   // a split that saw no key: w = 0
+            acc[0] += w * x[j].x; acc[1] += w * x[j].y; acc[2] += w * x[j].z; acc[3] += w * x[j].w;
+            L += w * ml[j].y;
+        }
+        M = bm;
+    }
+    return acc * (L > 0.f ? 1.f / L : 0.f);
+}
+
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-    const int r = find_row(a.t.block0, a.t.n_rows, blockIdx.x);
-    const int local = blockIdx.x - a.t.block0[r];
-    const int nch = a.t.nchunk[r];
+    const int nrow = a.t.n_rows;
+    const int first = lane_entry(a.t.block0, nrow, 0x7fffffff);
+    const int r = wave_find_row(first, blockIdx.x);
+    const int local = blockIdx.x - row_entry(first, r);
+    const int nch = row_entry(lane_entry(a.t.nchunk, nrow, 1), r);
     const int kvh = local / nch;
     const int chunk = local % nch;
-    const int b = a.t.b[r];
-    const int64_t span = (int64_t)a.t.n[r] * a.row_bytes;
+    const int b = row_entry(lane_entry(a.t.b, nrow, 0), r);
+    const int start = row_entry(lane_entry(a.t.start, nrow, 0), r);
+    const int slot0 = row_entry(lane_entry(a.t.slot0, nrow, 0), r);
+    const int ntok = row_entry(lane_entry(a.t.n, nrow, 0), r);
+    const int64_t span = (int64_t)ntok * a.row_bytes;
     const int64_t off = (int64_t)chunk * kAppendChunk + threadIdx.x * 16;
     const int64_t head = (int64_t)b * a.hkv + kvh;
     if (off < span) {
@@ -280,14 +358,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         const int tok = (int)(off >> a.row_shift);
         int64_t crow;                             // cache row of the token
         if (a.table == nullptr) {
-            int slot = a.t.slot0[r] + tok;
+            int slot = slot0 + tok;
             if (slot >= a.max_len) slot -= a.max_len;
             crow = head * a.max_len + slot;
         } else {
             // paged: position p sits in row p mod page of (page, kv head) in the
             // pool, page = block_table[b][p / page] ([GQA] reversal); the table
             // entries were set earlier on the stream
-            const int p = a.t.start[r] + tok;
+            const int p = start + tok;
             const int page = a.table[(int64_t)b * a.max_blocks + (p >> a.page_shift)];
             crow = (((int64_t)page * a.hkv + kvh) << a.page_shift) + (p & ((1 << a.page_shift) - 1));
         }
@@ -308,7 +386,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         }
     }
     // the row's new length becomes visible to later kernels in stream order
-    if (a.lens_dev != nullptr && local == 0 && threadIdx.x == 0) a.lens_dev[b] = a.t.start[r] + a.t.n[r];
+    if (a.lens_dev != nullptr && local == 0 && threadIdx.x == 0) a.lens_dev[b] = start + ntok;
 }
 
 __global__ __launch_bounds__(64) void set_lens_kernel(int32_t *lens_dev, LensTable t) {
@@ -501,7 +579,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     const int wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     unsigned char *lds = lds_all + wave * STAGE;
-    const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, a.cols, a.window);
+    const Item it = decode_item_wave(a.rows, blockIdx.x, a.hkv, a.group, a.cols, a.window);
 
     // this wave's share of the item's keys: every W-th 32-key tile from its
     // own, so at any time the work group streams one contiguous run of K and
@@ -831,7 +909,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
-    const Item it = decode_item(a.rows, blockIdx.x, a.hkv, a.group, C, a.window);
+    const Item it = decode_item_wave(a.rows, blockIdx.x, a.hkv, a.group, C, a.window);
 
     int pos[NS];
     vec qop[NS][KC];
@@ -1230,16 +1308,21 @@ template <typename E, int D>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     using O = Op<E>;
     constexpr int DC = D / 4;
-    const int r = find_row(a.rows.blk0, a.rows.n_rows, blockIdx.x);
-    const int local = blockIdx.x - a.rows.blk0[r];
-    const int cols = a.rows.cols[r], nsplit = a.rows.nsplit[r], n = a.rows.nnew[r];
+    const int nrow = a.rows.n_rows;
+    const int first = lane_entry(a.rows.blk0, nrow, 0x7fffffff);
+    const int r = wave_find_row(first, blockIdx.x);
+    const int local = blockIdx.x - row_entry(first, r);
+    const int cols = row_entry(lane_entry(a.rows.cols, nrow, 16), r);
+    const int nsplit = row_entry(lane_entry(a.rows.nsplit, nrow, 1), r);
+    const int n = row_entry(lane_entry(a.rows.nnew, nrow, 0), r);
     const int tq = cols / a.group;
     const int nq = (n + tq - 1) / tq;
     const int per_group = (cols * DC + 255) / 256;   // blocks per (kv head, query tile)
     const int grp = local / per_group, part = local % per_group;
     const int kvh = grp / nq, qtile = grp % nq;
-    const int b = a.rows.b[r];
-    const int64_t rec_first = a.rows.pbase[r] + (int64_t)((kvh * nq + qtile) * nsplit) * cols;
+    const int b = row_entry(lane_entry(a.rows.b, nrow, 0), r);
+    const int64_t rec_first = row_entry(lane_entry(a.rows.pbase, nrow, 0), r) +
+                              (int64_t)((kvh * nq + qtile) * nsplit) * cols;
     const int task = part * 256 + threadIdx.x;       // one (column, 4 outputs) per thread
     if (task >= cols * DC) return;
     const int col = task / DC, d = (task % DC) * 4;
@@ -1247,39 +1330,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     if (col >= tq * a.group || t >= n) return;
     const int h = kvh * a.group + col % a.group;
     const int64_t rec = rec_first + col;
-    float M = -INFINITY, L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
-        float2 ml[8];
-        float4 x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t rs = rec + (int64_t)(s0 + j) * cols;
-            if (s0 + j < nsplit) {
-                ml[j] = *reinterpret_cast<const float2 *>(a.ws_ml + rs * 2);
-                x[j] = *reinterpret_cast<const float4 *>(a.ws_acc + rs * D + d);
-            } else {
-                ml[j] = make_float2(-INFINITY, 0.f);
-                x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        }
-        float bm = M;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bm = fmaxf(bm, ml[j].x);
-        if (bm == -INFINITY) continue;            // no split so far saw a key of this column
-        const float c = fast_exp2(M - bm);        // M = -inf: c = 0 (acc and L are still 0)
-        acc *= c;
-        L *= c;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float w = fast_exp2(ml[j].x - bm);   // a split that saw no key: w = 0
-            acc[0] += w * x[j].x; acc[1] += w * x[j].y; acc[2] += w * x[j].z; acc[3] += w * x[j].w;
-            L += w * ml[j].y;
-        }
-        M = bm;
-    }
     E *op = reinterpret_cast<E *>(a.out) + (((int64_t)b * a.hq + h) * a.T + t) * D + d;
-    O::store4(op, acc * (L > 0.f ? 1.f / L : 0.f));
+    O::store4(op, merge_partials<D>(a.ws_acc, a.ws_ml, rec, cols, nsplit, d));
 }
 
 // ---------------------------------------------------------------------------

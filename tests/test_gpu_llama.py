@@ -56,6 +56,32 @@ def test_llama_decode_b32_s4096():
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+@pytest.mark.parametrize("tp", [2, 8])
+def test_llama_decode_head_shard(tp):
+    """One GPU's share under tensor parallelism over heads (Hkv = 8/tp, Hq =
+    32/tp, all 32 rows at 4,096 cached keys), as one kv_append_attention step
+    (the benchmark's step): with few (row, KV head) items every row is split
+    across work groups and merged by the combine kernel. Sampled rows against
+    the oracle; the same bits as kv_append + gqa_attention."""
+    from gqa_attention_preallocated_amd import append_attention
+    KVCache, gqa_attention = _lib()
+    sh, seed = W.llama8b_decode_shard(tp), 7
+    caches = [KVCache(sh.batch, sh.kv_heads, sh.max_len, sh.head_dim) for _ in range(2)]
+    fill_rows(caches, sh, seed, [4096] * sh.batch)
+    n = [1] * sh.batch
+    q, k, v = W.step_inputs(sh, seed, 10_000, 1, n, pad="nan")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    out = append_attention(caches[0], kd, vd, qd, n)
+    caches[1].append(kd, vd, n)
+    out2 = gqa_attention(qd, caches[1], n)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    got = out_f64(out, "bf16")
+    for b in [0, 17, 31]:
+        kr, vr = row_history(sh, seed, b, 4096, k[b, :, :1], v[b, :, :1])
+        ref = direct.attention_row(kr, vr, 4097, 1, q[b], "bf16", [(h, 0) for h in range(sh.q_heads)])
+        assert_close(got[b], ref, "bf16", f"tp{tp} row {b}")
+
+
 def test_llama_verify_b16_t4():
     KVCache, gqa_attention = _lib()
     sh, seed = W.LLAMA8B_VERIFY, 2

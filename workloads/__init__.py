@@ -15,6 +15,7 @@ from .synth import (  # noqa: F401
     LLAMA8B_CHUNKED_PREFILL,
     LLAMA8B_RAGGED,
     LLAMA8B_WINDOW_DECODE,
+    llama8b_decode_shard,
     WORKLOADS,
     to_bf16_bits,
     bf16_bits_to_f32,

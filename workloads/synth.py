@@ -112,6 +112,17 @@ LLAMA8B_CHUNKED_PREFILL = Shape("llama8b_chunked_prefill_b4_10240x512", "bf16", 
 LLAMA8B_RAGGED = Shape("llama8b_ragged_b64", "bf16", 64, 32, 8, 128, 32768,
                        notes={"len_range": (1, 32000), "n_new_choices": (0, 1, 4, 256), "T": 256})
 
+
+
+def llama8b_decode_shard(tp: int) -> Shape:
+    """One GPU's share of the decode workload when tp GPUs split the heads:
+    8/tp KV heads with their 32/tp query heads (group 4 kept), all 32 rows."""
+    if tp not in (1, 2, 4, 8):
+        raise ValueError(tp)
+    return Shape(f"llama8b_decode_b32_s4096_tp{tp}", "bf16", 32, 32 // tp, 8 // tp, 128, 8192,
+                 value_scale=1.0 / math.sqrt(128.0), notes={"cached": 4096, "T": 1, "tp": tp})
+
+
 WORKLOADS = {s.name: s for s in (TINY_FP32, LLAMA8B_DECODE, LLAMA8B_VERIFY,
                                  LLAMA8B_CHUNKED_PREFILL, LLAMA8B_RAGGED)}
 
