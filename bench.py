@@ -137,6 +137,9 @@ def run_decode(torch, steps, warmup):
 
     walls = {}
     for name, fn in (("one_call", step), ("two_calls", step_two_calls)):
+        # a short device spin first brings the clock up from idle (as the
+        # other workloads' timing does); then the untimed warm-up steps
+        torch.cuda._sleep(20_000_000)
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()

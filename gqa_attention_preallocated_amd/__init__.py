@@ -101,6 +101,7 @@ class KVCache:
             self.v = torch.zeros(shape, dtype=store, device=device)
         self.lens_dev = torch.zeros(max(batch, 1), dtype=torch.int32, device=device) if device_lens else None
         self.dtype = dtype
+        self._device = self.k.device
         self.batch, self.kv_heads, self.max_len, self.head_dim = shape
         self.window = window
         self._ws = None
@@ -143,7 +144,7 @@ class KVCache:
 
     @property
     def device(self):
-        return self.k.device
+        return self._device
 
     @property
     def lens(self):
@@ -174,7 +175,7 @@ class KVCache:
         return int(self._lib.kv_live_bytes(self._h))
 
     def _check_tensor(self, x, name, heads):
-        if not isinstance(x, torch.Tensor) or x.device != self.device or x.dtype != self.dtype:
+        if not isinstance(x, torch.Tensor) or x.device != self._device or x.dtype != self.dtype:
             raise ValueError(f"{name} must be a {self.dtype} tensor on {self.device}")
         if x.dim() != 4 or x.shape[0] != self.batch or x.shape[1] != heads or x.shape[3] != self.head_dim:
             raise ValueError(f"{name} must be [B={self.batch}, {heads}, T, d={self.head_dim}], got {tuple(x.shape)}")
@@ -244,12 +245,12 @@ def gqa_attention(q, cache: KVCache, n_new, out=None, workspace=None, parents=No
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     lib = cache._lib
-    size = ctypes.c_size_t()
-    _lib.check(lib.gqa_attention_workspace_size(cache.handle, hq, T, arr, ctypes.byref(size)), lib)
-    need = int(size.value)
     if workspace is None:
-        ws = cache._workspace(need)
+        size = ctypes.c_size_t()
+        _lib.check(lib.gqa_attention_workspace_size(cache.handle, hq, T, arr, ctypes.byref(size)), lib)
+        ws = cache._workspace(int(size.value))
     else:
+        # a caller's workspace: the library checks its size (KV_ERR_WORKSPACE)
         if workspace.device != cache.device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor on the cache's device")
         ws = workspace
@@ -293,12 +294,12 @@ def append_attention(cache: KVCache, k_new, v_new, q, n_new, out=None, workspace
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     lib = cache._lib
-    size = ctypes.c_size_t()
-    _lib.check(lib.kv_append_attention_workspace_size(cache.handle, hq, T, arr, ctypes.byref(size)), lib)
-    need = int(size.value)
     if workspace is None:
-        ws = cache._workspace(need)
+        size = ctypes.c_size_t()
+        _lib.check(lib.kv_append_attention_workspace_size(cache.handle, hq, T, arr, ctypes.byref(size)), lib)
+        ws = cache._workspace(int(size.value))
     else:
+        # a caller's workspace: the library checks its size (KV_ERR_WORKSPACE)
         if workspace.device != cache.device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor on the cache's device")
         ws = workspace
