@@ -29,6 +29,16 @@
  * next call sees it at once. All calls on one handle must be issued from one
  * host thread at a time and kept in stream order by the caller.
  *
+ * Graph capture. kv_append, gqa_attention, gqa_attention_tree,
+ * kv_append_attention and kv_truncate enqueue only kernel launches (and, for
+ * a call with prefill rows beside other rows, an event fork and join with the
+ * handle's side stream, created by the first such call): no copies, memsets
+ * or device allocations, so they may be captured into a HIP graph. The host
+ * state (lengths, pages) moves once, when the call is captured; each replay
+ * repeats the captured lengths and block-table entries. A step that appends
+ * at a fixed length and rolls back replays correctly; a growing decode loop
+ * needs a new capture (or eager calls) as the lengths move.
+ *
  * Errors. Every call validates all of its arguments on the host before it
  * enqueues anything. KV_ERR_INVALID_ARG, KV_ERR_CAPACITY, KV_ERR_UNSUPPORTED
  * and KV_ERR_WORKSPACE mean nothing was enqueued and no state changed: not
