@@ -266,24 +266,41 @@ def _time_calls(torch, fn, reps):
 
 
 def run_verify(torch, reps=30):
-    """Speculative verify: B=16, 4,092 cached + 4 new tokens per row, T=4."""
-    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    """Speculative verify: B=16, 4,092 cached + 4 new tokens per row, T=4. The
+    step: kv_append_attention of the 4 draft tokens, then a host-only rollback
+    to 4,092 (two caches in turn); also the attention call alone."""
+    from gqa_attention_preallocated_amd import KVCache, append_attention, gqa_attention
     import workloads as W
     sh = W.LLAMA8B_VERIFY
     B, hq, hkv, d = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim
+    cached = sh.notes["cached"]
     caches = [KVCache(B, hkv, sh.max_len, d, device_lens=False) for _ in range(2)]
     n = [4] * B
     for i, c in enumerate(caches):
-        _fill_gpu_random(torch, c, [4096] * B, 20 + i)
+        _fill_gpu_random(torch, c, [cached] * B, 20 + i)
     g = torch.Generator(device="cuda").manual_seed(7)
     q = torch.randn(B, hq, 4, d, device="cuda", generator=g).to(torch.bfloat16)
+    kn = torch.randn(B, hkv, 4, d, device="cuda", generator=g).to(torch.bfloat16)
     out = torch.empty_like(q)
-    ws = torch.zeros(max(max(c.workspace_bytes(hq, 4, n) for c in caches), 256), dtype=torch.uint8, device="cuda")
-    t = _time_calls(torch, lambda i: gqa_attention(q, caches[i & 1], n, out=out, workspace=ws), reps)
-    nbytes = attention_bytes([4096] * B, n, hq, hkv, d, 4)
-    return {"metric": "verify attention HBM GB/s", "value": round(nbytes / t / 1e9, 2), "unit": "GB/s",
-            "frac_of_8TBs": round(nbytes / t / 8e12, 4), "ms": round(t * 1e3, 5), "bytes": nbytes,
-            "config": {"workload": sh.name, "batch": B, "T": 4, "keys": 4096}}
+    caches[0].append(kn, kn, n)
+    ws = torch.zeros(max(caches[0].workspace_bytes(hq, 4, n), 256), dtype=torch.uint8, device="cuda")
+    caches[0].truncate([cached] * B)
+
+    def step(i):
+        c = caches[i & 1]
+        append_attention(c, kn, kn, q, n, out=out, workspace=ws)
+        c.truncate([cached] * B)
+
+    t_step = _time_calls(torch, step, reps)
+    for c in caches:
+        c.append(kn, kn, n)
+    t_att = _time_calls(torch, lambda i: gqa_attention(q, caches[i & 1], n, out=out, workspace=ws), reps)
+    nbytes = attention_bytes([cached + 4] * B, n, hq, hkv, d, 4)
+    step_bytes = nbytes + 2 * sum(n) * hkv * d * 2      # and the new K and V rows written
+    return {"metric": "verify step HBM GB/s", "value": round(step_bytes / t_step / 1e9, 2), "unit": "GB/s",
+            "frac_of_8TBs": round(step_bytes / t_step / 8e12, 4), "ms": round(t_step * 1e3, 5), "bytes": step_bytes,
+            "attention_only": {"ms": round(t_att * 1e3, 5), "bytes": nbytes, "GB/s": round(nbytes / t_att / 1e9, 2)},
+            "config": {"workload": sh.name, "batch": B, "T": 4, "cached": cached, "keys": cached + 4}}
 
 
 def run_shard(torch, reps=40):
@@ -410,8 +427,10 @@ def run_tree(torch, reps=30):
 
 
 def run_ragged(torch, seed=4, reps=20):
-    """Ragged batch: 64 rows, log-uniform lengths in [1, 32000], n_new in {0, 1, 4, 256}, T=256."""
-    from gqa_attention_preallocated_amd import KVCache, gqa_attention
+    """Ragged batch: 64 rows, log-uniform lengths in [1, 32000], n_new in {0, 1, 4, 256}, T=256.
+    The step: kv_append_attention of every row's new tokens, then a host-only
+    rollback; also the attention call alone."""
+    from gqa_attention_preallocated_amd import KVCache, append_attention, gqa_attention
     import workloads as W
     sh = W.LLAMA8B_RAGGED
     B, hq, hkv, d, T = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim, 256
@@ -422,17 +441,26 @@ def run_ragged(torch, seed=4, reps=20):
     kn = torch.randn(B, hkv, T, d, device="cuda", generator=g).to(torch.bfloat16)
     q = torch.randn(B, hq, T, d, device="cuda", generator=g).to(torch.bfloat16)
     n = [int(x) for x in n_new]
-    cache.append(kn, kn, n)
+    base = [int(x) for x in lens]
     out = torch.empty_like(q)
+    cache.append(kn, kn, n)
     ws = torch.zeros(max(cache.workspace_bytes(hq, T, n), 256), dtype=torch.uint8, device="cuda")
-    t = _time_calls(torch, lambda i: gqa_attention(q, cache, n, out=out, workspace=ws), reps)
-    after = [int(l) + x for l, x in zip(lens, n)]
-    nbytes = attention_bytes(after, n, hq, hkv, d, T)
+    t_att = _time_calls(torch, lambda i: gqa_attention(q, cache, n, out=out, workspace=ws), reps)
+    cache.truncate(base)
+
+    def step(i):
+        append_attention(cache, kn, kn, q, n, out=out, workspace=ws)
+        cache.truncate(base)
+
+    t = _time_calls(torch, step, reps)
+    after = [l + x for l, x in zip(base, n)]
+    nbytes = attention_bytes(after, n, hq, hkv, d, T) + 2 * sum(n) * hkv * d * 2
     flops = attention_flops(after, n, hq, d)
     t_bw, t_mm = nbytes / 8e12, flops / 2.5e15
-    return {"metric": "ragged batch attention, lower bound / time", "value": round(max(t_bw, t_mm) / t, 4),
-            "unit": "fraction", "ms": round(t * 1e3, 5), "bytes": nbytes, "flops": flops,
-            "hbm_frac": round(t_bw / t, 4), "mfma_frac": round(t_mm / t, 4),
+    return {"metric": "ragged batch step (append + attention), lower bound / time",
+            "value": round(max(t_bw, t_mm) / t, 4), "unit": "fraction", "ms": round(t * 1e3, 5),
+            "bytes": nbytes, "flops": flops, "hbm_frac": round(t_bw / t, 4), "mfma_frac": round(t_mm / t, 4),
+            "attention_only_ms": round(t_att * 1e3, 5),
             "rows_by_n_new": {str(k): int((n_new == k).sum()) for k in (0, 1, 4, 256)},
             "config": {"workload": sh.name, "seed": seed, "batch": B, "T": T, "sum_lens": int(sum(after))}}
 

@@ -173,7 +173,11 @@ constexpr int kPrefillKeyTile = 64;
 // float32 at d = 128 keeps 4 (its accumulators need the full register file
 // of one wave per SIMD). The planner and the kernels take the count from here.
 inline constexpr int prefill_waves(int dtype, int head_dim) { return (dtype == 0 && head_dim == 128) ? 4 : 8; }
-inline constexpr int prefill_cols(int dtype, int head_dim) { return 32 * prefill_waves(dtype, head_dim); }
+// 16-column subtiles per prefill wave (2: 32 columns)
+inline constexpr int prefill_subtiles(int dtype, int head_dim) { return (void)dtype, (void)head_dim, 2; }
+inline constexpr int prefill_cols(int dtype, int head_dim) {
+    return 16 * prefill_subtiles(dtype, head_dim) * prefill_waves(dtype, head_dim);
+}
 // Window of a linear cache: pos - kNoWindow < 0 <= every key, so no lower bound.
 constexpr int32_t kNoWindow = 0x7fffffff;
 // Ring caches hold a multiple of this many slots, and key ranges start at a

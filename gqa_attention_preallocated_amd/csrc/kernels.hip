@@ -886,7 +886,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 // or below the first query's position are not masked; only tiles straddling
 // the diagonal compare indices ([MASK] "A strong answer", tiled-kernel rule).
 // ---------------------------------------------------------------------------
-template <typename E, int D, bool F8, bool PG, int PW>
+template <typename E, int D, bool F8, bool PG, int PW, int NS>
 __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8 ? 2 : 1))) void prefill_kernel(AttnArgs a) {
     using O = Op<E>;
     using S = Stor<E, F8>;
@@ -894,9 +894,9 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     constexpr int KT = kPrefillKeyTile;           // 64 keys per tile
     constexpr int KC = D >= 32 ? D / 32 : 1;
     constexpr int NB = D / 16;
-    constexpr int C = 32 * PW;                    // columns per item
+    constexpr int WC = 16 * NS;                   // columns per wave (NS 16-column subtiles)
+    constexpr int C = WC * PW;                    // columns per item
     constexpr int NT = 64 * PW;                   // threads per work group
-    constexpr int NS = 2;                         // 16-column subtiles per wave
     constexpr int ROWB = D * O::kBytes;           // LDS bytes of a K or V row (compute type)
     constexpr int RS = ROWB + O::kPad;
     constexpr int CROWB = D * S::kBytes;          // cache bytes of a row
@@ -916,7 +916,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     int wave_pos_max = -1, wave_pos_min = 0x7fffffff;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        const int col = wave * 32 + s * 16 + lr;
+        const int col = wave * WC + s * 16 + lr;
         pos[s] = column_position(it, col, a.group, C);
         const E *qp = pos[s] >= 0 ? column_q<E>(a, it, col, D) : nullptr;
 #pragma unroll
@@ -926,9 +926,9 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
         }
     }
     {
-        // range of real positions among the wave's 32 columns (uniform over the wave)
+        // range of real positions among the wave's columns (uniform over the wave)
         const int tq = C / a.group;
-        const int c_lo = wave * 32, c_hi = min(wave * 32 + 31, tq * a.group - 1);
+        const int c_lo = wave * WC, c_hi = min(wave * WC + WC - 1, tq * a.group - 1);
         if (c_lo <= c_hi) {
             const int t_lo = it.t0 + c_lo / a.group;
             const int t_hi = min(it.t0 + c_hi / a.group, it.t_end - 1);
@@ -1080,13 +1080,14 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
         for (int s = 0; s < NS; ++s) m[s] = (st[s].m == -INFINITY) ? 0.f : st[s].m;
     };
 
-    // phase X: 2*NB steps of PV (ch = g / NB, nb = g % NB, both subtiles), the
+    // phase X: 2*NB steps of PV (ch = g / NB, nb = g % NB, every subtile), the
     // all-ones MFMAs of chunk 0 after step NB-1 and of chunk 1 at the end.
-    // VALU, first NB steps: the max tree of tile i as ten tasks (per subtile:
-    // four quarter maxima, then the column max), task t at step t * NB / 10 so
-    // every task runs after the ones it needs. VALU, last NB steps (chunk 0's
-    // operands are consumed by then): the probabilities of chunk 0 of tile i
-    // against the current reference max, task u at step NB + u * NB / 8. The
+    // VALU, first NB steps: the max tree of tile i as 5 NS tasks (per subtile:
+    // four quarter maxima, then the column max), task t at step t * NB / (5 NS)
+    // so every task runs after the ones it needs. VALU, last NB steps (chunk
+    // 0's operands are consumed by then): the 4 NS probability pairs of chunk 0
+    // of tile i against the current reference max, pair u at step NB + u * NB /
+    // (4 NS). The
     // reference only moves when a column's max outgrows it by more than
     // kRescaleLog2; finish_max then recomputes chunk 0 for those columns, so
     // every probability of the tile uses one reference, as if computed after
@@ -1112,22 +1113,22 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
             }
             if (g < NB) {
 #pragma unroll
-                for (int t = 0; t < 10; ++t) {
-                    if (t * NB / 10 != g) continue;
-                    if (t < 8) {
+                for (int t = 0; t < 5 * NS; ++t) {
+                    if (t * NB / (5 * NS) != g) continue;
+                    if (t < 4 * NS) {
                         const int s = t >> 2, q = t & 3;      // quarter q = (ch, ks) block
                         const f32x4 x = sc[q >> 1][s][q & 1];
                         part[s][q] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
                     } else {
-                        const int s = t - 8;
+                        const int s = t - 4 * NS;
                         const float m4 = fmaxf(fmaxf(part[s][0], part[s][1]), fmaxf(part[s][2], part[s][3]));
                         tmax[s] = wave_max_across_groups(m4) * score_c;
                     }
                 }
             } else {
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    if (NB + u * NB / 8 == g) prob_pair(0, u, m0[u >> 2]);
+                for (int u = 0; u < 4 * NS; ++u)
+                    if (NB + u * NB / (4 * NS) == g) prob_pair(0, u, m0[u >> 2]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1135,10 +1136,10 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
         for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, pb[1][s], acc[s][NB]);
     };
     // phase Y: 16 steps of scores for tile i+1 (ch = g / 8, kc = (g / 2) % 4,
-    // ks = g % 2, both subtiles; steps with kc >= KC issue no MFMA): an
-    // accumulator is updated every fourth MFMA, and only the four of one
-    // chunk are live while the probabilities of chunk 1 of tile i, one pair
-    // in each of the first 8 steps, free their scores
+    // ks = g % 2, every subtile; steps with kc >= KC issue no MFMA): an
+    // accumulator is updated every fourth MFMA, and only those of one chunk
+    // are live while the probabilities of chunk 1 of tile i, NS / 2 pairs in
+    // each of the first 8 steps, free their scores
     auto phase_y = [&](const unsigned char *kn, const float (&m_use)[NS], f32x4 (&scn)[2][NS][2]) {
         auto kop = [&](int g) {
             const int krow = (g >> 3) * 32 + (g & 1) * 16 + lr;
@@ -1159,7 +1160,9 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
                     scn[ch][s][ks] = O::mma(kv[g % 3], qop[s][kc], c0);
                 }
             }
-            if (g < 8) prob_pair(1, g, m_use[g >> 2]);
+#pragma unroll
+            for (int u = 0; u < 4 * NS; ++u)
+                if (u / (NS / 2) == g) prob_pair(1, u, m_use[u >> 2]);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -1184,7 +1187,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
         }
         if (!chunk0_done) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) prob_pair(0, u, m_use[u >> 2]);
+            for (int u = 0; u < 4 * NS; ++u) prob_pair(0, u, m_use[u >> 2]);
         }
     };
 
@@ -1252,7 +1255,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         const float l = acc[s][NB][0];
-        const int col = wave * 32 + s * 16 + lr;
+        const int col = wave * WC + s * 16 + lr;
         if (pos[s] < 0) continue;
         if (it.rec0 < 0) {
             E *op = column_out<E>(a, it, col, D);
@@ -1402,8 +1405,9 @@ hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, h
 
 template <typename E, int D, bool F8, bool PG>
 static void prefill_d(const AttnArgs &a, hipStream_t s) {
-    constexpr int PW = prefill_waves(std::is_same<E, float>::value ? 0 : 1, D);
-    hipLaunchKernelGGL((prefill_kernel<E, D, F8, PG, PW>), dim3(a.rows.total_items), dim3(64 * PW), 0, s, a);
+    constexpr int dt = std::is_same<E, float>::value ? 0 : 1;
+    constexpr int PW = prefill_waves(dt, D), NS = prefill_subtiles(dt, D);
+    hipLaunchKernelGGL((prefill_kernel<E, D, F8, PG, PW, NS>), dim3(a.rows.total_items), dim3(64 * PW), 0, s, a);
 }
 
 template <typename E, bool F8, bool PG>
