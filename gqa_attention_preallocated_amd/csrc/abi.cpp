@@ -577,9 +577,8 @@ kv_status kv_append_attention(kv_cache *c, const void *k_new, const void *v_new,
     Plan p;
     s = attention_prepare(c, after.data(), q, q_heads, T, n_new, out, workspace, workspace_bytes, p);
     if (s != KV_OK) return s;
-    // rows of the decode kernel append themselves (an E4M3 cache quantizes in
-    // the copy kernel, so its rows are all appended there)
-    const bool fuse = c->dtype != KV_DTYPE_FP8_E4M3 && !p.dec.empty();
+    // rows of the decode kernel append themselves
+    const bool fuse = !p.dec.empty();
     std::vector<char> skip(c->batch, 0);
     if (fuse)
         for (const RowPlan &r : p.dec) skip[r.b] = 1;
@@ -771,6 +770,8 @@ kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_
     for (size_t h = 0; h < c->k_scale.size(); ++h) {
         a.k_scale[h] = c->k_scale[h];
         a.v_scale[h] = c->v_scale[h];
+        a.k_inv[h] = c->k_inv[h];
+        a.v_inv[h] = c->v_inv[h];
     }
     a.records = p.records;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c->head_dim));

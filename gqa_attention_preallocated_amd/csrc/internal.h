@@ -90,12 +90,14 @@ struct AttnArgs {
     int64_t records;           // partial records available in the workspace
     float scale_log2;          // log2(e) / sqrt(d)
     float k_scale[kMaxScaleHeads], v_scale[kMaxScaleHeads];   // E4M3 caches: code x scale per KV head
+    float k_inv[kMaxScaleHeads], v_inv[kMaxScaleHeads];       // and the float32 1 / scale the append uses
     const int32_t *table;      // paged cache: block table [B, max_blocks] (null: linear or ring)
     int32_t page_shift;        // log2(page size)
     int32_t max_blocks;
     // kv_append_attention on decode-kernel rows: the kernel writes each row's
-    // new tokens from k_new / v_new ([B, Hkv, T, d]) into the cache and reads
-    // those keys from k_new / v_new; one work group per row sets lens_dev
+    // new tokens from k_new / v_new ([B, Hkv, T, d]) into the cache (E4M3:
+    // their codes) and reads those keys from k_new / v_new; one work group per
+    // row sets lens_dev
     int32_t fuse;
     const void *k_new;
     const void *v_new;

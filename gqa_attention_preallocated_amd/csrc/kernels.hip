@@ -613,28 +613,35 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k);
     const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v);
     KeyRows<PG> km(a, it, w_begin);
-    if constexpr (!F8) {
-        if (a.fuse) {
-            // kv_append_attention: the new tokens in this item's key range go
-            // into the cache here, 16 bytes per thread per step. Items of one
-            // row that hold the same token write the same bytes, and every new
-            // token lies in some item's range. The attention below reads these
-            // keys from k_new / v_new, so nothing waits for the writes.
-            const int lo = it.k_begin > it.base ? it.k_begin : it.base, n_tok = it.k_end - lo;
-            const int64_t knew_row0 = ((int64_t)it.b * a.hkv + it.kvh) * a.T + (lo - it.base);
-            for (int task = tid; task < 2 * n_tok * CPK; task += 64 * W) {
-                const int tv = task / (n_tok * CPK), rem = task % (n_tok * CPK);
-                const int tok = rem / CPK, part = rem % CPK;
-                const int64_t src = (knew_row0 + tok) * CROWB + part * 16;
-                const int64_t dst = cache_row<PG>(a, it.b, it.kvh, lo + tok) * CROWB + part * 16;
-                const unsigned char *sb = reinterpret_cast<const unsigned char *>(tv ? a.v_new : a.k_new);
-                unsigned char *db = reinterpret_cast<unsigned char *>(const_cast<void *>(tv ? a.v : a.k));
-                *reinterpret_cast<uint4 *>(db + dst) = *reinterpret_cast<const uint4 *>(sb + src);
-            }
-            // the first item of a row sets the row's device length
-            if (a.lens_dev != nullptr && tid == 0 && blockIdx.x == a.rows.item0[it.r])
-                a.lens_dev[it.b] = a.rows.len[it.r];
+    // rows of k_new / v_new hold d input elements (bfloat16 for an E4M3 cache)
+    constexpr int NROWB = D * (int)sizeof(E);
+    if (a.fuse) {
+        // kv_append_attention: the new tokens in this item's key range go into
+        // the cache here, 16 input bytes per thread per step (an E4M3 cache
+        // stores the codes of x * (1 / scale), computed as the append kernel
+        // does). Items of one row that hold the same token write the same
+        // bytes, and every new token lies in some item's range. The attention
+        // below reads these keys from k_new / v_new, so nothing waits for the
+        // writes.
+        const int lo = it.k_begin > it.base ? it.k_begin : it.base, n_tok = it.k_end - lo;
+        const int64_t new0 = ((int64_t)it.b * a.hkv + it.kvh) * a.T + (lo - it.base);
+        constexpr int PPR = NROWB / 16;                 // 16-byte input pieces per row
+        for (int task = tid; task < 2 * n_tok * PPR; task += 64 * W) {
+            const int tv = task / (n_tok * PPR), rem = task % (n_tok * PPR);
+            const int tok = rem / PPR, part = rem % PPR;
+            const unsigned char *sb = reinterpret_cast<const unsigned char *>(tv ? a.v_new : a.k_new);
+            unsigned char *db = reinterpret_cast<unsigned char *>(const_cast<void *>(tv ? a.v : a.k));
+            const uint4 x = *reinterpret_cast<const uint4 *>(sb + (new0 + tok) * NROWB + part * 16);
+            const int64_t crow = cache_row<PG>(a, it.b, it.kvh, lo + tok);
+            if constexpr (F8)
+                *reinterpret_cast<uint2 *>(db + crow * CROWB + part * 8) =
+                    quant8(x, tv ? a.v_inv[it.kvh] : a.k_inv[it.kvh]);
+            else
+                *reinterpret_cast<uint4 *>(db + crow * CROWB + part * 16) = x;
         }
+        // the first item of a row sets the row's device length
+        if (a.lens_dev != nullptr && tid == 0 && blockIdx.x == a.rows.item0[it.r])
+            a.lens_dev[it.b] = a.rows.len[it.r];
     }
     // an E4M3 cache stands for code x scale of the head: the K scale joins the
     // score scale, the V scale multiplies the output
@@ -662,39 +669,43 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     // a tile's keys are consecutive cache rows from km.row(tile): no tile
     // wraps (ring capacities are multiples of kRingAlign, pages of kMinPage,
     // and tiles start at multiples of KT)
-    // kv_append_attention (never for E4M3 caches): keys at or past the row's
-    // first new position come from k_new / v_new [B, Hkv, T, d] (FRESH tiles)
+    // kv_append_attention: keys at or past the row's first new position come
+    // from k_new / v_new [B, Hkv, T, d] (FRESH tiles)
     const unsigned char *knew = nullptr, *vnew = nullptr;
-    if constexpr (!F8) {
-        if (a.fuse) {
-            const int64_t r0 = ((int64_t)it.b * a.hkv + it.kvh) * a.T;
-            knew = reinterpret_cast<const unsigned char *>(a.k_new) + r0 * CROWB;
-            vnew = reinterpret_cast<const unsigned char *>(a.v_new) + r0 * CROWB;
-        }
+    if (a.fuse) {
+        const int64_t r0 = ((int64_t)it.b * a.hkv + it.kvh) * a.T;
+        knew = reinterpret_cast<const unsigned char *>(a.k_new) + r0 * NROWB;
+        vnew = reinterpret_cast<const unsigned char *>(a.v_new) + r0 * NROWB;
     }
+    const float kinv = F8 ? a.k_inv[it.kvh] : 1.f, vinv = F8 ? a.v_inv[it.kvh] : 1.f;
+    // 16 storage bytes at byte `off` of new token t, from k_new / v_new (nb):
+    // an E4M3 cache gets the 16 codes of 16 bfloat16 inputs, as stored
+    auto fresh16 = [&](const unsigned char *nb, int t, int off, float inv) -> uint4 {
+        if constexpr (F8) {
+            const unsigned char *p = nb + (int64_t)t * NROWB + off * 2;
+            const uint2 c0 = quant8(load_stream(p), inv), c1 = quant8(load_stream(p + 16), inv);
+            return make_uint4(c0.x, c0.y, c1.x, c1.y);
+        } else {
+            return load_stream(nb + (int64_t)t * NROWB + off);
+        }
+    };
     auto load_tile_as = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile, auto fresh) {
         constexpr bool FRESH = decltype(fresh)::value;
         const int64_t row0 = km.row(tile);
         const unsigned char *kt = kbase + row0 * CROWB;
         const unsigned char *vt = vbase + row0 * CROWB;
-        auto krow = [&](int key) -> const unsigned char * {
-            if constexpr (FRESH)
-                if (tile + key >= it.base) return knew + (int64_t)(tile + key - it.base) * CROWB;
-            return kt + key * CROWB;
-        };
-        auto vrow = [&](int key) -> const unsigned char * {
-            if constexpr (FRESH)
-                if (tile + key >= it.base) return vnew + (int64_t)(tile + key - it.base) * CROWB;
-            return vt + key * CROWB;
-        };
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int key = ks * 16 + lr;
             const bool ok = tile + key < w_end;
+            const bool nw = FRESH && tile + key >= it.base;       // a new key: from k_new
+            const int t = tile + key - it.base;
             if constexpr (KPAIR) {
 #pragma unroll
                 for (int j = 0; j < KC / 2; ++j) {
-                    const uint4 w = ok ? load_stream(krow(key) + dmap(2 * j)) : make_uint4(0, 0, 0, 0);
+                    const int off = dmap(2 * j);                  // codes: byte = d
+                    const uint4 w = !ok ? make_uint4(0, 0, 0, 0)
+                                  : nw ? fresh16(knew, t, off, kinv) : load_stream(kt + key * CROWB + off);
                     kop[ks][2 * j] = make_uint2(w.x, w.y);
                     kop[ks][2 * j + 1] = make_uint2(w.z, w.w);
                 }
@@ -702,7 +713,16 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
                     const int d0 = dmap(kc);
-                    kop[ks][kc] = (ok && d0 < D) ? S::load_k(krow(key) + d0 * S::kBytes) : S::zero_k();
+                    if (!(ok && d0 < D)) {
+                        kop[ks][kc] = S::zero_k();
+                    } else if (nw) {
+                        if constexpr (F8)
+                            kop[ks][kc] = quant8(*reinterpret_cast<const uint4 *>(knew + (int64_t)t * NROWB + d0 * 2), kinv);
+                        else
+                            kop[ks][kc] = S::load_k(knew + (int64_t)t * NROWB + d0 * S::kBytes);
+                    } else {
+                        kop[ks][kc] = S::load_k(kt + key * CROWB + d0 * S::kBytes);
+                    }
                 }
             }
         }
@@ -711,15 +731,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
             const int c = lane + 64 * i;
             const int key = c / CPK, part = c % CPK;
             const bool ok = (c < KT * CPK) && (tile + key < w_end);
-            vreg[i] = ok ? load_stream(vrow(key) + part * 16) : make_uint4(0, 0, 0, 0);
+            const bool nw = FRESH && tile + key >= it.base;
+            vreg[i] = !ok ? make_uint4(0, 0, 0, 0)
+                    : nw ? fresh16(vnew, tile + key - it.base, part * 16, vinv) : load_stream(vt + key * CROWB + part * 16);
         }
     };
     auto load_tile = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
-        if constexpr (!F8) {
-            if (a.fuse && tile + KT > it.base) {           // uniform over the wave
-                load_tile_as(kop, vreg, tile, std::true_type{});
-                return;
-            }
+        if (a.fuse && tile + KT > it.base) {               // uniform over the wave
+            load_tile_as(kop, vreg, tile, std::true_type{});
+            return;
         }
         load_tile_as(kop, vreg, tile, std::false_type{});
     };

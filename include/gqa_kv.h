@@ -284,9 +284,10 @@ kv_status gqa_attention_tree(kv_cache *c, const void *q, int32_t q_heads, int32_
  * Every check of both halves runs before anything is enqueued, with the
  * lengths the append will leave; any error other than KV_ERR_DEVICE changes
  * nothing. Rows that run on the split-K decode kernel are appended by that
- * kernel, which reads those keys from k_new / v_new, so one launch does the
- * append and the attention of a decode step; other rows, and every row of an
- * E4M3 cache, are appended by the copy kernel first.
+ * kernel, which reads those keys from k_new / v_new (an E4M3 cache: it stores
+ * their codes and attends to the same codes), so one launch does the append
+ * and the attention of a decode step; other rows are appended by the copy
+ * kernel first.
  *   k_new, v_new  device [B, Hkv, T, d]; q, out device [B, q_heads, T, d]
  *   n_new         HOST int32[B]
  *   workspace     as gqa_attention, of at least

@@ -222,8 +222,16 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
     // kv_append_attention: the kernel writes its key range's new tokens and
     // reads keys at or past the row's first new position from k_new / v_new
     const bool fuse = a.fuse != 0;
-    if (fuse && (cache_elem != elem || key_tile != kDecodeKeyTile || a.k_new == nullptr || a.v_new == nullptr))
-        err("attention: fused append outside the decode kernel of a float32 / bfloat16 cache");
+    const int64_t in_row = (int64_t)D * elem;                 // k_new / v_new rows (input type)
+    if (fuse && (key_tile != kDecodeKeyTile || a.k_new == nullptr || a.v_new == nullptr))
+        err("attention: fused append outside the decode kernel");
+    if (fuse && cache_elem != elem) {
+        // an E4M3 cache: codes of bfloat16 inputs, quantized with the append's 1 / scale
+        if (cache_elem != 1 || elem != 2) err("attention: fused append with mismatched element sizes");
+        for (int h = 0; h < a.hkv; ++h)
+            if (h >= kMaxScaleHeads || !(a.k_inv[h] > 0.f) || !(a.v_inv[h] > 0.f) || !(a.k_scale[h] > 0.f))
+                err("attention: fused E4M3 append without its scales");
+    }
     std::set<uintptr_t> fused_chunks;    // 16-byte chunks of K written by this launch
     auto new_row = [&](const Item &it, int r, int key) -> int64_t {   // k_new row of key `key`
         const int t = key - it.base;
@@ -263,7 +271,7 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
         const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
         if (fuse) {
             for (int p = std::max(it.k_begin, it.base); p < it.k_end; ++p) {
-                const int64_t src = new_row(it, r, p) * cache_row;
+                const int64_t src = new_row(it, r, p) * in_row;
                 int64_t dst = head * a.max_len + p % a.max_len;
                 if (paged) {
                     const int64_t ti = (int64_t)it.b * a.max_blocks + (p >> a.page_shift);
@@ -272,11 +280,13 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
                     if (page < 0) err("fused append: block without a page");
                     dst = (((int64_t)page * a.hkv + it.kvh) << a.page_shift) + (p & ((1 << a.page_shift) - 1));
                 }
-                access((const char *)a.k_new + src, cache_row, "k_new", "fused append read k_new");
-                access((const char *)a.v_new + src, cache_row, "v_new", "fused append read v_new");
+                access((const char *)a.k_new + src, in_row, "k_new", "fused append read k_new");
+                access((const char *)a.v_new + src, in_row, "v_new", "fused append read v_new");
                 access((const char *)a.k + dst * cache_row, cache_row, "k", "fused append write K");
                 access((const char *)a.v + dst * cache_row, cache_row, "v", "fused append write V");
-                for (int64_t o = 0; o < cache_row; o += 16) fused_chunks.insert((uintptr_t)a.k + dst * cache_row + o);
+                // one entry per 16 input bytes, at the bytes they land on (as the copy kernel's)
+                for (int64_t o = 0; o < in_row; o += 16)
+                    fused_chunks.insert((uintptr_t)a.k + dst * cache_row + o * cache_row / in_row);
             }
             if (a.lens_dev != nullptr && item == R.item0[r]) {
                 access(a.lens_dev + it.b, 4, "lens", "fused append lens_dev");
@@ -308,9 +318,9 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
             if (fuse && t0 + key_tile > it.base)
                 for (int key : {std::max(t0, it.base), t0 + n - 1}) {
                     if (key < it.base) continue;
-                    const int64_t src = new_row(it, r, key) * cache_row;
-                    access((const char *)a.k_new + src, cache_row, "k_new", "fused attention k_new");
-                    access((const char *)a.v_new + src, cache_row, "v_new", "fused attention v_new");
+                    const int64_t src = new_row(it, r, key) * in_row;
+                    access((const char *)a.k_new + src, in_row, "k_new", "fused attention k_new");
+                    access((const char *)a.v_new + src, in_row, "v_new", "fused attention v_new");
                 }
         }
         for (int col = 0; col < cols; ++col) {

@@ -4,7 +4,9 @@ The fused call must leave exactly what kv_append followed by gqa_attention
 leaves: the same output bits, the same cache bytes, the same host and device
 lengths, after every call of a schedule with prefill chunks, decode and verify
 steps, empty rows and a rollback, on every cache kind (float32, bfloat16,
-sliding-window ring, paged, E4M3) and under each kernel selection. The
+sliding-window ring, paged, E4M3: the decode kernel stores the codes and
+quantizes the new keys it reads exactly as the append kernel does) and under
+each kernel selection. The
 unfused pair is itself checked against the oracle elsewhere; the outputs here
 are also checked against the oracle directly for the linear caches.
 [GQA] "A strong answer" (each step appends at the row's length, then attends).
@@ -60,7 +62,7 @@ CALLS = [(70, [70, 33, 0]), (1, [1, 1, 1]), (5, [5, 2, 5]), (130, [3, 130, 64]),
 
 
 @pytest.mark.parametrize("kind", ["f32", "bf16", "ring", "paged", "fp8"])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_fused_matches_append_then_attention(kind, d):
     KVCache, append_attention, gqa_attention = _lib()
     B, hk, G, S = 3, 2, 4, 768
