@@ -32,8 +32,11 @@ def library_path():
     return _lib.LIB_PATH
 
 
-def _stream_ptr():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+def _stream_ptr(index=None):
+    """The current HIP stream of device `index` (default: the current device)."""
+    if index is None:
+        index = torch.cuda.current_device()
+    return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(index))
 
 
 def _row_counts(n_new, batch):
@@ -190,7 +193,7 @@ class KVCache:
             raise ValueError("k_new and v_new differ in shape")
         n = _row_counts(n_new, self.batch)
         st = self._lib.kv_append(self._h, ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
-                                 k_new.shape[2], _lib.int32_array(n), _stream_ptr())
+                                 k_new.shape[2], _lib.int32_array(n), _stream_ptr(self._device.index))
         _lib.check(st, self._lib)
 
     def truncate(self, new_lens):
@@ -198,7 +201,7 @@ class KVCache:
         if isinstance(new_lens, int):
             new_lens = [new_lens] * self.batch
         n = _row_counts(new_lens, self.batch)
-        _lib.check(self._lib.kv_truncate(self._h, _lib.int32_array(n), _stream_ptr()), self._lib)
+        _lib.check(self._lib.kv_truncate(self._h, _lib.int32_array(n), _stream_ptr(self._device.index)), self._lib)
 
     def reset(self):
         self.truncate(0)
@@ -258,14 +261,14 @@ def gqa_attention(q, cache: KVCache, n_new, out=None, workspace=None, parents=No
     ws_len = ws.numel() if ws is not None else 0
     if parents is None:
         st = lib.gqa_attention(cache.handle, ctypes.c_void_p(q.data_ptr()), hq, T, arr,
-                               ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_len, _stream_ptr())
+                               ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_len, _stream_ptr(cache._device.index))
     else:
         flat = [int(x) for row in (parents.tolist() if hasattr(parents, "tolist") else parents) for x in row]
         if len(flat) != B * T:
             raise ValueError(f"parents must be [B={B}, T={T}]")
         st = lib.gqa_attention_tree(cache.handle, ctypes.c_void_p(q.data_ptr()), hq, T, arr,
                                     _lib.int32_array(flat), ctypes.c_void_p(out.data_ptr()), ws_ptr, ws_len,
-                                    _stream_ptr())
+                                    _stream_ptr(cache._device.index))
     _lib.check(st, lib)
     return out
 
@@ -306,6 +309,6 @@ def append_attention(cache: KVCache, k_new, v_new, q, n_new, out=None, workspace
     st = lib.kv_append_attention(cache.handle, ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
                                  ctypes.c_void_p(q.data_ptr()), hq, T, arr, ctypes.c_void_p(out.data_ptr()),
                                  ctypes.c_void_p(ws.data_ptr() if ws is not None else 0),
-                                 ws.numel() if ws is not None else 0, _stream_ptr())
+                                 ws.numel() if ws is not None else 0, _stream_ptr(cache._device.index))
     _lib.check(st, lib)
     return out

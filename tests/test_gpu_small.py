@@ -90,6 +90,18 @@ def test_mqa_mha_and_odd_groups(hk, G, dtype):
         _run_schedule(shape, calls, 7, policy, check_bytes=False)
 
 
+@pytest.mark.parametrize("hk,G,d", [(1, 128, 64), (2, 64, 128), (1, 65, 32)])
+def test_largest_groups(hk, G, d):
+    """The largest group sizes: G = 64 still fits a decode work item (64
+    columns); above it every row runs on the prefill kernel (256 columns), up
+    to the ABI's limit of G = 128."""
+    shape = W.Shape(f"g{G}", "bf16", 2, hk * G, hk, d, 160)
+    calls = [{"T": 70, "n_new": [70, 33]}, {"T": 1, "n_new": [1, 1]}, {"T": 5, "n_new": [5, 2]},
+             {"T": 40, "n_new": [3, 40]}]
+    for policy in [(0, 0), (1, 0), (2, 0), (1, 32)]:
+        _run_schedule(shape, calls, 9, policy, check_bytes=False)
+
+
 def test_split_count_invariance():
     """Many small key splits vs one split agree within float32 rounding."""
     KVCache, gqa_attention = _lib()
