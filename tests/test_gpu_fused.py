@@ -144,3 +144,30 @@ def test_fused_refusals_change_nothing():
     assert cache.lens == before[0]
     assert torch.equal(cache.lens_dev, before[1])
     assert torch.equal(cache.k, before[2]) and torch.equal(cache.v, before[3])
+
+
+def test_fused_empty_inputs():
+    """No new tokens, T = 0 and B = 0 give zeros of the right shape and change
+    nothing; a row with no new tokens beside rows with some is zero-filled."""
+    KVCache, append_attention, gqa_attention = _lib()
+    cache = KVCache(2, 2, 16, 32, dtype=torch.float32)
+    q = torch.full((2, 4, 3, 32), float("nan"), device="cuda")
+    kn = torch.full((2, 2, 3, 32), float("nan"), device="cuda")
+    out = append_attention(cache, kn, kn, q, [0, 0])       # empty cache, nothing appended
+    assert torch.equal(out, torch.zeros_like(out))
+    assert cache.lens == [0, 0]
+    q0 = torch.zeros((2, 4, 0, 32), device="cuda")
+    k0 = torch.zeros((2, 2, 0, 32), device="cuda")
+    assert append_attention(cache, k0, k0, q0, [0, 0]).shape == (2, 4, 0, 32)
+    c0 = KVCache(0, 2, 16, 32, dtype=torch.float32)
+    z = torch.zeros((0, 4, 3, 32), device="cuda")
+    assert append_attention(c0, torch.zeros((0, 2, 3, 32), device="cuda"),
+                            torch.zeros((0, 2, 3, 32), device="cuda"), z, []).shape == (0, 4, 3, 32)
+    kv = torch.randn(2, 2, 3, 32, device="cuda")
+    qq = torch.randn(2, 4, 3, 32, device="cuda")
+    out = append_attention(cache, kv, kv, qq, [2, 0])
+    torch.cuda.synchronize()
+    assert cache.lens == [2, 0]
+    assert torch.equal(out[1], torch.zeros_like(out[1]))
+    assert torch.equal(out[0, :, 2:], torch.zeros_like(out[0, :, 2:]))
+    assert torch.isfinite(out).all()
