@@ -577,11 +577,12 @@ kv_status kv_append_attention(kv_cache *c, const void *k_new, const void *v_new,
     Plan p;
     s = attention_prepare(c, after.data(), q, q_heads, T, n_new, out, workspace, workspace_bytes, p);
     if (s != KV_OK) return s;
-    // rows of the decode kernel append themselves
+    // rows of the decode kernel append themselves; prefill rows go through
+    // the copy kernel (appending in the prefill kernel measured slower: it
+    // costs that kernel registers on every tile)
     const bool fuse = !p.dec.empty();
     std::vector<char> skip(c->batch, 0);
-    if (fuse)
-        for (const RowPlan &r : p.dec) skip[r.b] = 1;
+    for (const RowPlan &r : p.dec) skip[r.b] = 1;
     s = append_commit(c, k_new, v_new, T, n_new, pages, &skip, stream);
     if (s != KV_OK) return s;
     Fused f;

@@ -17,6 +17,7 @@
 namespace gqakv {
 
 GQAKV_HD inline int imin(int a, int b) { return a < b ? a : b; }
+GQAKV_HD inline int imax(int a, int b) { return a > b ? a : b; }
 
 // Largest r in [0, n_rows) with item0[r] <= item (item0 is nondecreasing
 // from item0[0] = 0): the number of rows r >= 1 whose first item is <= item.

@@ -476,6 +476,51 @@ __device__ inline int64_t cache_row(const AttnArgs &a, int b, int h, int p) {
     }
 }
 
+// kv_append_attention on decode-kernel rows. Each new token is written by
+// exactly one work item: the one whose query tile holds the token's own
+// query and whose key split holds the token (every new position p = base + t
+// lies in the key range of the tile of query t, and the splits of a tile
+// partition that range). The kernel reads the new keys from k_new / v_new
+// ([B, Hkv, T, d] rows of NROWB input bytes), so no read waits for these
+// writes.
+template <int D, bool F8, bool PG, int NROWB>
+__device__ inline void write_new_tokens(const AttnArgs &a, const Item &it, int tid, int nthreads) {
+    constexpr int CROWB = F8 ? D : NROWB;             // cache bytes of a row
+    constexpr int PPR = NROWB / 16;                   // 16-byte input pieces per row
+    const int lo = imax(it.k_begin, it.base + it.t0), hi = imin(it.k_end, it.base + it.t_end);
+    const int n_tok = hi - lo;
+    if (n_tok <= 0) return;
+    const int64_t new0 = ((int64_t)it.b * a.hkv + it.kvh) * a.T + (lo - it.base);
+    for (int task = tid; task < 2 * n_tok * PPR; task += nthreads) {
+        const int tv = task / (n_tok * PPR), rem = task % (n_tok * PPR);
+        const int tok = rem / PPR, part = rem % PPR;
+        const unsigned char *sb = reinterpret_cast<const unsigned char *>(tv ? a.v_new : a.k_new);
+        unsigned char *db = reinterpret_cast<unsigned char *>(const_cast<void *>(tv ? a.v : a.k));
+        const uint4 x = *reinterpret_cast<const uint4 *>(sb + (new0 + tok) * NROWB + part * 16);
+        const int64_t crow = cache_row<PG>(a, it.b, it.kvh, lo + tok);
+        // an E4M3 cache stores the codes of x * (1 / scale), as the append kernel does
+        if constexpr (F8)
+            *reinterpret_cast<uint2 *>(db + crow * CROWB + part * 8) =
+                quant8(x, tv ? a.v_inv[it.kvh] : a.k_inv[it.kvh]);
+        else
+            *reinterpret_cast<uint4 *>(db + crow * CROWB + part * 16) = x;
+    }
+}
+
+// 16 storage bytes at storage byte `off` of new token t of a (row, kv head)
+// whose k_new / v_new rows start at nb: an E4M3 cache gets the 16 codes of
+// 16 bfloat16 inputs, exactly as they are stored
+template <bool F8, int NROWB>
+__device__ inline uint4 new_chunk(const unsigned char *nb, int t, int off, float inv) {
+    if constexpr (F8) {
+        const unsigned char *p = nb + (int64_t)t * NROWB + off * 2;
+        const uint2 c0 = quant8(load_stream(p), inv), c1 = quant8(load_stream(p + 16), inv);
+        return make_uint4(c0.x, c0.y, c1.x, c1.y);
+    } else {
+        return load_stream(nb + (int64_t)t * NROWB + off);
+    }
+}
+
 // One online-softmax step for the 8 scores a lane holds for its column
 // (two 16-key blocks: s0 = keys 4g..4g+3, s1 = keys 16+4g..16+4g+3 of a
 // 32-key chunk, g = lane/16). Scores arrive unscaled; `pos` is the column's
@@ -616,29 +661,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     // rows of k_new / v_new hold d input elements (bfloat16 for an E4M3 cache)
     constexpr int NROWB = D * (int)sizeof(E);
     if (a.fuse) {
-        // kv_append_attention: the new tokens in this item's key range go into
-        // the cache here, 16 input bytes per thread per step (an E4M3 cache
-        // stores the codes of x * (1 / scale), computed as the append kernel
-        // does). Items of one row that hold the same token write the same
-        // bytes, and every new token lies in some item's range. The attention
-        // below reads these keys from k_new / v_new, so nothing waits for the
-        // writes.
-        const int lo = it.k_begin > it.base ? it.k_begin : it.base, n_tok = it.k_end - lo;
-        const int64_t new0 = ((int64_t)it.b * a.hkv + it.kvh) * a.T + (lo - it.base);
-        constexpr int PPR = NROWB / 16;                 // 16-byte input pieces per row
-        for (int task = tid; task < 2 * n_tok * PPR; task += 64 * W) {
-            const int tv = task / (n_tok * PPR), rem = task % (n_tok * PPR);
-            const int tok = rem / PPR, part = rem % PPR;
-            const unsigned char *sb = reinterpret_cast<const unsigned char *>(tv ? a.v_new : a.k_new);
-            unsigned char *db = reinterpret_cast<unsigned char *>(const_cast<void *>(tv ? a.v : a.k));
-            const uint4 x = *reinterpret_cast<const uint4 *>(sb + (new0 + tok) * NROWB + part * 16);
-            const int64_t crow = cache_row<PG>(a, it.b, it.kvh, lo + tok);
-            if constexpr (F8)
-                *reinterpret_cast<uint2 *>(db + crow * CROWB + part * 8) =
-                    quant8(x, tv ? a.v_inv[it.kvh] : a.k_inv[it.kvh]);
-            else
-                *reinterpret_cast<uint4 *>(db + crow * CROWB + part * 16) = x;
-        }
+        // kv_append_attention: this item's share of the new tokens goes into
+        // the cache here; the attention below reads them from k_new / v_new
+        write_new_tokens<D, F8, PG, NROWB>(a, it, tid, 64 * W);
         // the first item of a row sets the row's device length
         if (a.lens_dev != nullptr && tid == 0 && blockIdx.x == a.rows.item0[it.r])
             a.lens_dev[it.b] = a.rows.len[it.r];
@@ -678,17 +703,6 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         vnew = reinterpret_cast<const unsigned char *>(a.v_new) + r0 * NROWB;
     }
     const float kinv = F8 ? a.k_inv[it.kvh] : 1.f, vinv = F8 ? a.v_inv[it.kvh] : 1.f;
-    // 16 storage bytes at byte `off` of new token t, from k_new / v_new (nb):
-    // an E4M3 cache gets the 16 codes of 16 bfloat16 inputs, as stored
-    auto fresh16 = [&](const unsigned char *nb, int t, int off, float inv) -> uint4 {
-        if constexpr (F8) {
-            const unsigned char *p = nb + (int64_t)t * NROWB + off * 2;
-            const uint2 c0 = quant8(load_stream(p), inv), c1 = quant8(load_stream(p + 16), inv);
-            return make_uint4(c0.x, c0.y, c1.x, c1.y);
-        } else {
-            return load_stream(nb + (int64_t)t * NROWB + off);
-        }
-    };
     auto load_tile_as = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile, auto fresh) {
         constexpr bool FRESH = decltype(fresh)::value;
         const int64_t row0 = km.row(tile);
@@ -705,7 +719,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
                 for (int j = 0; j < KC / 2; ++j) {
                     const int off = dmap(2 * j);                  // codes: byte = d
                     const uint4 w = !ok ? make_uint4(0, 0, 0, 0)
-                                  : nw ? fresh16(knew, t, off, kinv) : load_stream(kt + key * CROWB + off);
+                                  : nw ? new_chunk<F8, NROWB>(knew, t, off, kinv) : load_stream(kt + key * CROWB + off);
                     kop[ks][2 * j] = make_uint2(w.x, w.y);
                     kop[ks][2 * j + 1] = make_uint2(w.z, w.w);
                 }
@@ -733,7 +747,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
             const bool ok = (c < KT * CPK) && (tile + key < w_end);
             const bool nw = FRESH && tile + key >= it.base;
             vreg[i] = !ok ? make_uint4(0, 0, 0, 0)
-                    : nw ? fresh16(vnew, tile + key - it.base, part * 16, vinv) : load_stream(vt + key * CROWB + part * 16);
+                    : nw ? new_chunk<F8, NROWB>(vnew, tile + key - it.base, part * 16, vinv)
+                         : load_stream(vt + key * CROWB + part * 16);
         }
     };
     auto load_tile = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {

@@ -6,8 +6,8 @@
 // checks on the CPU that
 //   * every K/V/q/out/workspace/lens access lies inside a registered buffer,
 //   * append writes only the slots [lens, lens + n_new) of each row, once
-//     (the copy kernel, or the decode kernel of kv_append_attention, whose
-//     items may write one token more than once within a launch),
+//     (the copy kernel, or in kv_append_attention the attention kernels'
+//     items, each token by exactly one item),
 //   * each attention call writes every output row (b, h, t) exactly once,
 //   * each split partial is written once before the combine kernel reads it.
 // Buffers are fake addresses registered by the test; nothing is dereferenced.
@@ -18,7 +18,6 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
-#include <set>
 #include <string>
 #include <vector>
 
@@ -223,8 +222,7 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
     // reads keys at or past the row's first new position from k_new / v_new
     const bool fuse = a.fuse != 0;
     const int64_t in_row = (int64_t)D * elem;                 // k_new / v_new rows (input type)
-    if (fuse && (key_tile != kDecodeKeyTile || a.k_new == nullptr || a.v_new == nullptr))
-        err("attention: fused append outside the decode kernel");
+    if (fuse && (a.k_new == nullptr || a.v_new == nullptr)) err("attention: fused append without k_new / v_new");
     if (fuse && cache_elem != elem) {
         // an E4M3 cache: codes of bfloat16 inputs, quantized with the append's 1 / scale
         if (cache_elem != 1 || elem != 2) err("attention: fused append with mismatched element sizes");
@@ -232,7 +230,6 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
             if (h >= kMaxScaleHeads || !(a.k_inv[h] > 0.f) || !(a.v_inv[h] > 0.f) || !(a.k_scale[h] > 0.f))
                 err("attention: fused E4M3 append without its scales");
     }
-    std::set<uintptr_t> fused_chunks;    // 16-byte chunks of K written by this launch
     auto new_row = [&](const Item &it, int r, int key) -> int64_t {   // k_new row of key `key`
         const int t = key - it.base;
         if (t < 0 || t >= R.nnew[r] || t >= a.T) err("attention: k_new row outside the row's new tokens");
@@ -270,7 +267,8 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
         if (windowed && lo_visible < std::max(0, R.len[r] - a.max_len)) err("attention: window key evicted");
         const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
         if (fuse) {
-            for (int p = std::max(it.k_begin, it.base); p < it.k_end; ++p) {
+            // the item writes the new tokens of its own query tile that lie in its key split
+            for (int p = std::max(it.k_begin, it.base + it.t0); p < std::min(it.k_end, it.base + it.t_end); ++p) {
                 const int64_t src = new_row(it, r, p) * in_row;
                 int64_t dst = head * a.max_len + p % a.max_len;
                 if (paged) {
@@ -286,7 +284,7 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
                 access((const char *)a.v + dst * cache_row, cache_row, "v", "fused append write V");
                 // one entry per 16 input bytes, at the bytes they land on (as the copy kernel's)
                 for (int64_t o = 0; o < in_row; o += 16)
-                    fused_chunks.insert((uintptr_t)a.k + dst * cache_row + o * cache_row / in_row);
+                    g_appended[(uintptr_t)a.k + dst * cache_row + o * cache_row / in_row]++;   // exactly once
             }
             if (a.lens_dev != nullptr && item == R.item0[r]) {
                 access(a.lens_dev + it.b, 4, "lens", "fused append lens_dev");
@@ -344,7 +342,6 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
             }
         }
     }
-    for (uintptr_t c : fused_chunks) g_appended[c]++;
 }
 
 hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t) {
