@@ -171,3 +171,39 @@ def test_fused_empty_inputs():
     assert torch.equal(out[1], torch.zeros_like(out[1]))
     assert torch.equal(out[0, :, 2:], torch.zeros_like(out[0, :, 2:]))
     assert torch.isfinite(out).all()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fused_random_trials(seed):
+    """Seeded random shapes and schedules (1, 2 or 4 KV heads, G 1..8, 1..3 rows,
+    chunks of 1..8 tokens, d in 16..128), each call made as one
+    kv_append_attention and as kv_append + gqa_attention on a twin cache: the
+    same output, cache and length bits, under each kernel selection."""
+    KVCache, append_attention, gqa_attention = _lib()
+    shape, calls = W.trial_spec(seed, head_dims=(16, 32, 64, 128))
+    kind = ["f32", "bf16", "paged", "fp8"][seed % 4]
+    dt = "f32" if kind == "f32" else "bf16"
+    shape = W.Shape(shape.name, dt, shape.batch, shape.q_heads, shape.kv_heads, shape.head_dim, 64)
+    B, hk, d = shape.batch, shape.kv_heads, shape.head_dim
+
+    def make():
+        if kind == "paged":
+            return KVCache(B, hk, 64, d, page_size=64, num_pages=B)
+        if kind == "fp8":
+            return KVCache(B, hk, 64, d, fp8_scales=([0.05] * hk, [0.05] * hk))
+        return KVCache(B, hk, 64, d, dtype=TORCH_DTYPE[dt])
+
+    for policy in [(0, 0), (1, 32), (2, 64)]:
+        ref, fus = make(), make()
+        for c in (ref, fus):
+            c.set_policy(*policy)
+        for i, call in enumerate(calls):
+            T, n = call["T"], call["n_new"]
+            q, k, v = W.step_inputs(shape, 91 + seed, i, T, n, pad="nan")
+            qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+            ref.append(kd, vd, n)
+            want = gqa_attention(qd, ref, n)
+            got = append_attention(fus, kd, vd, qd, n)
+            what = f"seed {seed} {kind} policy {policy} call {i}"
+            _same_state(ref, fus, what)
+            assert torch.equal(want.view(torch.uint8), got.view(torch.uint8)), f"{what}: output bits"
