@@ -273,11 +273,12 @@ def gqa_attention(q, cache: KVCache, n_new, out=None, workspace=None, parents=No
     return out
 
 
-def append_attention(cache: KVCache, k_new, v_new, q, n_new, out=None, workspace=None):
-    """``cache.append(k_new, v_new, n_new)`` then ``gqa_attention(q, cache, n_new)``
-    in one library call (kv_append_attention): rows on the decode kernel are
-    appended by that kernel, so a decode step is one launch. Same bits as the
-    two calls."""
+def append_attention(cache: KVCache, k_new, v_new, q, n_new, out=None, workspace=None, parents=None):
+    """``cache.append(k_new, v_new, n_new)`` then ``gqa_attention(q, cache, n_new,
+    parents=parents)`` in one library call (kv_append_attention, or
+    kv_append_attention_tree with ``parents``): rows on the decode kernel are
+    appended by that kernel, so a decode or verify step is one launch. Same bits
+    as the two calls."""
     cache._check_tensor(k_new, "k_new", cache.kv_heads)
     cache._check_tensor(v_new, "v_new", cache.kv_heads)
     if k_new.shape != v_new.shape:
@@ -306,9 +307,16 @@ def append_attention(cache: KVCache, k_new, v_new, q, n_new, out=None, workspace
         if workspace.device != cache.device or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
             raise ValueError("workspace must be a contiguous uint8 tensor on the cache's device")
         ws = workspace
-    st = lib.kv_append_attention(cache.handle, ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
-                                 ctypes.c_void_p(q.data_ptr()), hq, T, arr, ctypes.c_void_p(out.data_ptr()),
-                                 ctypes.c_void_p(ws.data_ptr() if ws is not None else 0),
-                                 ws.numel() if ws is not None else 0, _stream_ptr(cache._device.index))
+    ptrs = (ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(q.data_ptr()))
+    ws_args = (ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), ws.numel() if ws is not None else 0,
+               _stream_ptr(cache._device.index))
+    if parents is None:
+        st = lib.kv_append_attention(cache.handle, *ptrs, hq, T, arr, ctypes.c_void_p(out.data_ptr()), *ws_args)
+    else:
+        flat = [int(x) for row in (parents.tolist() if hasattr(parents, "tolist") else parents) for x in row]
+        if len(flat) != B * T:
+            raise ValueError(f"parents must be [B={B}, T={T}]")
+        st = lib.kv_append_attention_tree(cache.handle, *ptrs, hq, T, arr, _lib.int32_array(flat),
+                                          ctypes.c_void_p(out.data_ptr()), *ws_args)
     _lib.check(st, lib)
     return out

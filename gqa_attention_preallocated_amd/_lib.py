@@ -27,7 +27,7 @@ EXPORTED = (
     "gqa_attention", "kv_truncate", "kv_get_lens", "kv_cache_bytes", "kv_live_bytes",
     "kv_last_error", "kv_cache_set_policy", "kv_cache_create_ring", "kv_cache_create_fp8",
     "gqa_attention_tree", "kv_cache_create_paged", "kv_get_block_table", "kv_free_pages",
-    "kv_append_attention", "kv_append_attention_workspace_size",
+    "kv_append_attention", "kv_append_attention_workspace_size", "kv_append_attention_tree",
 )
 
 _lib = None
@@ -73,6 +73,8 @@ def load():
     lib.gqa_attention_tree.restype = ctypes.c_int
     lib.kv_append_attention.argtypes = [P, P, P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
     lib.kv_append_attention.restype = ctypes.c_int
+    lib.kv_append_attention_tree.argtypes = [P, P, P, P, I32, I32, I32P, I32P, P, P, ctypes.c_size_t, P]
+    lib.kv_append_attention_tree.restype = ctypes.c_int
     lib.kv_append_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]
     lib.kv_append_attention_workspace_size.restype = ctypes.c_int
     lib.kv_truncate.argtypes = [P, I32P, P]

@@ -327,6 +327,10 @@ kv_status attention_prepare(const kv_cache *c, const int32_t *lens, const void *
                             const int32_t *n_new, void *out, void *workspace, size_t workspace_bytes, Plan &p);
 // New tokens a decode kernel appends itself (kv_append_attention): read from
 // k_new / v_new [B, Hkv, T, d] and written to the cache by the kernel.
+kv_status check_tree(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new, const int32_t *parents);
+kv_status append_attention_call(kv_cache *c, const void *k_new, const void *v_new, const void *q, int32_t q_heads,
+                                int32_t T, const int32_t *n_new, const int32_t *parents, void *out,
+                                void *workspace, size_t workspace_bytes, void *stream);
 struct Fused {
     const void *k_new = nullptr, *v_new = nullptr;
 };
@@ -531,19 +535,8 @@ kv_status gqa_attention_tree(kv_cache *c, const void *q, int32_t q_heads, int32_
                              void *stream) {
     kv_status s = check_attention_args(c, c == nullptr ? nullptr : c->lens.data(), q_heads, T, n_new);
     if (s != KV_OK) return s;
-    if (T > kMaxTreeNodes || (int64_t)(q_heads / c->kv_heads) * T > 64)
-        return fail(KV_ERR_UNSUPPORTED, "tree verify takes at most %d nodes and G * T <= 64", kMaxTreeNodes);
-    if (c->ring) return fail(KV_ERR_UNSUPPORTED, "tree verify runs on linear caches");
-    if (c->path_policy == 2) return fail(KV_ERR_UNSUPPORTED, "tree verify runs on the split-K decode kernel");
-    if (c->batch > 0 && T > 0 && parents == nullptr) return fail(KV_ERR_INVALID_ARG, "parents is null");
-    // [MASK] "What interviewers probe next": parent pointers; here every parent
-    // is -1 (the committed prefix) or an earlier node of the same row
-    for (int b = 0; b < c->batch; ++b)
-        for (int u = 0; u < n_new[b]; ++u) {
-            const int p = parents[(int64_t)b * T + u];
-            if (p < -1 || p >= u)
-                return fail(KV_ERR_INVALID_ARG, "row %d node %d: parent %d is not -1 or an earlier node", b, u, p);
-        }
+    s = check_tree(c, q_heads, T, n_new, parents);
+    if (s != KV_OK) return s;
     return attention_call(c, q, q_heads, T, n_new, parents, out, workspace, workspace_bytes, stream);
 }
 
@@ -568,6 +561,50 @@ kv_status kv_append_attention_workspace_size(const kv_cache *c, int32_t q_heads,
 kv_status kv_append_attention(kv_cache *c, const void *k_new, const void *v_new, const void *q, int32_t q_heads,
                               int32_t T, const int32_t *n_new, void *out, void *workspace, size_t workspace_bytes,
                               void *stream) {
+    return append_attention_call(c, k_new, v_new, q, q_heads, T, n_new, nullptr, out, workspace, workspace_bytes,
+                                 stream);
+}
+
+kv_status kv_append_attention_tree(kv_cache *c, const void *k_new, const void *v_new, const void *q,
+                                   int32_t q_heads, int32_t T, const int32_t *n_new, const int32_t *parents,
+                                   void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
+    kv_status s = check_tree(c, q_heads, T, n_new, parents);
+    if (s != KV_OK) return s;
+    return append_attention_call(c, k_new, v_new, q, q_heads, T, n_new, parents, out, workspace, workspace_bytes,
+                                 stream);
+}
+
+}  // extern "C"
+
+namespace {
+kv_status check_tree(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new, const int32_t *parents) {
+    if (q_heads <= 0 || q_heads % c->kv_heads != 0)
+        return fail(KV_ERR_INVALID_ARG, "q_heads %d is not a positive multiple of kv_heads %d", q_heads,
+                    c->kv_heads);
+    if (T < 0 || (c->batch > 0 && n_new == nullptr)) return fail(KV_ERR_INVALID_ARG, "bad T or null n_new");
+    if (T > kMaxTreeNodes || (int64_t)(q_heads / c->kv_heads) * T > 64)
+        return fail(KV_ERR_UNSUPPORTED, "tree verify takes at most %d nodes and G * T <= 64", kMaxTreeNodes);
+    if (c->ring) return fail(KV_ERR_UNSUPPORTED, "tree verify runs on linear caches");
+    if (c->path_policy == 2) return fail(KV_ERR_UNSUPPORTED, "tree verify runs on the split-K decode kernel");
+    if (c->batch > 0 && T > 0 && parents == nullptr) return fail(KV_ERR_INVALID_ARG, "parents is null");
+    // [MASK] "What interviewers probe next": parent pointers; here every parent
+    // is -1 (the committed prefix) or an earlier node of the same row
+    for (int b = 0; b < c->batch; ++b) {
+        if (n_new[b] < 0 || n_new[b] > T)
+            return fail(KV_ERR_INVALID_ARG, "row %d: n_new %d outside 0..%d", b, n_new[b], T);
+        for (int u = 0; u < n_new[b]; ++u) {
+            const int p = parents[(int64_t)b * T + u];
+            if (p < -1 || p >= u)
+                return fail(KV_ERR_INVALID_ARG, "row %d node %d: parent %d is not -1 or an earlier node", b, u, p);
+        }
+    }
+    return KV_OK;
+}
+
+kv_status append_attention_call(kv_cache *c, const void *k_new, const void *v_new, const void *q, int32_t q_heads,
+                                int32_t T, const int32_t *n_new, const int32_t *parents, void *out,
+                                void *workspace, size_t workspace_bytes, void *stream) {
     // every check of both halves first, against the lengths after the append
     int64_t pages = 0;
     kv_status s = append_check(c, k_new, v_new, T, n_new, &pages);
@@ -588,13 +625,10 @@ kv_status kv_append_attention(kv_cache *c, const void *k_new, const void *v_new,
     Fused f;
     f.k_new = k_new;
     f.v_new = v_new;
-    s = attention_launch(c, p, q, q_heads, T, n_new, nullptr, out, workspace, fuse ? &f : nullptr, stream);
+    s = attention_launch(c, p, q, q_heads, T, n_new, parents, out, workspace, fuse ? &f : nullptr, stream);
     return s == KV_OK ? ok() : s;
 }
 
-}  // extern "C"
-
-namespace {
 kv_status append_check(const kv_cache *c, const void *k_new, const void *v_new, int32_t T, const int32_t *n_new,
                        int64_t *pages_out, bool check_pointers) {
     if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");

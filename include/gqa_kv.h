@@ -298,6 +298,17 @@ kv_status kv_append_attention(kv_cache *c, const void *k_new, const void *v_new,
                               void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kv_append_attention for a draft tree: exactly kv_append followed by
+ * gqa_attention_tree with the same parents ([MASK] "What interviewers probe
+ * next"), bit for bit, in one launch of the decode kernel. Arguments and
+ * limits as both; parents HOST int32 [B, T]. Any error other than
+ * KV_ERR_DEVICE changes nothing.
+ */
+kv_status kv_append_attention_tree(kv_cache *c, const void *k_new, const void *v_new, const void *q,
+                                   int32_t q_heads, int32_t T, const int32_t *n_new, const int32_t *parents,
+                                   void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Workspace kv_append_attention needs for these arguments (the
  * gqa_attention workspace for the lengths after the append), in bytes.
  */

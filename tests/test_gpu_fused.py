@@ -207,3 +207,42 @@ def test_fused_random_trials(seed):
             what = f"seed {seed} {kind} policy {policy} call {i}"
             _same_state(ref, fus, what)
             assert torch.equal(want.view(torch.uint8), got.view(torch.uint8)), f"{what}: output bits"
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_fused_tree_matches_append_then_tree_attention(paged):
+    """kv_append_attention_tree: the draft tree's tokens appended and verified in
+    one launch, with the bits of kv_append + gqa_attention_tree ([MASK] "What
+    interviewers probe next"), rolled back after every step as a verifier does;
+    refusals (a ring, a bad parent) change nothing."""
+    KVCache, append_attention, gqa_attention = _lib()
+    B, hk, G, d, S = 3, 2, 4, 128, 512
+    shape = W.Shape("tree_fused", "bf16", B, hk * G, hk, d, S)
+    kw = dict(page_size=64, num_pages=B * S // 64) if paged else {}
+    ref, fus = KVCache(B, hk, S, d, **kw), KVCache(B, hk, S, d, **kw)
+    base = [300, 17, 64]
+    fill_rows([ref, fus], shape, 5, base)
+    par = [[-1, 0, 1, 2, 0, 4, -1, 6], [-1, -1, 1, 1, 3, 0, 5, 2], [-1, 0, 0, 0, 1, 2, 3, 4]]
+    for step, n in enumerate([[8, 8, 8], [5, 8, 0], [1, 2, 3]]):
+        q, k, v = W.step_inputs(shape, 5, step, 8, n, pad="nan")
+        qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+        ref.append(kd, vd, n)
+        want = gqa_attention(qd, ref, n, parents=par)
+        got = append_attention(fus, kd, vd, qd, n, parents=par)
+        _same_state(ref, fus, f"tree step {step}")
+        assert torch.equal(want.view(torch.uint8), got.view(torch.uint8)), f"tree step {step}: output bits"
+        ref.truncate(base)
+        fus.truncate(base)
+    torch.cuda.synchronize()
+    before = (fus.lens, fus.k.clone(), fus.v.clone())
+    q, k, v = W.step_inputs(shape, 5, 9, 8, [8, 8, 8], pad="nan")
+    with pytest.raises(ValueError):                    # node 3's parent is not an earlier node
+        append_attention(fus, to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(q, "bf16"), [8, 8, 8],
+                         parents=[[-1, 0, 1, 3, 0, 4, -1, 6]] * 3)
+    torch.cuda.synchronize()
+    assert fus.lens == before[0] and torch.equal(fus.k, before[1]) and torch.equal(fus.v, before[2])
+    ring = KVCache(B, hk, 256, d, window=64)
+    with pytest.raises(ValueError):                    # tree verify runs on linear caches
+        append_attention(ring, to_dev(k, "bf16"), to_dev(v, "bf16"), to_dev(q, "bf16"), [1, 1, 1],
+                         parents=[[-1] * 8] * 3)
+    assert ring.lens == [0, 0, 0]
