@@ -47,6 +47,7 @@ def sim(tmp_path_factory):
     lib.gqa_attention_tree.argtypes = [P, P, I32, I32, I32P, I32P, P, P, ctypes.c_size_t, P]
     lib.kv_append_attention.argtypes = [P, P, P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
     lib.kv_append_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kv_append_attention_tree.argtypes = [P, P, P, P, I32, I32, I32P, I32P, P, P, ctypes.c_size_t, P]
     lib.kv_truncate.argtypes = [P, I32P, P]
     lib.kv_cache_set_policy.argtypes = [P, I32, I32]
     lib.kv_cache_destroy.argtypes = [P]
@@ -539,3 +540,34 @@ def test_append_attention_ring_wraps(sim, d, C, win):
         for call in calls:
             c.append_attention(call["T"], call["n_new"])
             c.check(call["T"])
+
+
+def test_append_attention_tree(sim):
+    """kv_append_attention_tree: the tree's tokens written exactly once by the
+    decode kernel's items, every output row once, lens_dev set; the tree rules
+    refuse a bad parent before anything is written."""
+    sh = W.LLAMA8B_VERIFY
+    c = SimCache(sim, sh.batch, sh.kv_heads, sh.max_len, sh.head_dim, "bf16", sh.q_heads, 4096)
+    for call in _prefix_calls([4092] * sh.batch):
+        c.append(call["T"], call["n_new"])
+    T = 8
+    n = [8] * (sh.batch - 2) + [5, 0]
+    parents = [-1, 0, 1, 2, 0, 4, -1, 6] * sh.batch
+    size = ctypes.c_size_t()
+    assert sim.kv_append_attention_workspace_size(c.h, sh.q_heads, T, _i32(n), ctypes.byref(size)) == 0
+    a = c.addr
+
+    def call(par):
+        sim.hostcheck_begin_call()
+        return sim.kv_append_attention_tree(c.h, ctypes.c_void_p(a["k_new"]), ctypes.c_void_p(a["v_new"]),
+                                            ctypes.c_void_p(a["q"]), sh.q_heads, T, _i32(n), _i32(par),
+                                            ctypes.c_void_p(a["out"]), ctypes.c_void_p(a["ws"]), size.value, None)
+    bad = list(parents)
+    bad[3] = 3
+    launches = sim.hostcheck_launches()
+    assert call(bad) == 1 and b"parent" in sim.kv_last_error()
+    assert sim.hostcheck_launches() == launches          # refused before any launch
+    assert call(parents) == 0, sim.kv_last_error()
+    c.lens += np.asarray(n)
+    c.appended += int(np.sum(n)) * c.hk * c.d * c.elem // 16
+    c.check(T)
