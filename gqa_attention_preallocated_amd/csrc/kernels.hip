@@ -591,12 +591,15 @@ __device__ inline void softmax_tile(const float (&v)[N], float c, ColState &st, 
 
 // ---------------------------------------------------------------------------
 // split-K decode / verify kernel. One work group of W waves per work item
-// (row, kv head, query tile, key split) with 16*NSUB columns. The item's key
-// range is cut into W contiguous pieces, one per wave (a fixed assignment, so
-// results are bitwise reproducible); each wave streams its 32-key tiles from
-// HBM with the next tiles in flight while one is computed, then the waves
-// merge their partial results through LDS (reusing the V staging space), so a
-// split-free row needs no second pass.
+// (row, kv head, query tile, key split) with 16*NSUB columns. The item's
+// 32-key tiles are dealt to the waves in turn (wave w takes tiles w, w + W,
+// ...: a fixed assignment, so results are bitwise reproducible, and the work
+// group reads one contiguous run of K and of V at a time); each wave streams
+// its tiles from HBM with the next tile in flight while one is computed, then
+// the waves merge their partial results through LDS (reusing the V staging
+// space), so a split-free row needs no second pass. In kv_append_attention
+// the kernel also writes its share of the new tokens into the cache and reads
+// the new keys from k_new / v_new.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int NSUB, int W, bool F8, bool PG>
 __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
