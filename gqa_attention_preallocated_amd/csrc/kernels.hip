@@ -228,14 +228,24 @@ template <> struct Stor<bf16_t, true> {
 // results below 2^-126; a probability that small is zero for every purpose here.
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max of scores, which are finite or -inf (masked keys), never NaN. The
+// NaN-propagating maximum needs no quieting of its inputs, where fmaxf makes
+// the compiler canonicalize every operand that is not the result of another
+// max first (one extra VALU instruction per score), and it pairs into the
+// three-input v_maximum3_f32.
+__device__ inline float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ inline float smax8(float a, float b, float c, float d, float e, float f, float g, float h) {
+    return smax(smax(smax(smax(a, b), c), smax(smax(d, e), f)), smax(g, h));
+}
+
 __device__ inline float wave_max_across_groups(float v) {
     // lanes l, l^16, l^32, l^48 hold the same column. A gfx950 lane-half swap
     // returns (own, partner) in some order, so the max of the pair is the max
     // over the two lanes, with no LDS traffic.
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    v = smax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return smax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ inline float wave_sum_across_groups(float v) {
@@ -545,7 +555,7 @@ constexpr float kRescaleLog2 = 8.f;
 // the scaled scores. Writes p = exp2(v*c - m) and updates the state.
 template <int NB>
 __device__ inline void softmax_step(const float (&v)[8], float c, ColState &st, f32x4 (&acc)[NB], f32x8 &p) {
-    float tmax = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    float tmax = smax8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
     tmax = wave_max_across_groups(tmax) * c;
     if (tmax > st.m + kRescaleLog2) {             // st.m = -inf: the first visible key sets it
         const float alpha = fast_exp2(st.m - tmax);   // 0 when st.m = -inf (acc and l are still 0)
@@ -572,9 +582,9 @@ __device__ inline void softmax_step(const float (&v)[8], float c, ColState &st, 
 template <int NB, int N>
 __device__ inline void softmax_tile(const float (&v)[N], float c, ColState &st, f32x4 (&acc)[NB], f32x8 &p0,
                                     f32x8 &p1) {
-    float t0 = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-    float t1 = fmaxf(fmaxf(fmaxf(v[8], v[9]), fmaxf(v[10], v[11])), fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15])));
-    const float tmax = wave_max_across_groups(fmaxf(t0, t1)) * c;
+    float t0 = smax8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+    float t1 = smax8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
+    const float tmax = wave_max_across_groups(smax(t0, t1)) * c;
     if (tmax > st.m + kRescaleLog2) {
         const float alpha = fast_exp2(st.m - tmax);
 #pragma unroll
@@ -1079,8 +1089,8 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
             for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    t = fmaxf(t, fmaxf(fmaxf(sc[ch][s][ks][0], sc[ch][s][ks][1]),
-                                       fmaxf(sc[ch][s][ks][2], sc[ch][s][ks][3])));
+                    t = smax(t, smax(smax(smax(sc[ch][s][ks][0], sc[ch][s][ks][1]), sc[ch][s][ks][2]),
+                                     sc[ch][s][ks][3]));
             tmax[s] = wave_max_across_groups(t) * score_c;
         }
     };
@@ -1156,10 +1166,10 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
                     if (t < 4 * NS) {
                         const int s = t >> 2, q = t & 3;      // quarter q = (ch, ks) block
                         const f32x4 x = sc[q >> 1][s][q & 1];
-                        part[s][q] = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+                        part[s][q] = smax(smax(smax(x[0], x[1]), x[2]), x[3]);
                     } else {
                         const int s = t - 4 * NS;
-                        const float m4 = fmaxf(fmaxf(part[s][0], part[s][1]), fmaxf(part[s][2], part[s][3]));
+                        const float m4 = smax(smax(smax(part[s][0], part[s][1]), part[s][2]), part[s][3]);
                         tmax[s] = wave_max_across_groups(m4) * score_c;
                     }
                 }
