@@ -79,6 +79,19 @@ def test_random_trials_bf16(seed):
         _run_schedule(shape, calls, seed, policy, check_bytes=(policy == (0, 0)))
 
 
+def test_random_trials_wide():
+    """200 more seeded schedules (shapes, group sizes, head dims 16..128, row
+    mixes), each in float32 and bfloat16 under every kernel selection and the
+    tiny key splits: 2,000 schedules against the oracle in one test (about 20 s)."""
+    for seed in range(16, 216):
+        shape, calls = W.trial_spec(seed, head_dims=(16, 32, 64, 128))
+        for dt in ("f32", "bf16"):
+            sh = W.Shape(shape.name, dt, shape.batch, shape.q_heads, shape.kv_heads, shape.head_dim,
+                         shape.max_len)
+            for policy in POLICIES:
+                _run_schedule(sh, calls, seed, policy, check_bytes=(policy == (0, 0)))
+
+
 @pytest.mark.parametrize("hk,G", [(1, 8), (1, 32), (4, 1), (2, 3)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_mqa_mha_and_odd_groups(hk, G, dtype):
