@@ -108,6 +108,10 @@ int64_t tile_span(int32_t len, int32_t n, int tq, int qt, int32_t window) {
     return hi - range_start(base + t0, window);
 }
 
+// Automatic kernel choice: rows of up to 32 columns (G * n_new, one or two
+// 16-column subtiles) stream faster on the split-K decode kernel; wider rows
+// measured 1.5-1.7x faster on the chunked-prefill kernel (both at 4,096 keys).
+constexpr int64_t kDecodeAutoCols = 32;
 // Decode work groups (kDecodeWaves waves each) the chip runs at once: one per
 // CU. Rows are split across work groups only as far as needed to fill them.
 constexpr int64_t kDecodeSlots = 256;
@@ -118,7 +122,7 @@ constexpr int64_t kPrefillSlots = 256;
 // `lens`: the row lengths the call sees (the host lengths, or those after a
 // fused append)
 void plan_attention(const kv_cache *c, const int32_t *lens, int32_t q_heads, int32_t T, const int32_t *n_new,
-                    Plan &p) {
+                    Plan &p, bool all_decode) {
     const int G = q_heads / c->kv_heads;
     p.group = G;
     std::vector<int> dec_rows, pre_rows;
@@ -130,9 +134,9 @@ void plan_attention(const kv_cache *c, const int32_t *lens, int32_t q_heads, int
             continue;
         }
         bool use_dec;
-        if (c->path_policy == 1) use_dec = G <= 64;
+        if (c->path_policy == 1 || all_decode) use_dec = G <= 64;
         else if (c->path_policy == 2) use_dec = false;
-        else use_dec = (int64_t)G * n <= 64;
+        else use_dec = (int64_t)G * n <= kDecodeAutoCols;
         if (use_dec) {
             dec_rows.push_back(b);
             max_dec_cols = std::max<int>(max_dec_cols, (int)std::min<int64_t>((int64_t)G * n, 64));
@@ -268,6 +272,21 @@ kv_status check_attention_args(const kv_cache *c, const int32_t *lens, int32_t q
     return KV_OK;
 }
 
+// Workspace for a call with these rows: the larger of the automatic plan and
+// the all-decode plan that a tree-verify call makes (the size queries do not
+// know whether the call will pass parents).
+size_t workspace_need(const kv_cache *c, const int32_t *lens, int32_t q_heads, int32_t T, const int32_t *n_new) {
+    Plan p;
+    plan_attention(c, lens, q_heads, T, n_new, p, false);
+    size_t need = workspace_bytes_for(c, p);
+    if ((int64_t)(q_heads / c->kv_heads) * T <= 64) {
+        Plan t;
+        plan_attention(c, lens, q_heads, T, n_new, t, true);
+        need = std::max(need, workspace_bytes_for(c, t));
+    }
+    return need;
+}
+
 void fill_attn_rows(const std::vector<RowPlan> &rows, size_t lo, size_t hi, int hkv, AttnRows &t) {
     std::memset(&t, 0, sizeof t);
     t.n_rows = (int32_t)(hi - lo);
@@ -324,7 +343,8 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
 
 // An attention call's checks and plan, against `lens`, before anything is enqueued.
 kv_status attention_prepare(const kv_cache *c, const int32_t *lens, const void *q, int32_t q_heads, int32_t T,
-                            const int32_t *n_new, void *out, void *workspace, size_t workspace_bytes, Plan &p);
+                            const int32_t *n_new, void *out, void *workspace, size_t workspace_bytes, Plan &p,
+                            bool all_decode);
 // New tokens a decode kernel appends itself (kv_append_attention): read from
 // k_new / v_new [B, Hkv, T, d] and written to the cache by the kernel.
 kv_status check_tree(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new, const int32_t *parents);
@@ -519,9 +539,7 @@ kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32
     kv_status s = check_attention_args(c, c == nullptr ? nullptr : c->lens.data(), q_heads, T, n_new);
     if (s != KV_OK) return s;
     if (c->batch == 0 || T == 0) return ok();
-    Plan p;
-    plan_attention(c, c->lens.data(), q_heads, T, n_new, p);
-    *bytes = workspace_bytes_for(c, p);
+    *bytes = workspace_need(c, c->lens.data(), q_heads, T, n_new);
     return ok();
 }
 
@@ -552,9 +570,7 @@ kv_status kv_append_attention_workspace_size(const kv_cache *c, int32_t q_heads,
     s = check_attention_args(c, after.data(), q_heads, T, n_new);
     if (s != KV_OK) return s;
     if (c->batch == 0 || T == 0) return ok();
-    Plan p;
-    plan_attention(c, after.data(), q_heads, T, n_new, p);
-    *bytes = workspace_bytes_for(c, p);
+    *bytes = workspace_need(c, after.data(), q_heads, T, n_new);
     return ok();
 }
 
@@ -612,7 +628,8 @@ kv_status append_attention_call(kv_cache *c, const void *k_new, const void *v_ne
     std::vector<int32_t> after(c->lens);
     for (int b = 0; b < c->batch; ++b) after[b] += n_new[b];
     Plan p;
-    s = attention_prepare(c, after.data(), q, q_heads, T, n_new, out, workspace, workspace_bytes, p);
+    s = attention_prepare(c, after.data(), q, q_heads, T, n_new, out, workspace, workspace_bytes, p,
+                          parents != nullptr);
     if (s != KV_OK) return s;
     // rows of the decode kernel append themselves; prefill rows go through
     // the copy kernel (appending in the prefill kernel measured slower: it
@@ -736,14 +753,15 @@ kv_status append_commit(kv_cache *c, const void *k_new, const void *v_new, int32
 }
 
 kv_status attention_prepare(const kv_cache *c, const int32_t *lens, const void *q, int32_t q_heads, int32_t T,
-                            const int32_t *n_new, void *out, void *workspace, size_t workspace_bytes, Plan &p) {
+                            const int32_t *n_new, void *out, void *workspace, size_t workspace_bytes, Plan &p,
+                            bool all_decode) {
     kv_status s = check_attention_args(c, lens, q_heads, T, n_new);
     if (s != KV_OK) return s;
     if (c->batch == 0 || T == 0) return KV_OK;           // an empty plan: nothing to launch
     if (q == nullptr || out == nullptr) return fail(KV_ERR_INVALID_ARG, "q/out is null");
     if (!aligned16(q) || !aligned16(out) || !aligned16(workspace))
         return fail(KV_ERR_INVALID_ARG, "q/out/workspace must be 16-byte aligned");
-    plan_attention(c, lens, q_heads, T, n_new, p);
+    plan_attention(c, lens, q_heads, T, n_new, p, all_decode);
     const size_t need = workspace_bytes_for(c, p);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need))
         return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
@@ -756,7 +774,8 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
                          const int32_t *parents, void *out, void *workspace, size_t workspace_bytes,
                          void *stream) {
     Plan p;
-    kv_status s = attention_prepare(c, c->lens.data(), q, q_heads, T, n_new, out, workspace, workspace_bytes, p);
+    kv_status s = attention_prepare(c, c->lens.data(), q, q_heads, T, n_new, out, workspace, workspace_bytes, p,
+                                    parents != nullptr);
     if (s != KV_OK) return s;
     s = attention_launch(c, p, q, q_heads, T, n_new, parents, out, workspace, nullptr, stream);
     return s == KV_OK ? ok() : s;

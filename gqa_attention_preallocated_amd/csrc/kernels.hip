@@ -1420,7 +1420,15 @@ static hipError_t decode_d(int nsub, const AttnArgs &a, hipStream_t s) {
     switch (nsub) {
         case 1: hipLaunchKernelGGL((decode_kernel<E, D, 1, W, F8, PG>), grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL((decode_kernel<E, D, 2, W, F8, PG>), grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<E, D, 4, W, F8, PG>), grid, block, 0, s, a); break;
+        case 4:
+            // four subtiles over rows of 256 bytes or more (in the compute type)
+            // need more registers than two waves per SIMD leave a wave, and
+            // spilled heavily: their work groups are 4 waves at one per SIMD
+            if constexpr (D * sizeof(E) >= 256)
+                hipLaunchKernelGGL((decode_kernel<E, D, 4, 4, F8, PG>), grid, dim3(256), 0, s, a);
+            else
+                hipLaunchKernelGGL((decode_kernel<E, D, 4, W, F8, PG>), grid, block, 0, s, a);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -347,7 +347,7 @@ const char *kv_last_error(void);
 
 /*
  * Kernel selection, for tests and tuning. path: 0 = automatic (rows with
- * G * n_new[b] <= 64 use the split-K decode kernel, the others the tiled
+ * G * n_new[b] <= 32 use the split-K decode kernel, the others the tiled
  * chunked-prefill kernel), 1 = every row through the split-K decode kernel,
  * 2 = every row through the chunked-prefill kernel. keys_per_split: 0 =
  * automatic, otherwise the key range of one split (rounded up to the key

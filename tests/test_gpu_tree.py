@@ -61,10 +61,16 @@ def test_tree_verify(dt, d, name):
 
 
 def test_chain_gives_the_bits_of_plain_attention():
+    """A chain (each node's parent the node before it) is the causal rule, so
+    the tree call gives the bits of plain attention on the same kernel. Tree
+    verify always runs on the split-K decode kernel; the plain call here has
+    48 columns a row, which the automatic plan would give to the prefill
+    kernel, so the cache is set to the decode kernel for both calls."""
     KVCache, gqa_attention = _lib()
     B, hk, G, d, T = 4, 8, 4, 128, 12
     shape = W.Shape("chain", "bf16", B, hk * G, hk, d, 2048)
     cache = KVCache(B, hk, 2048, d)
+    cache.set_policy(1, 0)
     _, k, v = W.step_inputs(shape, 5, 0, 1500, [1500, 900, 1200, 64], pad="normal")
     cache.append(to_dev(k, "bf16"), to_dev(v, "bf16"), [1500, 900, 1200, 64])
     q, k, v = W.step_inputs(shape, 5, 1, T, [T] * B, pad="normal")
