@@ -215,7 +215,9 @@ kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T
 /*
  * Workspace that gqa_attention needs for this call (split-K partial results),
  * in bytes, written to *bytes. Depends on the current lengths and n_new.
- * Zero means no workspace is needed.
+ * Zero means no workspace is needed. The figure also covers the tree-verify
+ * variants of the call (gqa_attention_tree, which keeps every row on the
+ * split-K decode kernel), so one size serves both.
  */
 kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32_t T,
                                        const int32_t *n_new, size_t *bytes);
@@ -310,7 +312,8 @@ kv_status kv_append_attention_tree(kv_cache *c, const void *k_new, const void *v
 
 /*
  * Workspace kv_append_attention needs for these arguments (the
- * gqa_attention workspace for the lengths after the append), in bytes.
+ * gqa_attention workspace for the lengths after the append), in bytes; it
+ * also covers kv_append_attention_tree.
  */
 kv_status kv_append_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32_t T,
                                              const int32_t *n_new, size_t *bytes);
