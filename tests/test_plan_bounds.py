@@ -571,3 +571,30 @@ def test_append_attention_tree(sim):
     c.lens += np.asarray(n)
     c.appended += int(np.sum(n)) * c.hk * c.d * c.elem // 16
     c.check(T)
+
+
+def test_append_attention_tree_wide_rows(sim):
+    """A tree call with 48 columns a row (G=4, T=12). The automatic plan gives
+    rows that wide to the prefill kernel; a tree call keeps them on the split-K
+    decode kernel, and the workspace query covers that plan: the call succeeds
+    with exactly the queried bytes and writes every new token once. At 24 rows
+    x 8 KV heads (192 items) the prefill plan needs no split, and with it no
+    workspace, while the decode plan splits each row in two."""
+    B, hk, hq, d, T = 24, 8, 32, 128, 12
+    c = SimCache(sim, B, hk, 8192, d, "bf16", hq, 4096)
+    for call in _prefix_calls([4092] * B):
+        c.append(call["T"], call["n_new"])
+    n = [T] * (B - 1) + [7]
+    parents = list(range(-1, T - 1)) * B
+    size = ctypes.c_size_t()
+    assert sim.kv_append_attention_workspace_size(c.h, hq, T, _i32(n), ctypes.byref(size)) == 0
+    assert size.value > 0                       # split-K partials of the decode plan
+    a = c.addr
+    sim.hostcheck_begin_call()
+    st = sim.kv_append_attention_tree(c.h, ctypes.c_void_p(a["k_new"]), ctypes.c_void_p(a["v_new"]),
+                                      ctypes.c_void_p(a["q"]), hq, T, _i32(n), _i32(parents),
+                                      ctypes.c_void_p(a["out"]), ctypes.c_void_p(a["ws"]), size.value, None)
+    assert st == 0, sim.kv_last_error()
+    c.lens += np.asarray(n)
+    c.appended += int(np.sum(n)) * c.hk * c.d * c.elem // 16
+    c.check(T)
