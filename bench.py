@@ -150,11 +150,18 @@ def run_decode(torch, steps, warmup):
         walls[name] = (time.perf_counter() - t0) / steps
 
     # the step's kernel alone: back-to-back launches (alternating caches)
-    # between two HIP events on the stream the library launches on; the
-    # average launch duration includes no event or host gaps
-    reps = max(steps, 20)
+    # between two HIP events on the stream the library launches on (torch's
+    # current stream, which the binding passes to every call). Like the wall
+    # loop it starts behind a device spin and untimed warm-up steps, and it
+    # times at least ROOFLINE_REPS launches whatever --steps is, so the host
+    # has enqueued the launches before the GPU reaches them and the average
+    # holds no first-launch or enqueue gap.
+    reps = max(steps, ROOFLINE_REPS)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    torch.cuda._sleep(20_000_000)
+    for i in range(max(warmup, ROOFLINE_WARMUP)):
+        step(i)
     e0.record()
     for i in range(reps):
         step(i)
@@ -195,7 +202,7 @@ def run_prefill(torch, reps=3):
     n = [512] * B
     chunks = []
     for c in range(20):
-        q, k, v = W.step_inputs(sh, 3, c, 512, n, pad="normal")
+        q, k, v = W.step_inputs(sh, PREFILL_SEED, c, 512, n, pad="normal")
         chunks.append((dev_bf16(torch, q), dev_bf16(torch, k), dev_bf16(torch, v)))
     out = torch.empty_like(chunks[0][0])
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
@@ -604,6 +611,12 @@ def run_probe(torch, reps=10):
 
 
 DECODE_SEED, DECODE_CACHED = 1, 4096
+# the event-timed roofline loop: untimed warm-up steps and timed launches, at
+# least these many whatever --steps and --warmup are
+ROOFLINE_WARMUP, ROOFLINE_REPS = 200, 400
+# chunked-prefill oracle baseline: the chunk in the middle of the 10,240-token
+# prompt (keys 0 .. 5,631), prompt seed as in run_prefill
+PREFILL_SEED, PREFILL_CPU_CHUNK = 3, 10
 
 
 def _oracle_worker(rank, nproc, reps, budget_s, barrier, results):
@@ -643,6 +656,80 @@ def _oracle_worker(rank, nproc, reps, budget_s, barrier, results):
         break
     t1 = time.perf_counter()
     results.put((rank, done, t0, t1))
+
+
+def _oracle_prefill_worker(rank, nproc, budget_s, barrier, results):
+    """One host process of the chunked-prefill CPU baseline: regenerate the
+    prompt up to chunk PREFILL_CPU_CHUNK, then run the float64 oracle over
+    (row, query) units of that chunk (all 32 heads each), units dealt
+    round-robin over the processes in a strided order over the chunk's
+    queries, until budget_s of compute has passed (checked after each unit)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except ImportError:       # pragma: no cover
+        pass
+    import workloads as W
+    from oracle import direct
+    sh = W.LLAMA8B_CHUNKED_PREFILL
+    c = PREFILL_CPU_CHUNK
+    n = [512] * sh.batch
+    ks, vs = [], []
+    for i in range(c + 1):
+        q, k, v = W.step_inputs(sh, PREFILL_SEED, i, 512, n, pad="normal")
+        ks.append(k)
+        vs.append(v)
+    L = 512 * (c + 1)
+    kr = np.concatenate(ks, axis=2)                    # [B, Hkv, L, d]
+    vr = np.concatenate(vs, axis=2)
+    # units (b, t): t in a stride-67 order over the chunk so every worker's
+    # sample spreads over early and late queries
+    units = [(b, (67 * j) % 512) for j in range(512) for b in range(sh.batch)][rank::nproc]
+    heads = range(sh.q_heads)
+    direct.attention_row(kr[0], vr[0], L, 512, q[0], "bf16", [(0, 0)])     # one-off set-up, untimed
+    barrier.wait()
+    t0 = time.perf_counter()
+    done, flop = 0, 0
+    for b, t in units:
+        direct.attention_row(kr[b], vr[b], L, 512, q[b], "bf16", [(h, t) for h in heads])
+        done += 1
+        flop += 4 * sh.head_dim * sh.q_heads * (L - 512 + t + 1)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t1 = time.perf_counter()
+    results.put((rank, done, t0, t1, flop))
+
+
+def cpu_baseline_prefill(budget_s=1.5, max_procs=16):
+    """The float64 oracle on the host over a sample of the chunked-prefill
+    workload: (row, query) units of the middle chunk of the 10,240-token
+    prompt, every head, over one single-threaded process per host core (at
+    most max_procs). Reported in GFLOP/s of the same algorithmic count (4 d
+    FLOP per visible pair and head)."""
+    import multiprocessing as mp
+    import workloads as W
+    sh = W.LLAMA8B_CHUNKED_PREFILL
+    nproc = max(1, min(max_procs, len(os.sched_getaffinity(0))))
+    ctx = mp.get_context("spawn")
+    barrier, results = ctx.Barrier(nproc), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_prefill_worker, args=(r, nproc, budget_s, barrier, results))
+             for r in range(nproc)]
+    for pr in procs:
+        pr.start()
+    got = [results.get(timeout=600) for _ in procs]
+    for pr in procs:
+        pr.join()
+    units = sum(g[1] for g in got)
+    flop = sum(g[4] for g in got)
+    wall = max(g[3] for g in got) - min(g[2] for g in got)
+    cpu_s = sum(g[3] - g[2] for g in got)
+    total = sh.batch * 512
+    return {"value": round(flop / wall / 1e9, 4), "unit": "GFLOP/s", "cores": nproc, "kind": "oracle",
+            "sample": f"{units} of the {total} (row, query) units of chunk {PREFILL_CPU_CHUNK} "
+                      f"(keys 0..{512 * (PREFILL_CPU_CHUNK + 1) - 1}) of the 10,240-token prompt "
+                      f"({units / total:.1%}), each over all 32 heads; {flop / 1e9:.1f} GFLOP, "
+                      f"{cpu_s:.1f} s of CPU over {nproc} single-threaded processes, {wall:.2f} s wall, "
+                      f"float64 numpy"}
 
 
 def cpu_baseline(reps=20, budget_s=1.5, max_procs=16):
@@ -714,12 +801,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.only == "cpu":
-        print(json.dumps({"cpu_baseline": cpu_baseline()}), flush=True)
+        print(json.dumps({"cpu_baseline": cpu_baseline(), "prefill_cpu_baseline": cpu_baseline_prefill()}),
+              flush=True)
         return
     # the CPU baseline runs first, while no GPU context exists in this process
-    cpu = None
+    cpu = cpu_pre = None
     if not args.no_cpu_baseline and args.only is None:
         cpu = cpu_baseline()
+        if not args.no_prefill:
+            cpu_pre = cpu_baseline_prefill()
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -776,6 +866,8 @@ def main():
     }
     if not args.no_prefill:
         line["prefill"] = run_prefill(torch)
+        if cpu_pre is not None:
+            line["prefill"]["cpu_baseline"] = cpu_pre
         probe = run_probe(torch)
         if probe is not None:
             probe["decode_kernel_frac"] = round(achieved / probe["nontemporal_GB/s"], 4)

@@ -95,13 +95,15 @@ class KVCache:
                 raise ValueError("max_len must be a multiple of page_size")
             pool = (int(num_pages), kv_heads, int(page_size), head_dim)
             self.page_size, self.num_pages, self.max_blocks = int(page_size), int(num_pages), max_len // page_size
-            self.k = torch.zeros(pool, dtype=dtype, device=device)
-            self.v = torch.zeros(pool, dtype=dtype, device=device)
+            # kv_cache_create_paged sets the pool to zero on the current stream
+            self.k = torch.empty(pool, dtype=dtype, device=device)
+            self.v = torch.empty(pool, dtype=dtype, device=device)
             self.block_table_dev = torch.empty((max(batch, 1), self.max_blocks), dtype=torch.int32, device=device)
         else:
             store = torch.uint8 if fp8_scales is not None else dtype
-            self.k = torch.zeros(shape, dtype=store, device=device)
-            self.v = torch.zeros(shape, dtype=store, device=device)
+            # kv_cache_create* sets K and V to zero on the current stream
+            self.k = torch.empty(shape, dtype=store, device=device)
+            self.v = torch.empty(shape, dtype=store, device=device)
         self.lens_dev = torch.zeros(max(batch, 1), dtype=torch.int32, device=device) if device_lens else None
         self.dtype = dtype
         self._device = self.k.device

@@ -43,7 +43,12 @@ def load():
             f"{LIB_PATH} is missing: build it with `python -m gqa_attention_preallocated_amd.build` "
             "(hipcc, gfx950). There is no CPU fallback.")
     import torch  # noqa: F401  (loads the HIP runtime torch was built with)
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = configure(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def configure(lib):
+    """Declare the C signatures of include/gqa_kv.h on a loaded library; returns it."""
     P = ctypes.c_void_p
     I32 = ctypes.c_int32
     I32P = ctypes.POINTER(ctypes.c_int32)
@@ -62,7 +67,7 @@ def load():
     lib.kv_free_pages.argtypes = [P]
     lib.kv_free_pages.restype = I32
     lib.kv_cache_destroy.argtypes = [P]
-    lib.kv_cache_destroy.restype = None
+    lib.kv_cache_destroy.restype = ctypes.c_int
     lib.kv_append.argtypes = [P, P, P, I32, I32P, P]
     lib.kv_append.restype = ctypes.c_int
     lib.gqa_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]
@@ -89,7 +94,6 @@ def load():
     lib.kv_last_error.restype = ctypes.c_char_p
     lib.kv_cache_set_policy.argtypes = [P, I32, I32]
     lib.kv_cache_set_policy.restype = ctypes.c_int
-    _lib = lib
     return lib
 
 

@@ -119,6 +119,17 @@ constexpr int64_t kDecodeSlots = 256;
 // (8 waves, or 4 at one wave per SIMD; prefill_waves).
 constexpr int64_t kPrefillSlots = 256;
 
+// A split length fixed by the policy: keys_per_split rounded up to the key
+// tile, but never past the row's own key range rounded up to the tile (one
+// split then covers the row), so every row gets at least one split. Computed
+// in 64 bits: a policy near INT32_MAX must not wrap.
+void fixed_split(int64_t keys_per_split, int64_t span, int tile, RowPlan &r) {
+    const int64_t whole = std::max<int64_t>(tile, ceil_div(span, tile) * tile);
+    const int64_t ls = std::min(whole, ceil_div(keys_per_split, tile) * tile);
+    r.lsplit = (int32_t)ls;
+    r.nsplit = (int32_t)std::max<int64_t>(1, ceil_div(span, ls));
+}
+
 // `lens`: the row lengths the call sees (the host lengths, or those after a
 // fused append)
 void plan_attention(const kv_cache *c, const int32_t *lens, int32_t q_heads, int32_t T, const int32_t *n_new,
@@ -171,8 +182,7 @@ void plan_attention(const kv_cache *c, const int32_t *lens, int32_t q_heads, int
             for (int qt = 0; qt < r.nq; ++qt) span = std::max(span, tile_span(r.len, r.nnew, tq, qt, c->window));
             const int64_t tiles = ceil_div(span, kDecodeKeyTile);
             if (c->keys_per_split > 0) {
-                r.lsplit = (int)(ceil_div(c->keys_per_split, kDecodeKeyTile) * kDecodeKeyTile);
-                r.nsplit = (int)ceil_div(span, r.lsplit);
+                fixed_split(c->keys_per_split, span, kDecodeKeyTile, r);
             } else {
                 r.nsplit = (int)ceil_div(tiles, tpw);
                 r.lsplit = (int)(ceil_div(tiles, r.nsplit) * kDecodeKeyTile);
@@ -203,8 +213,7 @@ void plan_attention(const kv_cache *c, const int32_t *lens, int32_t q_heads, int
             for (int qt = 0; qt < r.nq; ++qt) span = std::max(span, tile_span(r.len, r.nnew, tq, qt, c->window));
             const int64_t tiles = ceil_div(span, kPrefillKeyTile);
             if (c->keys_per_split > 0) {
-                r.lsplit = (int)(ceil_div(c->keys_per_split, kPrefillKeyTile) * kPrefillKeyTile);
-                r.nsplit = (int)ceil_div(span, r.lsplit);
+                fixed_split(c->keys_per_split, span, kPrefillKeyTile, r);
             } else {
                 r.nsplit = 2 * tiles > 3 * cap ? (int)ceil_div(tiles, cap) : 1;
                 r.lsplit = (int)(ceil_div(tiles, r.nsplit) * kPrefillKeyTile);
@@ -495,6 +504,20 @@ kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t
             return device_fail(e, "kv_cache_create_paged");
         }
     }
+    // the reservation starts as zeros ([GQA] "A strong answer" and [CH16]
+    // "Layout and validity" both build the cache from zeros), so every byte
+    // past a row's length is defined from the start
+    if (batch > 0) {
+        const int64_t bytes = pg != nullptr
+            ? (int64_t)pg->num_pages * kv_heads * pg->page_size * head_dim * c->elem_bytes
+            : (int64_t)batch * kv_heads * max_len * head_dim * c->elem_bytes;
+        hipError_t e = launch_zero_bytes(k_buf, bytes, (hipStream_t)stream);
+        if (e == hipSuccess) e = launch_zero_bytes(v_buf, bytes, (hipStream_t)stream);
+        if (e != hipSuccess) {
+            delete c;
+            return device_fail(e, "kv_cache_create (zero fill)");
+        }
+    }
     if (lens_dev != nullptr) {
         for (int lo = 0; lo < batch; lo += kMaxRows) {
             LensTable t{};
@@ -517,10 +540,11 @@ kv_status create_cache(int32_t batch, int32_t kv_heads, int32_t max_len, int32_t
 
 extern "C" {
 
-void kv_cache_destroy(kv_cache *c) {
-    if (c == nullptr) return;
+kv_status kv_cache_destroy(kv_cache *c) {
+    if (c == nullptr) return ok();
     side_stream_destroy(c->side);
     delete c;
+    return ok();
 }
 
 kv_status kv_append(kv_cache *c, const void *k_new, const void *v_new, int32_t T, const int32_t *n_new,
@@ -767,6 +791,14 @@ kv_status attention_prepare(const kv_cache *c, const int32_t *lens, const void *
         return fail(KV_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
     if (p.records > INT32_MAX / 2)
         return fail(KV_ERR_UNSUPPORTED, "too many split partials");
+    // each launch's work items must fit one grid dimension
+    for (const std::vector<RowPlan> *rows : {&p.dec, &p.pre})
+        for (size_t lo = 0; lo < rows->size(); lo += kMaxRows) {
+            int64_t items = 0;
+            for (size_t i = lo; i < std::min(rows->size(), lo + kMaxRows); ++i)
+                items += (int64_t)c->kv_heads * (*rows)[i].nq * (*rows)[i].nsplit;
+            if (items > INT32_MAX) return fail(KV_ERR_UNSUPPORTED, "too many work items in one launch");
+        }
     return KV_OK;
 }
 

@@ -148,6 +148,9 @@ hipError_t launch_append(const AppendArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t s);
 hipError_t launch_table_set(const TableArgs &a, hipStream_t s);
 hipError_t launch_table_fill(int32_t *table, int64_t n, int32_t value, hipStream_t s);
+// +0 into `bytes` bytes from p (16-byte aligned, a multiple of 16 bytes): the
+// cache buffers at creation
+hipError_t launch_zero_bytes(void *p, int64_t bytes, hipStream_t s);
 // nsub: 16-column subtiles per decode work item (1, 2 or 4); a.table selects
 // the paged kernels (float32 and bfloat16 caches)
 hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, hipStream_t s);

@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "indexing.h"
@@ -413,6 +414,13 @@ __global__ __launch_bounds__(256) void table_set_kernel(TableArgs a) {
 __global__ __launch_bounds__(256) void table_fill_kernel(int32_t *table, int64_t n, int32_t value) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) table[i] = value;
+}
+
+// zero K and V at creation: 16-byte stores over a grid-stride loop (a kernel,
+// not a memset, so a captured graph holds no memset node)
+__global__ __launch_bounds__(256) void zero_bytes_kernel(uint4 *p, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1409,6 +1417,15 @@ hipError_t launch_table_set(const TableArgs &a, hipStream_t s) {
 hipError_t launch_table_fill(int32_t *table, int64_t n, int32_t value, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(table_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, table, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_bytes(void *p, int64_t bytes, hipStream_t s) {
+    const int64_t n16 = bytes / 16;
+    if (n16 <= 0) return hipSuccess;
+    // at most 8,192 blocks of 256 threads; each thread stores 16 bytes per pass
+    const int64_t blocks = std::min<int64_t>(8192, (n16 + 255) / 256);
+    hipLaunchKernelGGL(zero_bytes_kernel, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<uint4 *>(p), n16);
     return hipGetLastError();
 }
 

@@ -81,9 +81,11 @@ typedef enum kv_dtype {
  * Wrap caller-allocated cache buffers in a handle.
  * [GQA] "A strong answer" (the cache is allocated once as [B, Hkv, max_len, d]
  * plus a length per row); [CH16] "Layout and validity" (capacity vs length).
- *   k_buf, v_buf  device, B*Hkv*max_len*d elements each. Their contents are
- *                 never read outside a row's valid prefix; the caller should
- *                 zero-fill them if it wants bit-defined tails.
+ *   k_buf, v_buf  device, B*Hkv*max_len*d elements each, set to zero here
+ *                 on `stream` by a fill kernel ([GQA] "A strong answer" and
+ *                 [CH16] "Layout and validity" build the cache from zeros), so
+ *                 every byte past a row's length is defined. Bytes outside a
+ *                 row's valid prefix are never read by attention.
  *   lens_dev      optional device int32[B] that the library keeps equal to the
  *                 per-row lengths in stream order (append, truncate). May be NULL.
  *                 When given, it is set to zero on `stream` here.
@@ -99,9 +101,10 @@ kv_status kv_cache_create(int32_t batch, int32_t kv_heads, int32_t max_len, int3
 /*
  * Sliding-window cache: wrap caller-allocated buffers as a ring of `capacity`
  * slots per row, keeping only the latest tokens, with attention limited to a
- * window. [MASK] "A strong answer" (the reversal: with a window W the mask
- * gains the lower bound j > (S - T) + i - W, and in a ring buffer the
- * comparison uses the tokens' absolute positions, not slot indices) and
+ * window. [MASK] "A strong answer", the reversal paragraph (a window adds a
+ * lower limit on the visible keys, and once tokens sit in ring slots the
+ * visibility test has to compare positions, since a slot number no longer
+ * says where a token came in) and
  * [CH16] exercise 3 (a cache that keeps only the last positions in a ring).
  *   capacity      slots per row, a positive multiple of 64; k_buf and v_buf
  *                 hold B*Hkv*capacity*d elements each, laid out as
@@ -151,8 +154,9 @@ kv_status kv_cache_create_fp8(int32_t batch, int32_t kv_heads, int32_t max_len, 
  * table per row that maps the row's logical blocks to pages, so memory is held
  * in proportion to the tokens stored instead of max_len per row. [GQA] "A
  * strong answer" (preallocating max_len per row is the waste a paged cache
- * removes) and the reversal (rows of wildly different lengths call for a block
- * table and a paged kernel); [CH16] "16. Prefill, decode and the KV cache",
+ * removes) and its reversal paragraph (rows whose lengths differ by orders of
+ * magnitude leave most of a dense reservation empty; a per-row page table
+ * and a kernel that follows it fix that); [CH16] "16. Prefill, decode and the KV cache",
  * design choices (a paged cache keeps the in-place O(1) write without
  * reserving the maximum up front).
  *   num_pages     pages in the pool; k_pool and v_pool are device arrays of
@@ -191,8 +195,12 @@ kv_status kv_get_block_table(const kv_cache *c, int32_t *table_host);
 /* Pages of a paged cache's pool that hold no token (0 for other caches). */
 int32_t kv_free_pages(const kv_cache *c);
 
-/* Release the handle (never the caller's buffers). NULL is ignored. */
-void kv_cache_destroy(kv_cache *c);
+/*
+ * Release the handle (never the caller's buffers); KV_OK, also for NULL. Work
+ * already enqueued on the caller's streams is not waited for: the buffers must
+ * outlive it.
+ */
+kv_status kv_cache_destroy(kv_cache *c);
 
 /*
  * Append in place: for each row b, write k_new[b,:,0:n_new[b]] and
@@ -258,9 +266,10 @@ kv_status gqa_attention(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
 /*
  * Tree-based speculative verify: as gqa_attention, but the n_new[b] tokens just
  * appended to row b are the nodes of a draft tree rather than a chain. [MASK]
- * "What interviewers probe next": each draft token attends the full cache plus
- * its own ancestors, so the T x T corner of the mask becomes an ancestor mask
- * built from parent pointers.
+ * "What interviewers probe next": with a tree-shaped draft, the block of the
+ * mask among the new tokens follows the tree (a node sees the committed keys,
+ * itself and the nodes on its path to the root, given by parent pointers)
+ * instead of a triangle.
  *   parents       HOST int32[B * T]; parents[b * T + u] for u < n_new[b] is -1
  *                 (node u follows the committed prefix) or the index of an
  *                 earlier node (0 <= parent < u). Entries for u >= n_new[b]

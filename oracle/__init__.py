@@ -11,9 +11,10 @@ check it against the pages by eye:
   * ``direct``     -- the cache (append / truncate / reset / bytes) and the
                       "direct reference" attention: KV heads repeated, a loop
                       over every query, a plain softmax over keys 0..pos.
-  * ``vectorised`` -- a second, independently written formulation (grouped
-                      reshape, an index-arithmetic mask, guarded softmax),
-                      used to cross-check ``direct``.
+  * ``vectorised`` -- a second formulation, per (row, KV head) block over
+                      the row's own prefix, with the bottom-right triangle
+                      as the mask and a log-sum-exp normalisation, used to
+                      cross-check ``direct``.
   * ``window``     -- sliding-window attention over a ring-buffer cache whose
                       slots store the absolute positions they hold.
   * ``fp8``        -- an E4M3 cache with one scale per KV head: the format's

@@ -6,8 +6,9 @@ TEST INFRASTRUCTURE (see the package docstring): imported only by tests/ and
 Sources: [GQA] "Implement grouped-query attention over a preallocated KV cache,
 with no torch.cat, for both prefill chunks and decode" (inferenceinterviews.com),
 "A strong answer" (reserving max_len per row is the waste paged caches remove)
-and the reversal (rows of wildly different lengths: move to a block table and a
-paged kernel); [CH16] "16. Prefill, decode and the KV cache", design choices
+and its reversal paragraph (when row lengths differ by orders of magnitude, the
+dense reservation mostly holds nothing, and a per-row table of pages read by
+a page-aware kernel is the better layout); [CH16] "16. Prefill, decode and the KV cache", design choices
 (a paged cache keeps the O(1) write without reserving the maximum up front).
 
 Readings taken where the pages are silent (each listed in the design notes):

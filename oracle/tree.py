@@ -5,10 +5,10 @@ TEST INFRASTRUCTURE (see the package docstring): imported only by tests/ and
 
 Source: [MASK] "Write the causal mask for a decode step with a KV cache, where
 the query is shorter than the keys" (inferenceinterviews.com), "What
-interviewers probe next": with tree-based speculative decoding the draft tokens
-are not a chain, each one attends to the full cache plus its own ancestors in
-the tree, and the T by T corner of the mask becomes an ancestor mask built from
-parent pointers.
+interviewers probe next". When the draft is a tree rather than a chain, the
+new tokens' block of the mask is no longer triangular: a draft token sees
+every committed key, and among the new tokens only those on its own path to
+the root, which parent pointers describe.
 
 Readings taken where the page is silent (each listed in the design notes):
   * The n_new[b] tree nodes of row b are the tokens just appended, in node

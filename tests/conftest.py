@@ -1,4 +1,6 @@
+import ctypes
 import os
+import subprocess
 import sys
 
 import pytest
@@ -35,3 +37,32 @@ def read_golden_rows(name):
             if line:
                 rows.append([int(x) for x in line.split()])
     return rows
+
+
+# --------------------------------------------------------------------------
+# The library's host code (tests/hostcheck): abi.cpp linked against a CPU
+# simulator of the kernel launchers instead of the HIP kernels, so every call
+# can run without a GPU. With GQAKV_HOSTCHECK_SANITIZE=1 in the environment
+# (set by the sanitizer test, which also preloads the ASan runtime) it is
+# built with AddressSanitizer and UndefinedBehaviorSanitizer.
+# --------------------------------------------------------------------------
+
+CSRC = os.path.join(ROOT, "gqa_attention_preallocated_amd", "csrc")
+SANITIZE = os.environ.get("GQAKV_HOSTCHECK_SANITIZE") == "1"
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+
+
+def build_hostcheck(out):
+    """Compile abi.cpp + the launch simulator with g++ into `out` (host code only)."""
+    flags = ["-O1", "-g"] + (SANITIZE_FLAGS if SANITIZE else [])
+    cmd = ["g++", *flags, "-std=c++17", "-shared", "-fPIC", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "abi.cpp"), os.path.join(ROOT, "tests", "hostcheck", "launch_sim.cpp"),
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return ctypes.CDLL(str(out))
+
+
+@pytest.fixture(scope="session")
+def hostcheck_lib(tmp_path_factory):
+    return build_hostcheck(tmp_path_factory.mktemp("hostcheck") / "libhostcheck.so")

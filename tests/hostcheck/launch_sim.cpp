@@ -181,6 +181,18 @@ hipError_t launch_table_fill(int32_t *table, int64_t n, int32_t value, hipStream
     return hipSuccess;
 }
 
+hipError_t launch_zero_bytes(void *p, int64_t bytes, hipStream_t) {
+    ++g_launches;
+    if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(p) & 15) != 0) err("zero bytes: not 16-byte granular");
+    // the whole range must be one buffer: K or V
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    bool inside = false;
+    for (const Region &r : g_regions)
+        if (a >= r.base && a + (uintptr_t)bytes <= r.base + r.size && (r.name == "k" || r.name == "v")) inside = true;
+    if (bytes > 0 && !inside) err("zero bytes: range is not inside K or V");
+    return hipSuccess;
+}
+
 hipError_t launch_table_set(const TableArgs &a, hipStream_t) {
     ++g_launches;
     if (a.n <= 0 || a.n > kMaxTableUpdates) err("table set: bad update count");

@@ -1,7 +1,10 @@
 """The C-ABI library loads and exports every entry point include/gqa_kv.h declares,
-and its host-side validation behaves as documented (no device work is needed
-for any call here: every call either fails validation before enqueuing or
-enqueues nothing)."""
+and its host-side validation behaves as documented.
+
+Calls that fail validation enqueue nothing, so they run on the built library
+itself. Calls that succeed enqueue kernels (creation zero-fills K and V), so
+they run on the same host code (abi.cpp) linked against the CPU launch
+simulator instead of the kernels (the ``hostcheck_lib`` fixture)."""
 
 import ctypes
 import os
@@ -38,6 +41,12 @@ def test_every_declared_symbol_is_exported(lib):
     assert sorted(_lib.EXPORTED) == _declared()
 
 
+@pytest.fixture(scope="module")
+def host(hostcheck_lib):
+    from gqa_attention_preallocated_amd import _lib
+    return _lib.configure(hostcheck_lib)
+
+
 def _fake_cache(lib, B=2, hk=2, max_len=64, d=16, dtype=0):
     h = ctypes.c_void_p()
     st = lib.kv_cache_create(B, hk, max_len, d, dtype, ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20), None,
@@ -67,7 +76,8 @@ def test_create_validation(lib):
                                None, ctypes.byref(h)) == 1
 
 
-def test_capacity_error_text_and_nothing_changes(lib):
+def test_capacity_error_text_and_nothing_changes(host):
+    lib = host
     h = _fake_cache(lib)
     st = lib.kv_append(h, ctypes.c_void_p(3 << 20), ctypes.c_void_p(4 << 20), 80, _arr([3, 70]), None)
     assert st == 2
@@ -80,7 +90,8 @@ def test_capacity_error_text_and_nothing_changes(lib):
     lib.kv_cache_destroy(h)
 
 
-def test_attention_argument_checks(lib):
+def test_attention_argument_checks(host):
+    lib = host
     h = _fake_cache(lib)
     size = ctypes.c_size_t()
     assert lib.gqa_attention_workspace_size(h, 3, 4, _arr([0, 0]), ctypes.byref(size)) == 1   # Hq % Hkv
@@ -91,7 +102,8 @@ def test_attention_argument_checks(lib):
     lib.kv_cache_destroy(h)
 
 
-def test_truncate_rules_and_bytes(lib):
+def test_truncate_rules_and_bytes(host):
+    lib = host
     h = _fake_cache(lib, B=2, hk=2, max_len=64, d=16, dtype=1)
     assert lib.kv_cache_bytes(h) == 2 * 2 * 2 * 64 * 16 * 2
     assert lib.kv_live_bytes(h) == 0
@@ -103,7 +115,7 @@ def test_truncate_rules_and_bytes(lib):
     lib.kv_cache_destroy(h)
 
 
-def test_paged_create_validation(lib):
+def test_paged_create_validation(lib, host):
     """kv_cache_create_paged refuses bad pool geometry and E4M3 storage before
     enqueueing anything; the block-table query refuses a linear cache."""
     h = ctypes.c_void_p()
@@ -122,10 +134,11 @@ def test_paged_create_validation(lib):
     st = lib.kv_cache_create_paged(2, 2, 8, 64, 4, 64, 1, a, a, ctypes.c_void_p((3 << 20) + 4), None, None,
                                    ctypes.byref(h))
     assert st == 1                  # misaligned block table
-    lin = _fake_cache(lib)
-    assert lib.kv_get_block_table(lin, _arr([0] * 8)) == 1
-    assert lib.kv_free_pages(lin) == 0
-    lib.kv_cache_destroy(lin)
+    lin = _fake_cache(host)
+    assert host.kv_get_block_table(lin, _arr([0] * 8)) == 1
+    assert host.kv_free_pages(lin) == 0
+    assert host.kv_cache_destroy(lin) == 0
+    assert host.kv_cache_destroy(None) == 0
 
 
 def test_python_layer_refuses_without_gpu_buffers():

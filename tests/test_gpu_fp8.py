@@ -100,11 +100,15 @@ def test_llama_fp8_decode():
 
 def test_fp8_error_against_a_bf16_cache():
     """[CH16] exercise 4 measures the error of the FP8 cache against a bfloat16
-    one over many decode steps. Here: 200 decode steps of one Llama-shaped row
-    set (B=4), the attention outputs of the two caches compared each step; the
-    worst relative error stays within what 3 mantissa bits allow."""
+    one over 1,000 decode steps. Here: 1,000 decode steps of a Llama-shaped
+    row set (B=4, from 512 to 1,512 cached tokens), the attention outputs of
+    the two caches compared at every step. With no model there are no logits:
+    the error is taken on the attention output, relative to its largest
+    value. E4M3 keeps 3 mantissa bits (a code is within 2^-4 of its value),
+    but each output averages thousands of keys, so the measured worst is
+    about 3%; the gate is about twice that."""
     KVCache, gqa_attention = _lib()
-    B, hk, G, d, S = 4, 8, 4, 128, 1024
+    B, hk, G, d, S = 4, 8, 4, 128, 2048
     shape = W.Shape("fp8err", "bf16", B, hk * G, hk, d, S, value_scale=1.0 / np.sqrt(128.0))
     sc = [2.0 ** -9] * hk
     c8 = KVCache(B, hk, S, d, fp8_scales=(sc, sc))
@@ -112,13 +116,17 @@ def test_fp8_error_against_a_bf16_cache():
     q, k, v = W.step_inputs(shape, 6, 0, 512, [512] * B, pad="normal")
     for c in (c8, c16):
         c.append(to_dev(k, "bf16"), to_dev(v, "bf16"), [512] * B)
-    worst = 0.0
-    for step in range(1, 201):
+    worst, total = 0.0, 0.0
+    steps = 1000
+    for step in range(1, steps + 1):
         q, k, v = W.step_inputs(shape, 6, step, 1, [1] * B, pad="normal")
         outs = []
         for c in (c8, c16):
             c.append(to_dev(k, "bf16"), to_dev(v, "bf16"), [1] * B)
             outs.append(out_f64(gqa_attention(to_dev(q, "bf16"), c, [1] * B), "bf16"))
-        worst = max(worst, float(np.abs(outs[0] - outs[1]).max() / np.abs(outs[1]).max()))
-    assert worst < 0.15, worst
-    print(f"fp8 vs bf16 cache, 200 decode steps: worst relative error {worst:.4f}")
+        rel = float(np.abs(outs[0] - outs[1]).max() / np.abs(outs[1]).max())
+        worst = max(worst, rel)
+        total += rel
+    print(f"fp8 vs bf16 cache, {steps} decode steps: worst relative error {worst:.4f}, "
+          f"mean {total / steps:.4f}")
+    assert worst < 0.065, worst

@@ -7,7 +7,8 @@ oracle's page assignment), every page's bytes after every append, outputs
 within the contract tolerances, and, against the linear cache on the same
 inputs, the same output bits. [GQA] "Implement grouped-query attention over a
 preallocated KV cache, with no torch.cat, for both prefill chunks and decode",
-the reversal (a block table and a paged kernel for wildly ragged rows).
+the reversal paragraph (a page table per row for rows of very different
+lengths).
 """
 
 import numpy as np

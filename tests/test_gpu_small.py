@@ -280,3 +280,43 @@ def test_bytes_accounting():
     _, k, v = W.step_inputs(shape, 0, 0, 16, [16] * 32, pad="normal")
     cache.append(to_dev(k, "bf16"), to_dev(v, "bf16"), [16] * 32)
     assert cache.live_bytes == direct.kv_cache_bytes(1, 32, 16, 8, 128, 2)
+
+
+def test_create_zero_fills_every_cache_kind():
+    """kv_cache_create* set K, V (a paged cache: the pool) and the device lengths
+    to zero on the stream ([GQA] "A strong answer" and [CH16] "Layout and
+    validity" build the cache from zeros): buffers holding 0xFF bytes before
+    the call read back as zeros, through the C ABI on caller-owned memory."""
+    import ctypes
+    from gqa_attention_preallocated_amd import _lib as L
+    lib = L.load()
+    _lib()
+    B, hk, S, d = 3, 2, 128, 64
+    P = ctypes.c_void_p
+    stream = P(torch.cuda.current_stream().cuda_stream)
+    for kind in ["f32", "bf16", "ring", "fp8", "paged"]:
+        elem = {"f32": 4, "bf16": 2, "ring": 2, "fp8": 1, "paged": 2}[kind]
+        rows = 5 * 64 if kind == "paged" else B * S          # the paged pool: 5 pages of 64 tokens
+        k = torch.full((rows * hk * d * elem,), 0xFF, dtype=torch.uint8, device="cuda")
+        v = torch.full_like(k, 0xFF)
+        lens = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+        table = torch.full((B * 2,), 7, dtype=torch.int32, device="cuda")
+        h = P()
+        args = (P(k.data_ptr()), P(v.data_ptr()), P(lens.data_ptr()))
+        if kind == "ring":
+            st = lib.kv_cache_create_ring(B, hk, S, d, 1, 64, *args, stream, ctypes.byref(h))
+        elif kind == "fp8":
+            sc = (ctypes.c_float * hk)(*([0.1] * hk))
+            st = lib.kv_cache_create_fp8(B, hk, S, d, sc, sc, *args, stream, ctypes.byref(h))
+        elif kind == "paged":
+            st = lib.kv_cache_create_paged(B, hk, 5, 64, 2, d, 1, *args[:2], P(table.data_ptr()), args[2], stream,
+                                           ctypes.byref(h))
+        else:
+            st = lib.kv_cache_create(B, hk, S, d, 0 if kind == "f32" else 1, *args, stream, ctypes.byref(h))
+        assert st == 0, lib.kv_last_error()
+        torch.cuda.synchronize()
+        assert not k.any() and not v.any(), kind
+        assert lens.tolist() == [0] * B
+        if kind == "paged":
+            assert table.tolist() == [-1] * (B * 2)
+        assert lib.kv_cache_destroy(h) == 0

@@ -1,8 +1,8 @@
 """Pins of the paged-cache oracle (oracle/paged.py).
 
 [GQA] "Implement grouped-query attention over a preallocated KV cache, with no
-torch.cat, for both prefill chunks and decode", the reversal (rows of wildly
-different lengths move to a block table and a paged kernel) and [CH16]
+torch.cat, for both prefill chunks and decode", the reversal paragraph (rows
+whose lengths differ by orders of magnitude call for per-row page tables) and [CH16]
 "16. Prefill, decode and the KV cache", design choices (a paged cache keeps the
 O(1) write without reserving max_len per row). Pins: paging changes where the
 bytes live, never the result, so outputs equal the linear oracle bit for bit

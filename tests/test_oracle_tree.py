@@ -1,8 +1,8 @@
 """Pins of the tree-verify oracle (oracle/tree.py).
 
 [MASK] "Write the causal mask for a decode step with a KV cache, where the
-query is shorter than the keys", "What interviewers probe next": each draft
-token attends the full cache plus its ancestors. Pins: a chain is the ordinary
+query is shorter than the keys", "What interviewers probe next": a draft
+node sees the committed keys and its own path to the root. Pins: a chain is the ordinary
 causal verify of the linear oracle, a tree of roots is T independent decode
 steps, other branches never reach a node, visible counts follow depth, and the
 plain causal triangle fails on a branching tree.

@@ -12,6 +12,7 @@ equal to the host lengths.
 import ctypes
 import os
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -19,18 +20,11 @@ import pytest
 import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-CSRC = os.path.join(ROOT, "gqa_attention_preallocated_amd", "csrc")
 
 
 @pytest.fixture(scope="session")
-def sim(tmp_path_factory):
-    out = tmp_path_factory.mktemp("hostcheck") / "libhostcheck.so"
-    cmd = ["g++", "-O1", "-std=c++17", "-shared", "-fPIC", "-D__HIP_PLATFORM_AMD__",
-           "-I/opt/rocm/include", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           os.path.join(CSRC, "abi.cpp"), os.path.join(ROOT, "tests", "hostcheck", "launch_sim.cpp"),
-           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
-    lib = ctypes.CDLL(str(out))
+def sim(hostcheck_lib):
+    lib = hostcheck_lib
     P, I32 = ctypes.c_void_p, ctypes.c_int32
     I32P = ctypes.POINTER(ctypes.c_int32)
     lib.kv_cache_create.argtypes = [I32, I32, I32, I32, ctypes.c_int, P, P, P, P, ctypes.POINTER(P)]
@@ -199,6 +193,57 @@ def _run(sim, B, hk, G, d, max_len, dtype, calls, policy=(0, 0)):
 def test_tiny_schedule(sim, policy):
     sh = W.TINY_FP32
     _run(sim, sh.batch, sh.kv_heads, sh.group, sh.head_dim, sh.max_len, "f32", W.tiny_schedule(0), policy)
+
+
+@pytest.mark.parametrize("kps", [2**31 - 1, 2**31 - 32, 2**31 - 64, 2**31 - 65, 10**9])
+@pytest.mark.parametrize("path", [1, 2])
+def test_huge_keys_per_split_means_one_split(sim, path, kps):
+    """A split length near INT32_MAX ("never split") gives every row one split:
+    rounding it up to the key tile must not wrap to a negative length and
+    leave a row with no work items (its outputs unwritten, its fused append
+    skipped)."""
+    sh = W.TINY_FP32
+    _run(sim, sh.batch, sh.kv_heads, sh.group, sh.head_dim, sh.max_len, "f32", W.tiny_schedule(0), (path, kps))
+    # Llama-shaped rows: 4,097 keys each, decode and prefill kernels, one call
+    # through kv_append_attention (the fused append writes every new token once)
+    B, hk, hq, d = 4, 8, 32, 128
+    c = SimCache(sim, B, hk, 8192, d, "bf16", hq, 4096)
+    sim.kv_cache_set_policy(c.h, path, kps)
+    for call in _prefix_calls([4096] * B):
+        c.append(call["T"], call["n_new"])
+    for T in (1, 64):
+        ws = c.append_attention(T, [T] * B)
+        assert ws == 0                           # one split per row: no partials
+        c.check(T)
+        sim.kv_truncate(c.h, _i32([4096] * B), None)
+        c.lens[:] = 4096
+        c.rewrote = True
+
+
+def test_sanitized_replay():
+    """The host library (abi.cpp with the launch simulator) under AddressSanitizer
+    and UndefinedBehaviorSanitizer: the smaller simulator cases of this file and
+    the host ABI checks, in a child process that preloads the ASan runtime. Any
+    report aborts the child."""
+    if os.environ.get("GQAKV_HOSTCHECK_SANITIZE") == "1":
+        pytest.skip("already the sanitized run")
+    asan = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True, text=True).stdout.strip()
+    if not os.path.isabs(asan) or not os.path.exists(asan):
+        pytest.skip("no ASan runtime for g++ here")
+    env = dict(os.environ)
+    env.update({"GQAKV_HOSTCHECK_SANITIZE": "1", "LD_PRELOAD": asan,
+                "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1",
+                "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1"})
+    sel = ("tiny_schedule or random_trials or huge_keys or ring_schedules or paged_random or mqa "
+           "or more_rows or append_attention_trials or tree_verify or refus or invalid "
+           "or capacity_error or argument_checks or truncate_rules or paged_create")
+    cmd = [sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "-p", "no:xdist",
+           os.path.join(ROOT, "tests", "test_plan_bounds.py"), os.path.join(ROOT, "tests", "test_abi_host.py"),
+           "-k", sel]
+    res = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=900, cwd=ROOT)
+    tail = (res.stdout + res.stderr)[-4000:]
+    assert res.returncode == 0, tail
+    assert "passed" in res.stdout and "AddressSanitizer" not in tail and "runtime error" not in tail, tail
 
 
 @pytest.mark.parametrize("seed", range(40))
