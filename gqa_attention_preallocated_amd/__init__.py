@@ -23,7 +23,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["KVCache", "gqa_attention", "append_attention", "library_path"]
+__all__ = ["KVCache", "gqa_attention", "append_attention", "append_attention_noalloc", "library_path"]
 
 _DTYPES = {torch.float32: _lib.KV_DTYPE_F32, torch.bfloat16: _lib.KV_DTYPE_BF16}
 
@@ -320,5 +320,35 @@ def append_attention(cache: KVCache, k_new, v_new, q, n_new, out=None, workspace
             raise ValueError(f"parents must be [B={B}, T={T}]")
         st = lib.kv_append_attention_tree(cache.handle, *ptrs, hq, T, arr, _lib.int32_array(flat),
                                           ctypes.c_void_p(out.data_ptr()), *ws_args)
+    _lib.check(st, lib)
+    return out
+
+
+def append_attention_noalloc(cache: KVCache, k_new, v_new, q, n_new, out):
+    """``append_attention`` through kv_append_attention_noalloc: no workspace,
+    and nothing allocated by the library or here (``out`` is the caller's).
+    The split partials live in the library's scratch on the cache's device,
+    shared by every such call on that GPU: calls that may overlap there race.
+    Raises ValueError when the call's partials need more than that scratch."""
+    cache._check_tensor(k_new, "k_new", cache.kv_heads)
+    cache._check_tensor(v_new, "v_new", cache.kv_heads)
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new differ in shape")
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-d tensor [B, Hq, T, d]")
+    cache._check_tensor(q, "q", q.shape[1])
+    cache._check_tensor(out, "out", q.shape[1])
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    B, hq, T, _ = q.shape
+    if k_new.shape[2] != T:
+        raise ValueError("k_new and q differ in T")
+    arr = _lib.int32_array(_row_counts(n_new, B))
+    lib = cache._lib
+    with torch.cuda.device(cache.device):     # the scratch of the cache's device
+        st = lib.kv_append_attention_noalloc(cache.handle, ctypes.c_void_p(k_new.data_ptr()),
+                                             ctypes.c_void_p(v_new.data_ptr()), ctypes.c_void_p(q.data_ptr()),
+                                             hq, T, arr, ctypes.c_void_p(out.data_ptr()),
+                                             _stream_ptr(cache._device.index))
     _lib.check(st, lib)
     return out

@@ -28,6 +28,7 @@ EXPORTED = (
     "kv_last_error", "kv_cache_set_policy", "kv_cache_create_ring", "kv_cache_create_fp8",
     "gqa_attention_tree", "kv_cache_create_paged", "kv_get_block_table", "kv_free_pages",
     "kv_append_attention", "kv_append_attention_workspace_size", "kv_append_attention_tree",
+    "kv_append_attention_noalloc",
 )
 
 _lib = None
@@ -78,6 +79,8 @@ def configure(lib):
     lib.gqa_attention_tree.restype = ctypes.c_int
     lib.kv_append_attention.argtypes = [P, P, P, P, I32, I32, I32P, P, P, ctypes.c_size_t, P]
     lib.kv_append_attention.restype = ctypes.c_int
+    lib.kv_append_attention_noalloc.argtypes = [P, P, P, P, I32, I32, I32P, P, P]
+    lib.kv_append_attention_noalloc.restype = ctypes.c_int
     lib.kv_append_attention_tree.argtypes = [P, P, P, P, I32, I32, I32P, I32P, P, P, ctypes.c_size_t, P]
     lib.kv_append_attention_tree.restype = ctypes.c_int
     lib.kv_append_attention_workspace_size.argtypes = [P, I32, I32, I32P, ctypes.POINTER(ctypes.c_size_t)]

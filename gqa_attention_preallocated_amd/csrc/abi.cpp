@@ -357,15 +357,17 @@ kv_status attention_prepare(const kv_cache *c, const int32_t *lens, const void *
 // New tokens a decode kernel appends itself (kv_append_attention): read from
 // k_new / v_new [B, Hkv, T, d] and written to the cache by the kernel.
 kv_status check_tree(const kv_cache *c, int32_t q_heads, int32_t T, const int32_t *n_new, const int32_t *parents);
+// one_stream: every kernel of the call on `stream` (no side stream is created
+// or used, so the call creates no stream or event)
 kv_status append_attention_call(kv_cache *c, const void *k_new, const void *v_new, const void *q, int32_t q_heads,
                                 int32_t T, const int32_t *n_new, const int32_t *parents, void *out,
-                                void *workspace, size_t workspace_bytes, void *stream);
+                                void *workspace, size_t workspace_bytes, void *stream, bool one_stream = false);
 struct Fused {
     const void *k_new = nullptr, *v_new = nullptr;
 };
 kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_heads, int32_t T,
                            const int32_t *n_new, const int32_t *parents, void *out, void *workspace,
-                           const Fused *fused, void *stream);
+                           const Fused *fused, void *stream, bool one_stream = false);
 // An append's checks (all rows, the pool), before anything is enqueued.
 kv_status append_check(const kv_cache *c, const void *k_new, const void *v_new, int32_t T, const int32_t *n_new,
                        int64_t *pages_needed, bool check_pointers = true);
@@ -605,6 +607,24 @@ kv_status kv_append_attention(kv_cache *c, const void *k_new, const void *v_new,
                                  stream);
 }
 
+kv_status kv_append_attention_noalloc(kv_cache *c, const void *k_new, const void *v_new, const void *q,
+                                      int32_t q_heads, int32_t T, const int32_t *n_new, void *out, void *stream) {
+    if (c == nullptr) return fail(KV_ERR_INVALID_ARG, "null cache handle");
+    // the library's own scratch on the current device stands in for the
+    // caller's workspace; every kernel runs on `stream`
+    void *scratch = nullptr;
+    const hipError_t e = scratch_region(&scratch);
+    if (e != hipSuccess) return device_fail(e, "kv_append_attention_noalloc (scratch address)");
+    const kv_status s = append_attention_call(c, k_new, v_new, q, q_heads, T, n_new, nullptr, out, scratch,
+                                              kScratchBytes, stream, true);
+    if (s == KV_ERR_WORKSPACE) {
+        const std::string why = g_err;
+        return fail(KV_ERR_WORKSPACE, "kv_append_attention_noalloc: %s; the entry point holds %zu bytes of scratch "
+                    "per GPU (call kv_append_attention with a workspace instead)", why.c_str(), kScratchBytes);
+    }
+    return s;
+}
+
 kv_status kv_append_attention_tree(kv_cache *c, const void *k_new, const void *v_new, const void *q,
                                    int32_t q_heads, int32_t T, const int32_t *n_new, const int32_t *parents,
                                    void *out, void *workspace, size_t workspace_bytes, void *stream) {
@@ -644,7 +664,7 @@ kv_status check_tree(const kv_cache *c, int32_t q_heads, int32_t T, const int32_
 
 kv_status append_attention_call(kv_cache *c, const void *k_new, const void *v_new, const void *q, int32_t q_heads,
                                 int32_t T, const int32_t *n_new, const int32_t *parents, void *out,
-                                void *workspace, size_t workspace_bytes, void *stream) {
+                                void *workspace, size_t workspace_bytes, void *stream, bool one_stream) {
     // every check of both halves first, against the lengths after the append
     int64_t pages = 0;
     kv_status s = append_check(c, k_new, v_new, T, n_new, &pages);
@@ -666,7 +686,8 @@ kv_status append_attention_call(kv_cache *c, const void *k_new, const void *v_ne
     Fused f;
     f.k_new = k_new;
     f.v_new = v_new;
-    s = attention_launch(c, p, q, q_heads, T, n_new, parents, out, workspace, fuse ? &f : nullptr, stream);
+    s = attention_launch(c, p, q, q_heads, T, n_new, parents, out, workspace, fuse ? &f : nullptr, stream,
+                         one_stream);
     return s == KV_OK ? ok() : s;
 }
 
@@ -815,7 +836,7 @@ kv_status attention_call(kv_cache *c, const void *q, int32_t q_heads, int32_t T,
 
 kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_heads, int32_t T,
                            const int32_t *n_new, const int32_t *parents, void *out, void *workspace,
-                           const Fused *fused, void *stream) {
+                           const Fused *fused, void *stream, bool one_stream) {
     if (p.dec.empty() && p.pre.empty() && p.pad_rows.empty()) return KV_OK;
     hipStream_t st = (hipStream_t)stream;
     const WsLayout w = ws_layout(c, p);
@@ -826,7 +847,7 @@ kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_
     // stream, beside the prefill kernel: the MFMA-bound prefill then starts
     // at once and the HBM-bound work fills the chip around it. The three
     // write disjoint output slots.
-    const bool mixed = !p.pre.empty() && (!p.dec.empty() || !p.pad_rows.empty());
+    const bool mixed = !one_stream && !p.pre.empty() && (!p.dec.empty() || !p.pad_rows.empty());
     hipStream_t dec_stream = st;
     if (mixed) {
         hipError_t e = side_stream_init(c->side);

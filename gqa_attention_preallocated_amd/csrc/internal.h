@@ -143,6 +143,14 @@ struct ZeroArgs {
     ZeroRows rows;
 };
 
+// Scratch of the no-allocation entry point (kv_append_attention_noalloc): a
+// file-scope device array of this many bytes in kernels.hip, one copy per GPU,
+// held until the process ends. It holds a call's split partial records.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+// The device address of that array on the current device, looked up with
+// hipGetSymbolAddress on the first call on each device and kept per device.
+hipError_t scratch_region(void **ptr);
+
 // element type codes match kv_dtype
 hipError_t launch_append(const AppendArgs &a, int n_blocks, hipStream_t s);
 hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t s);

@@ -28,12 +28,42 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "indexing.h"
 #include "internal.h"
 
 namespace gqakv {
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation entry point: the split partial records of one
+// call (what the caller's workspace holds in the other entry points). Each GPU
+// the library runs on gets its own copy at its own address. In host code the
+// name below is only a host-side handle for the symbol, never a device
+// address: host code uses the pointer scratch_region() returns.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_region(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::mutex mu;
+    static std::vector<void *> addr;      // device address of `scratch`, per device
+    std::lock_guard<std::mutex> lock(mu);
+    if ((size_t)dev >= addr.size()) addr.resize((size_t)dev + 1, nullptr);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with device `dev` current
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 // every launch passes its tables by value: keep them inside the kernel-argument space
 static_assert(sizeof(AttnArgs) <= 4096 && sizeof(AppendArgs) <= 4096 && sizeof(CombineArgs) <= 4096 &&

@@ -320,6 +320,29 @@ kv_status kv_append_attention_tree(kv_cache *c, const void *k_new, const void *v
                                    void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kv_append_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call, with the same cache bytes, lengths and output
+ * bits, but no workspace argument. The split partial records live in a
+ * scratch array of 16 MiB that the library holds in device memory, one copy
+ * per GPU, from the first call on that GPU until the process ends; the call
+ * itself allocates nothing (no device memory, stream or event), and every
+ * kernel runs on `stream`, with a mixed batch's decode and prefill kernels
+ * one after the other. Call it with the cache's device current: the scratch
+ * of the current device is used. Every call on a GPU shares that GPU's
+ * scratch, which keeps whatever the last call left (nothing in it needs to
+ * start at any value: each partial is written before it is read): two calls
+ * that may overlap on one GPU, on different streams or from different
+ * threads, race and must be ordered by the caller.
+ * Returns KV_ERR_WORKSPACE, with nothing changed, for a call whose partials
+ * need more than the 16 MiB (the size kv_append_attention_workspace_size
+ * reports for it, before the tree-verify margin); KV_ERR_DEVICE if the
+ * scratch address cannot be looked up; otherwise as kv_append_attention.
+ */
+kv_status kv_append_attention_noalloc(kv_cache *c, const void *k_new, const void *v_new, const void *q,
+                                      int32_t q_heads, int32_t T, const int32_t *n_new, void *out, void *stream);
+
+/*
  * Workspace kv_append_attention needs for these arguments (the
  * gqa_attention workspace for the lengths after the append), in bytes; it
  * also covers kv_append_attention_tree.

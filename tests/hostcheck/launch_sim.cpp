@@ -181,6 +181,19 @@ hipError_t launch_table_fill(int32_t *table, int64_t n, int32_t value, hipStream
     return hipSuccess;
 }
 
+// the no-allocation entry point's scratch: here the test's registered
+// workspace region, so its accesses are checked like a caller's workspace
+hipError_t scratch_region(void **ptr) {
+    for (const Region &r : g_regions)
+        if (r.name == "ws") {
+            if (r.size < kScratchBytes) err("scratch: the ws region is smaller than the scratch array");
+            *ptr = reinterpret_cast<void *>(r.base);
+            return hipSuccess;
+        }
+    err("scratch: no ws region registered");
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_zero_bytes(void *p, int64_t bytes, hipStream_t) {
     ++g_launches;
     if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(p) & 15) != 0) err("zero bytes: not 16-byte granular");

@@ -643,3 +643,39 @@ def test_append_attention_tree_wide_rows(sim):
     c.lens += np.asarray(n)
     c.appended += int(np.sum(n)) * c.hk * c.d * c.elem // 16
     c.check(T)
+
+
+def test_noalloc_entry_point(sim):
+    """kv_append_attention_noalloc: the same launches as kv_append_attention with
+    the library's scratch as workspace (the simulator maps it onto the
+    registered workspace region), every kernel on one stream; a call whose
+    partials need more than the scratch is refused before anything is
+    enqueued, with nothing changed."""
+    P, I32 = ctypes.c_void_p, ctypes.c_int32
+    sim.kv_append_attention_noalloc.argtypes = [P, P, P, P, I32, I32, ctypes.POINTER(I32), P, P]
+    B, hk, hq, d = 16, 8, 32, 128
+    c = SimCache(sim, B, hk, 8192, d, "bf16", hq, 4096)
+    for call in _prefix_calls([4092] * B):
+        c.append(call["T"], call["n_new"])
+    a = c.addr
+    for T in (4, 1):                            # verify, then a smaller decode call: both split rows
+        size = ctypes.c_size_t()
+        assert sim.kv_append_attention_workspace_size(c.h, hq, T, _i32([T] * B), ctypes.byref(size)) == 0
+        assert 0 < size.value <= 16 << 20
+        sim.hostcheck_begin_call()
+        st = sim.kv_append_attention_noalloc(c.h, P(a["k_new"]), P(a["v_new"]), P(a["q"]), hq, T, _i32([T] * B),
+                                             P(a["out"]), None)
+        assert st == 0, sim.kv_last_error()
+        c.lens += T
+        c.appended += B * T * hk * d * c.elem // 16
+        c.check(T)
+    # a prefill row forced into 64-key splits needs far more than 16 MiB of partials
+    sim.kv_cache_set_policy(c.h, 2, 64)
+    launches = sim.hostcheck_launches()
+    st = sim.kv_append_attention_noalloc(c.h, P(a["k_new"]), P(a["v_new"]), P(a["q"]), hq, 256, _i32([256] * B),
+                                         P(a["out"]), None)
+    assert st == 4
+    assert "16777216 bytes of scratch" in sim.kv_last_error().decode()
+    assert sim.hostcheck_launches() == launches
+    lens = (ctypes.c_int32 * B)()
+    assert sim.kv_get_lens(c.h, lens) == 0 and list(lens) == c.lens.tolist()
