@@ -962,11 +962,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     }
 }
 
+
 // ---------------------------------------------------------------------------
 // chunked-prefill kernel: PW waves x 32 columns per work item, 64-key tiles
-// of K and V shared by the waves through double-buffered LDS. With PW = 8 one
-// work group fills a CU at two waves per SIMD; eight waves rather than four
-// halve the staging (global loads, LDS stores, their registers) per FLOP.
+// of K and V shared by the waves through LDS. With PW = 8 one work group
+// fills a CU at two waves per SIMD; eight waves rather than four halve the
+// staging (global loads, LDS stores, their registers) per FLOP. The two waves
+// of a SIMD run each tile's matrix work and softmax in opposite orders, so
+// one's exponentials and vector work run beside the other's MFMAs (on gfx950
+// a wave's exponentials overlap another wave's MFMAs, but stall its own).
 // float32 at d = 128 runs PW = 4 at one wave per SIMD (prefill_waves).
 // Key tiles past the last query's position are never loaded; tiles wholly at
 // or below the first query's position are not masked; only tiles straddling
@@ -984,16 +988,26 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     constexpr int C = WC * PW;                    // columns per item
     constexpr int NT = 64 * PW;                   // threads per work group
     constexpr int ROWB = D * O::kBytes;           // LDS bytes of a K or V row (compute type)
+    // padded LDS rows keep the operand reads conflict-free
     constexpr int RS = ROWB + O::kPad;
     constexpr int CROWB = D * S::kBytes;          // cache bytes of a row
     constexpr int CPK = CROWB / 16;               // 16-byte cache chunks per row
     constexpr int TILE_BYTES = KT * RS;
     constexpr int PCH = (KT * CPK + NT - 1) / NT; // 16-byte chunks per thread per tensor
-    __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char lds_v[2][TILE_BYTES];
+    // With 8 waves, waves w and w + 4 share a SIMD and run a tile's work in
+    // opposite orders (PING, below); a K or V tile is then read in two
+    // iterations, and each tensor gets three slots. With 4 waves (one per
+    // SIMD) every wave takes the same order, and two slots suffice.
+    constexpr bool PING = PW == 8;
+    constexpr int SL = PING ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) unsigned char lds_k[SL][TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char lds_v[SL][TILE_BYTES];
+    static_assert(2 * SL * TILE_BYTES <= 160 * 1024, "prefill LDS tiles exceed the CU's 160 KiB");
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    // the wave index is the same in every lane: a scalar, so that per-wave
+    // conditions and tile positions stay in scalar registers and branches
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const Item it = decode_item_wave(a.rows, blockIdx.x, a.hkv, a.group, C, a.window);
 
@@ -1065,39 +1079,6 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
             if ((KT * CPK) % NT == 0 || c < KT * CPK) S::stage(dst + (c / CPK) * RS + (c % CPK) * S::kLdsPerChunk, reg[i]);
         }
     };
-    // S^T of one 64-key tile for the wave's 32 columns (32 MFMAs)
-    auto scores = [&](const unsigned char *kl, f32x4 (&sc)[2][NS][2]) {
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int krow = ch * 32 + ks * 16 + lr;
-#pragma unroll
-                for (int s = 0; s < NS; ++s) sc[ch][s][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kc = 0; kc < KC; ++kc) {
-                    const int d0 = kc * 32 + lg * 8;
-                    const vec kv = (d0 < D) ? O::lds_load(kl + krow * RS + d0 * O::kBytes) : O::zero();
-#pragma unroll
-                    for (int s = 0; s < NS; ++s) sc[ch][s][ks] = O::mma(kv, qop[s][kc], sc[ch][s][ks]);
-                }
-            }
-    };
-
-    // O^T += V^T P^T for one staged V tile, and the row sums on the all-ones block
-    auto pv = [&](const unsigned char *vl, const vec (&pb)[2][NS]) {
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const vec vt = O::vt_operand(vl, RS, ch * 32, nb * 16, lane);
-#pragma unroll
-                for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt, pb[ch][s], acc[s][nb]);
-            }
-#pragma unroll
-            for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, pb[ch][s], acc[s][NB]);
-        }
-    };
     // straddling tiles only: key (ch, ks, j) = tile + ch*32 + ks*16 + 4*lg + j
     // is visible iff it is <= the column's position, > that position minus
     // the window, and < the split end
@@ -1118,185 +1099,201 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
                     }
         }
     };
-    // column max of the tile in log2 units
-    auto tile_max = [&](const f32x4 (&sc)[2][NS][2], float (&tmax)[NS]) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            float t = -INFINITY;
-#pragma unroll
-            for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    t = smax(t, smax(smax(smax(sc[ch][s][ks][0], sc[ch][s][ks][1]), sc[ch][s][ks][2]),
-                                     sc[ch][s][ks][3]));
-            tmax[s] = wave_max_across_groups(t) * score_c;
+    // Software pipeline over the item's key tiles, one iteration per tile i
+    // between barriers. A wave's work for a tile is a matrix block (MFMAs
+    // with their LDS operand reads: PV of one tile, the scores of another)
+    // and a softmax block (vector work: column max, rescale decision,
+    // probabilities). Group A (waves 0-3) runs the matrix block first, PV of
+    // tile i-1 and the scores of tile i, then the softmax of tile i; group B
+    // (waves 4-7, the other wave of each SIMD) runs the softmax of tile i
+    // first (its scores came with the previous iteration), then PV of tile i
+    // and the scores of tile i+1. So on every SIMD one wave's softmax runs
+    // beside the other wave's MFMAs. With 4 waves there are no pairs: every
+    // wave takes group B's order.
+    // Staging: iteration i stores K(i+1) and V(i) into slot (i+1) % SL and
+    // i % SL of their tensors, issues the global loads of K(i+2) and V(i+1)
+    // into the registers just stored, then the barrier. In iteration i the
+    // waves read K(i), K(i+1), V(i-1) and V(i) (group A the first and third,
+    // group B the others); a wave that is still in iteration i-1 when another
+    // stores reads K(i-1), K(i), V(i-2), V(i-1); with three slots (two without
+    // group A) the slots written are never among them. A wave computes tiles
+    // 0..wave_last only (tiles past its last query are skipped); it still
+    // takes part in staging and barriers, and group A finishes the PV of its
+    // last tile in the first skipped iteration or after the loop.
+    // waves w and w + 4 share a SIMD (the waves of a work group go to the
+    // SIMDs in turn)
+    const bool grp_a = PING && wave < 4;
+    // an empty asm that takes v in registers: v is computed by this point
+    auto pin = [](vec &v) {
+        if constexpr (sizeof(vec) == 16) {
+            uint4 u = __builtin_bit_cast(uint4, v);
+            asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+            v = __builtin_bit_cast(vec, u);
+        } else {
+            struct U8 { uint4 a, b; };
+            U8 u = __builtin_bit_cast(U8, v);
+            asm volatile("" : "+v"(u.a.x), "+v"(u.a.y), "+v"(u.a.z), "+v"(u.a.w));
+            asm volatile("" : "+v"(u.b.x), "+v"(u.b.y), "+v"(u.b.z), "+v"(u.b.w));
+            v = __builtin_bit_cast(vec, u);
         }
     };
-    // Software pipeline over the item's key tiles, two matrix phases per tile,
-    // each interleaved by hand with independent VALU work of the same wave so
-    // that the wave issues VALU while its MFMAs occupy the matrix core:
-    //   phase X: O^T += V(i-1)^T P(i-1)^T   beside   the column max of tile i
-    //   phase Y: scores of tile i+1         beside   the probabilities of tile i
-    // Each phase is a fixed sequence of steps (2 MFMAs, their LDS operands
-    // fetched ahead, a few VALU ops) fenced with sched_barrier.
-    // Staging: iteration i writes K(i+1) and V(i-1) to LDS, then one barrier.
-    // Its stores run before that barrier, so a slower wave may still be in
-    // iteration i-1, which reads K(i) and V(i-2); the slots written hold
-    // K(i-1) and V(i-3), last read in iteration i-2. The tile loads for the
-    // next stores (K(i+2), V(i)) are issued right after this iteration's
-    // stores, before the barrier, into the registers just stored. V(last) is
-    // staged after the loop behind its own barrier. A wave computes tiles
-    // 0..wave_last only (tiles past its last query are skipped; it still
-    // takes part in staging and barriers).
     const int ntiles = it.k_end > it.k_begin ? (it.k_end - it.k_begin + KT - 1) / KT : 0;
     const int wave_last = wave_pos_max < it.k_begin ? -1 : imin(ntiles - 1, (wave_pos_max - it.k_begin) / KT);
-    f32x4 sc[2][NS][2];
-    vec pb[2][NS];
+    f32x4 sc[2][NS][2];      // scores of tile i (chunk, subtile, 16-key block)
+    vec pb[2][NS];           // PV B operands: the probabilities of one tile, both chunks
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) pb[ch][s] = O::zero();
 
-    // probability pair u (0..7) of chunk ch of tile i: subtile u / 4, elements
-    // 2 (u % 4) and 2 (u % 4) + 1, packed into the PV operand
+    // probability pair u (0..4 NS - 1) of chunk ch of tile i: subtile u / 4,
+    // elements 2 (u % 4) and 2 (u % 4) + 1, packed into the PV operand
     auto prob_pair = [&](int ch, int u, float m) {
         const int ps = u >> 2, j = (u & 3) * 2;
         O::set_pair(pb[ch][ps], j, fast_exp2(fmaf(sc[ch][ps][j >> 2][j & 3], score_c, -m)),
                     fast_exp2(fmaf(sc[ch][ps][(j + 1) >> 2][(j + 1) & 3], score_c, -m)));
     };
-    // the reference max as it stands before tile i's rescale decision
-    auto ref_max = [&](float (&m)[NS]) {
+    // S^T of one 64-key tile for the wave's columns (prologue: tile 0)
+    auto scores = [&](const unsigned char *kl, f32x4 (&out)[2][NS][2]) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) m[s] = (st[s].m == -INFINITY) ? 0.f : st[s].m;
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int krow = ch * 32 + ks * 16 + lr;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) out[ch][s][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    const int d0 = kc * 32 + lg * 8;
+                    const vec kv = (d0 < D) ? O::lds_load(kl + krow * RS + d0 * O::kBytes) : O::zero();
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) out[ch][s][ks] = O::mma(kv, qop[s][kc], out[ch][s][ks]);
+                }
+            }
+    };
+    // PV of one 32-key chunk (outside the phases: a wave's last tile)
+    auto pv_chunk = [&](const unsigned char *vl, int ch, const vec (&b)[NS]) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const vec vt = O::vt_operand(vl, RS, ch * 32, nb * 16, lane);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt, b[s], acc[s][nb]);
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, b[s], acc[s][NB]);
     };
 
-    // phase X: 2*NB steps of PV (ch = g / NB, nb = g % NB, every subtile), the
-    // all-ones MFMAs of chunk 0 after step NB-1 and of chunk 1 at the end.
-    // VALU, first NB steps: the max tree of tile i as 5 NS tasks (per subtile:
-    // four quarter maxima, then the column max), task t at step t * NB / (5 NS)
-    // so every task runs after the ones it needs. VALU, last NB steps (chunk
-    // 0's operands are consumed by then): the 4 NS probability pairs of chunk 0
-    // of tile i against the current reference max, pair u at step NB + u * NB /
-    // (4 NS). The
-    // reference only moves when a column's max outgrows it by more than
-    // kRescaleLog2; finish_max then recomputes chunk 0 for those columns, so
-    // every probability of the tile uses one reference, as if computed after
-    // the decision.
-    auto phase_x = [&](const unsigned char *vp, float (&tmax)[NS]) {
-        constexpr int NSX = 2 * NB;
-        float m0[NS];
-        ref_max(m0);
-        // V^T operands are read from LDS two steps ahead of their MFMAs
-        vec vt[3];
-        vt[0] = O::vt_operand(vp, RS, 0, 0, lane);
-        if (NSX > 1) vt[1] = O::vt_operand(vp, RS, (1 / NB) * 32, (1 % NB) * 16, lane);
-        float part[NS][4];
-#pragma unroll
-        for (int g = 0; g < NSX; ++g) {
-            const int ch = g / NB, nb = g % NB;
-            if (g + 2 < NSX) vt[(g + 2) % 3] = O::vt_operand(vp, RS, ((g + 2) / NB) * 32, ((g + 2) % NB) * 16, lane);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(vt[g % 3], pb[ch][s], acc[s][nb]);
-            if (g == NB - 1) {
-#pragma unroll
-                for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, pb[0][s], acc[s][NB]);
-            }
-            if (g < NB) {
-#pragma unroll
-                for (int t = 0; t < 5 * NS; ++t) {
-                    if (t * NB / (5 * NS) != g) continue;
-                    if (t < 4 * NS) {
-                        const int s = t >> 2, q = t & 3;      // quarter q = (ch, ks) block
-                        const f32x4 x = sc[q >> 1][s][q & 1];
-                        part[s][q] = smax(smax(smax(x[0], x[1]), x[2]), x[3]);
-                    } else {
-                        const int s = t - 4 * NS;
-                        const float m4 = smax(smax(smax(part[s][0], part[s][1]), part[s][2]), part[s][3]);
-                        tmax[s] = wave_max_across_groups(m4) * score_c;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4 * NS; ++u)
-                    if (NB + u * NB / (4 * NS) == g) prob_pair(0, u, m0[u >> 2]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, pb[1][s], acc[s][NB]);
-    };
-    // phase Y: 16 steps of scores for tile i+1 (ch = g / 8, kc = (g / 2) % 4,
-    // ks = g % 2, every subtile; steps with kc >= KC issue no MFMA): an
-    // accumulator is updated every fourth MFMA, and only those of one chunk
-    // are live while the probabilities of chunk 1 of tile i, NS / 2 pairs in
-    // each of the first 8 steps, free their scores
-    auto phase_y = [&](const unsigned char *kn, const float (&m_use)[NS], f32x4 (&scn)[2][NS][2]) {
-        auto kop = [&](int g) {
-            const int krow = (g >> 3) * 32 + (g & 1) * 16 + lr;
-            const int d0 = ((g >> 1) & 3) * 32 + lg * 8;
-            return (d0 < D) ? O::lds_load(kn + krow * RS + d0 * O::kBytes) : O::zero();
+    // Half of a matrix block: NSTEP = NB + 2 KC steps of NS MFMAs. PV steps
+    // (NB of them: output block nb of chunk c of the V tile vl, B operand
+    // pb[c]) and score steps (2 KC: (kc, ks) of chunk c of the K tile kl into
+    // scn) are spread evenly, so the LDS reads of both kinds interleave; a
+    // score accumulator is updated every other score step. Operands are read
+    // from LDS two steps ahead; steps are fenced with sched_barrier so the
+    // order holds. The all-ones row-sum MFMAs of the PV chunk close it.
+    constexpr int NSTEP = NB + 2 * KC;
+    auto half_block = [&](const unsigned char *vl, const unsigned char *kl, int c, f32x4 (&scn)[2][NS][2]) {
+        // step g is a PV step iff the Bresenham count of PV steps grows at g
+        auto is_pv = [](int g) { return ((g + 1) * NB) / NSTEP != (g * NB) / NSTEP; };
+        auto pv_idx = [](int g) { return (g * NB) / NSTEP; };
+        auto operand = [&](int g) -> vec {
+            if (is_pv(g)) return O::vt_operand(vl, RS, c * 32, pv_idx(g) * 16, lane);
+            const int q = g - pv_idx(g), kc = q >> 1, ks = q & 1;
+            const int d0 = kc * 32 + lg * 8;
+            return (d0 < D) ? O::lds_load(kl + (c * 32 + ks * 16 + lr) * RS + d0 * O::kBytes) : O::zero();
         };
-        vec kv[3];
-        kv[0] = kop(0);
-        kv[1] = kop(1);
+        vec op[3];
+        op[0] = operand(0);
+        if (NSTEP > 1) op[1] = operand(1);
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
-            const int ch = g >> 3, kc = (g >> 1) & 3, ks = g & 1;
-            if (g + 2 < 16) kv[(g + 2) % 3] = kop(g + 2);
-            if (kc < KC) {
+        for (int g = 0; g < NSTEP; ++g) {
+            if (g + 2 < NSTEP) op[(g + 2) % 3] = operand(g + 2);
+            if (is_pv(g)) {
+                const int nb = pv_idx(g);
+#pragma unroll
+                for (int s = 0; s < NS; ++s) acc[s][nb] = O::mma(op[g % 3], pb[c][s], acc[s][nb]);
+            } else {
+                const int q = g - pv_idx(g), kc = q >> 1, ks = q & 1;
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    const f32x4 c0 = kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : scn[ch][s][ks];
-                    scn[ch][s][ks] = O::mma(kv[g % 3], qop[s][kc], c0);
+                    const f32x4 c0 = kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : scn[c][s][ks];
+                    scn[c][s][ks] = O::mma(op[g % 3], qop[s][kc], c0);
                 }
             }
-#pragma unroll
-            for (int u = 0; u < 4 * NS; ++u)
-                if (u / (NS / 2) == g) prob_pair(1, u, m_use[u >> 2]);
             __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[s][NB] = O::mma(ones, pb[c][s], acc[s][NB]);
     };
-    // move the reference max where a column's max outgrew it by more than
-    // kRescaleLog2 (st.m = -inf: the first visible key sets it; alpha is then
-    // 0 and acc is still 0), and give those columns chunk 0 again against the
-    // new reference; with chunk0_done false, chunk 0 is computed here for all
-    auto finish_max = [&](const float (&tmax)[NS], float (&m_use)[NS], bool chunk0_done) {
+    // The softmax of tile i as one block of vector work: the column max of
+    // the tile, the rescale decision (the reference max moves only when a
+    // column's max outgrows it by more than kRescaleLog2; acc then holds every
+    // PV product of the tiles before i), and the probabilities of both chunks
+    // against the reference, packed into the PV operands pb. Each result is
+    // pinned at the end of the block, so the block stays where it is placed
+    // and its exponentials run while the other wave of the SIMD issues MFMAs.
+    auto softmax_block = [&](int tile) {
+        if ((tile + KT > it.k_end) || (tile + KT - 1 > wave_pos_min) || (tile <= wave_pos_max - a.window))
+            mask(tile, sc);                              // uniform over the wave
+        float tmax[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            float q4[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const f32x4 x = sc[qq >> 1][s][qq & 1];
+                q4[qq] = smax(smax(smax(x[0], x[1]), x[2]), x[3]);
+            }
+            tmax[s] = wave_max_across_groups(smax(smax(smax(q4[0], q4[1]), q4[2]), q4[3])) * score_c;
+        }
+        float m_use[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             if (tmax[s] > st[s].m + kRescaleLog2) {
-                const float alpha = fast_exp2(st[s].m - tmax[s]);
+                const float alpha = fast_exp2(st[s].m - tmax[s]);   // st.m = -inf: 0 (acc is still 0)
 #pragma unroll
                 for (int nb = 0; nb <= NB; ++nb) acc[s][nb] *= alpha;
                 st[s].m = tmax[s];
-                if (chunk0_done) {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) prob_pair(0, s * 4 + u, tmax[s]);
-                }
             }
             m_use[s] = (st[s].m == -INFINITY) ? 0.f : st[s].m;    // no key seen yet: every p is 0
         }
-        if (!chunk0_done) {
 #pragma unroll
-            for (int u = 0; u < 4 * NS; ++u) prob_pair(0, u, m_use[u >> 2]);
-        }
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int u = 0; u < 4 * NS; ++u) prob_pair(ch, u, m_use[u >> 2]);
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+            for (int s = 0; s < NS; ++s) pin(pb[ch][s]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // The matrix block: PV of both chunks of the V tile vl with pb, and the
+    // scores of both chunks of the K tile kl into scn.
+    auto matrix_block = [&](const unsigned char *vl, const unsigned char *kl, f32x4 (&scn)[2][NS][2]) {
+        half_block(vl, kl, 0, scn);
+        half_block(vl, kl, 1, scn);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    int64_t row_cur = 0, row_next = 0;                 // cache rows of tiles i and i + 1
+    int64_t row_next = 0;                              // cache row of tile i + 1
     if (ntiles > 0) {
-        row_cur = km.row(it.k_begin);
-        load(kreg, kbase, row_cur, it.k_begin);
+        const int64_t row0 = km.row(it.k_begin);
+        load(kreg, kbase, row0, it.k_begin);
         store(kreg, lds_k[0]);
         __syncthreads();
         if (ntiles > 1) {
             row_next = km.row(it.k_begin + KT);
             load(kreg, kbase, row_next, it.k_begin + KT);
         }
-        load(vreg, vbase, row_cur, it.k_begin);
-        if (wave_last >= 0) scores(lds_k[0], sc);
+        load(vreg, vbase, row0, it.k_begin);
+        if (!grp_a && wave_last >= 0) scores(lds_k[0], sc);   // group A computes them in its first step
     }
+    int sl = 0;                                        // slot of K(i) and V(i): i % SL
     for (int i = 0; i < ntiles; ++i) {
         const int tile = it.k_begin + i * KT;
         const bool has_next = i + 1 < ntiles;          // uniform over the work group
-        const unsigned char *kn = lds_k[(i + 1) & 1];  // K(i+1)
-        const unsigned char *vp = lds_v[(i + 1) & 1];  // V(i-1)
-        if (has_next) store(kreg, lds_k[(i + 1) & 1]);
-        if (i > 0) store(vreg, lds_v[(i + 1) & 1]);
+        const int sn = sl == SL - 1 ? 0 : sl + 1, sp = sl == 0 ? SL - 1 : sl - 1;
+        if (has_next) store(kreg, lds_k[sn]);          // K(i+1)
+        store(vreg, lds_v[sl]);                        // V(i)
         // the registers are free again: the next loads go out before the
         // barrier, so they have the barrier wait as well as one iteration
         int64_t row_k2 = 0;
@@ -1304,38 +1301,42 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
             row_k2 = km.row(tile + 2 * KT);
             load(kreg, kbase, row_k2, tile + 2 * KT);
         }
-        if (i > 0) load(vreg, vbase, row_cur, tile);     // V(0) came with the prologue
-        row_cur = row_next;
+        if (has_next) load(vreg, vbase, row_next, tile + KT);
         row_next = row_k2;
         __syncthreads();
+        const int cur = sl;
+        sl = sn;
         if (i > wave_last) {
-            if (i == wave_last + 1 && wave_last >= 0) pv(vp, pb);   // the last tile this wave computed
+            // group A still owes the PV of its last computed tile
+            if (grp_a && i == wave_last + 1 && wave_last >= 0) {
+                pv_chunk(lds_v[sp], 0, pb[0]);
+                pv_chunk(lds_v[sp], 1, pb[1]);
+            }
             continue;
         }
-        if ((tile + KT > it.k_end) || (tile + KT - 1 > wave_pos_min) || (tile <= wave_pos_max - a.window))
-            mask(tile, sc);                              // uniform over the wave
-
-        float tmax[NS], m_use[NS];
+        // group B: the softmax of tile i (its scores came with the previous
+        // iteration), then PV of tile i and the scores of tile i+1. Group A:
+        // PV of tile i-1 and the scores of tile i, then the softmax of tile i.
+        // The matrix block is one piece of code for both groups. Tile 0 has no
+        // predecessor: group A's pb is still zero then, and V(0) (finite,
+        // already staged) stands in for V(-1), so those products add nothing.
+        if (!grp_a) softmax_block(tile);
         __builtin_amdgcn_s_setprio(1);
-        if (i > 0) phase_x(vp, tmax);
-        else tile_max(sc, tmax);
-        finish_max(tmax, m_use, i > 0);
-        // on the last tile the K slot holds an older tile: those scores are never used
-        f32x4 scn[2][NS][2];
-        phase_y(kn, m_use, scn);
+        // the V slot of group A's PV: V(i-1), or V(0) for tile 0; the choice is
+        // hidden from the optimizer, which would otherwise peel iteration 0
+        // into a second copy of the loop body
+        int va = __builtin_amdgcn_readfirstlane(i > 0 ? sp : cur);
+        asm volatile("" : "+s"(va));
+        matrix_block(grp_a ? lds_v[va] : lds_v[cur], grp_a ? lds_k[cur] : lds_k[sn], sc);
         __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-        for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                sc[ch][s][0] = scn[ch][s][0];
-                sc[ch][s][1] = scn[ch][s][1];
-            }
+        if (grp_a) softmax_block(tile);
     }
-    if (ntiles > 0) {
-        store(vreg, lds_v[(ntiles - 1) & 1]);            // V(last)
-        __syncthreads();
-        if (wave_last == ntiles - 1) pv(lds_v[(ntiles - 1) & 1], pb);
+    // group A: the PV of the last tile (V(last) was staged in the last
+    // iteration, before its barrier)
+    if (grp_a && ntiles > 0 && wave_last == ntiles - 1) {
+        const int last = (ntiles - 1) % SL;
+        pv_chunk(lds_v[last], 0, pb[0]);
+        pv_chunk(lds_v[last], 1, pb[1]);
     }
 
 #pragma unroll
@@ -1361,6 +1362,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     }
 }
 
+// ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
 // zero fill: +0.0 into every padded slot t >= n_new[b] (and every slot of a
 // row with no new tokens). [GQA] "A strong answer": such rows give zeros,
