@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <array>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -96,6 +97,7 @@ struct Plan {
     std::vector<RowPlan> dec, pre;     // rows per kernel
     std::vector<int32_t> zero_rows;    // rows with no new tokens (all slots zero)
     int64_t records = 0;               // partial records (d + 2 floats each)
+    int64_t dec_records = 0;           // those of decode rows (the first dec_records)
     std::vector<int32_t> pad_rows;     // rows with padded slots (n_new < T), zero-filled
 };
 
@@ -186,6 +188,15 @@ void plan_attention(const kv_cache *c, const int32_t *lens, int32_t q_heads, int
             } else {
                 r.nsplit = (int)ceil_div(tiles, tpw);
                 r.lsplit = (int)(ceil_div(tiles, r.nsplit) * kDecodeKeyTile);
+                // A work group's waves take its tiles in rounds of kDecodeWaves.
+                // When whole rounds per split leave at most one more round of
+                // tiles (a decode step: a cached length of whole rounds plus
+                // the new token), only the last split runs that round, and its
+                // tiles there are the row's last (the new token's tile holds
+                // one key), instead of every split running one more round.
+                const int64_t whole = tiles / (r.nsplit * kDecodeWaves) * kDecodeWaves;
+                if (r.nsplit > 1 && whole > 0 && tiles - r.nsplit * whole <= kDecodeWaves)
+                    r.lsplit = (int)(whole * kDecodeKeyTile);
             }
             r.work = tiles * r.nq;
             p.dec.push_back(r);
@@ -238,15 +249,17 @@ void plan_attention(const kv_cache *c, const int32_t *lens, int32_t q_heads, int
         }
     };
     for (auto &r : p.dec) assign(r, p.dec_cols);
+    p.dec_records = p.records;
     for (auto &r : p.pre) assign(r, prefill_cols(c->dtype, c->head_dim));
     for (int b = 0; b < c->batch; ++b)
         if (n_new[b] < T) p.pad_rows.push_back(b);
 }
 
-// workspace: [partial acc: records x d floats][partial (m, l): records x 2 floats],
-// the second region 256-byte aligned
+// workspace: [partial acc: records x d floats][partial (m, l): records x 2 floats]
+// [arrival counters of the decode kernel's merge: one 64-bit word per dec_cols
+// decode records], each region 256-byte aligned
 struct WsLayout {
-    size_t acc = 0, ml = 0, total = 0;
+    size_t acc = 0, ml = 0, cnt = 0, total = 0;
 };
 
 WsLayout ws_layout(const kv_cache *c, const Plan &p) {
@@ -255,8 +268,27 @@ WsLayout ws_layout(const kv_cache *c, const Plan &p) {
     if (p.records == 0) return w;
     w.acc = 0;
     w.ml = up((size_t)p.records * c->head_dim * sizeof(float));
-    w.total = w.ml + (size_t)p.records * 2 * sizeof(float);
+    w.cnt = up(w.ml + (size_t)p.records * 2 * sizeof(float));
+    w.total = w.cnt + (size_t)(p.dec_records / p.dec_cols) * sizeof(unsigned long long);
     return w;
+}
+
+// The tag of the decode kernel's arrival counters in this process: splitmix64
+// (Steele, Lea and Flood, "Fast splittable pseudorandom number generators",
+// 2014) of the clock at first use, cut to 64 - kMergeCountBits bits, never
+// zero. Every completed call leaves its counter words at (tag, 0); a word the
+// process has not used yet matches the tag only by chance (2^-56), so the
+// workspace needs no clearing.
+unsigned long long merge_tag() {
+    static const unsigned long long tag = [] {
+        uint64_t z = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() + 0x9E3779B97F4A7C15ull;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        z ^= z >> 31;
+        z >>= kMergeCountBits;
+        return z == 0 ? 1ull : (unsigned long long)z;
+    }();
+    return tag;
 }
 
 size_t workspace_bytes_for(const kv_cache *c, const Plan &p) { return ws_layout(c, p).total; }
@@ -863,6 +895,8 @@ kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_
     a.v = c->v;
     a.ws_acc = w.total ? (float *)(ws + w.acc) : nullptr;
     a.ws_ml = w.total ? (float *)(ws + w.ml) : nullptr;
+    a.counters = w.total ? (unsigned long long *)(ws + w.cnt) : nullptr;
+    a.merge_tag = merge_tag();
     a.batch = c->batch;
     a.T = T;
     a.hq = q_heads;
@@ -934,12 +968,13 @@ kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_
         hipError_t e = side_stream_join(c->side, st);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (side stream)");
     }
-    // rows split across work groups: merge their partials
+    // rows split across work groups and not merged in the decode kernel:
+    // merge their partials
     std::vector<std::pair<const RowPlan *, int>> split_rows;
     for (auto &r : p.pre)
         if (r.nsplit > 1) split_rows.push_back({&r, prefill_cols(c->dtype, c->head_dim)});
     for (auto &r : p.dec)
-        if (r.nsplit > 1) split_rows.push_back({&r, p.dec_cols});
+        if (r.nsplit > kMergeMaxSplits) split_rows.push_back({&r, p.dec_cols});
     for (size_t lo = 0; lo < split_rows.size(); lo += kMaxRows) {
         CombineArgs m{};
         m.out = out;

@@ -75,10 +75,12 @@ GQAKV_HD inline Item decode_item_at(const RowFields &f, int r, int item, int hkv
     it.t_end = imin(it.t0 + tq, n);
     // bottom-right rule: the tile's last query sits at base + t_end - 1 and sees
     // keys up to that position, never past the row's length; with a window the
-    // tile's first query sees nothing below base + t0 - window + 1
+    // tile's first query sees nothing below base + t0 - window + 1. Splits
+    // of lsplit keys each, the last one up to the tile's last key (the
+    // planner may hand it more than lsplit)
     const int keys_hi = it.base + it.t_end;
     it.k_begin = range_start(it.base + it.t0, window) + it.split * f.lsplit;
-    it.k_end = imin(it.k_begin + f.lsplit, keys_hi);
+    it.k_end = it.split == it.nsplit - 1 ? keys_hi : imin(it.k_begin + f.lsplit, keys_hi);
     it.rec0 = f.pbase < 0 ? -1 : f.pbase + ((it.kvh * it.nq + it.qtile) * it.nsplit + it.split) * cols;
     return it;
 }

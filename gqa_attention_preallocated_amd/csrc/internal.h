@@ -12,6 +12,13 @@ namespace gqakv {
 
 constexpr int kMaxRows = 64;
 
+// Decode rows split into at most this many work groups are merged by the last
+// of them to finish, in the decode kernel; rows split further (only under a
+// small keys-per-split policy) are merged by the combine kernel.
+constexpr int kMergeMaxSplits = 64;
+constexpr int kMergeCountBits = 8;     // arrivals field of a counter word (> log2 kMergeMaxSplits)
+static_assert(kMergeMaxSplits < (1 << kMergeCountBits), "arrival count field too narrow");
+
 // ---------------------------------------------------------------- append
 struct AppendTable {
     int32_t n_rows;
@@ -102,6 +109,12 @@ struct AttnArgs {
     const void *k_new;
     const void *v_new;
     int32_t *lens_dev;         // optional
+    // rows split across decode work groups into at most kMergeMaxSplits
+    // splits are merged in the decode kernel: one arrival counter per (row,
+    // kv head, query tile) group, at the group's first partial record / cols;
+    // each word holds (merge_tag << kMergeCountBits) | arrivals
+    unsigned long long *counters;
+    unsigned long long merge_tag;   // nonzero, below 2^(64 - kMergeCountBits), fixed per process
     int32_t tree;              // 1: the new tokens of each row form a tree (parent below)
     int8_t parent[kMaxRows][kMaxTreeNodes];   // per launch row: parent node of node u, -1 = the committed prefix
     AttnRows rows;

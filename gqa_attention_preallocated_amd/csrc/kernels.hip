@@ -313,9 +313,13 @@ __device__ inline uint2 quant8(const uint4 &x, float inv) {
 // (A search over the table would chain one dependent load per step before a
 // block could issue its first memory access.)
 // ---------------------------------------------------------------------------
+// Entry `lane` of a launch table of kMaxRows (or kMaxRows + 1) entries, pad
+// past the n in use. The load does not wait for n: every lane's entry lies
+// inside the table.
 __device__ inline int lane_entry(const int32_t *table, int n, int pad) {
     const int l = threadIdx.x & 63;
-    return l < n ? table[l] : pad;
+    const int v = table[l];
+    return l < n ? v : pad;
 }
 
 // find_row over `first` (nondecreasing, first[0] = 0) with one ballot
@@ -337,24 +341,51 @@ __device__ inline Item decode_item_wave(const AttnRows &R, int item, int hkv, in
     return decode_item_at(f, r, item, hkv, group, cols, window);
 }
 
+// Partial records written and read by different work groups of one launch
+// (the decode kernel's merge): agent-scope accesses, which reach the
+// device-coherent level rather than stopping in (or hitting a stale line of)
+// one XCD's L2. Two floats per access: 64 bits is the widest atomic access.
+__device__ inline float2 coherent_load2(const float *p) {
+    const unsigned long long u =
+        __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_bit_cast(float2, u);
+}
+__device__ inline void coherent_store2(float *p, float x, float y) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), __builtin_bit_cast(unsigned long long, make_float2(x, y)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Split partials: the nsplit partial records rec, rec + stride, ... of one
 // column hold unnormalised sums acc and (running max m in log2 units, sum l).
-// Their outputs d..d+3 are merged by log-sum-exp in split order, eight splits
+// Their outputs d..d+3 are merged by log-sum-exp in split order, BATCH splits
 // per batch of loads, and normalised (0 when no split saw a key).
-template <int D>
+// COHERENT: the records were written in this launch by other work groups
+// (the decode kernel's in-kernel merge), else by an earlier launch. Eight
+// splits per batch (one round trip for up to eight), four in the decode
+// kernel's merge at d < 64, whose smaller instances would otherwise lose
+// occupancy to these registers.
+template <int D, bool COHERENT = false>
 __device__ inline f32x4 merge_partials(const float *ws_acc, const float *ws_ml, int64_t rec, int64_t stride,
                                        int nsplit, int d) {
+    constexpr int BATCH = COHERENT && D < 64 ? 4 : 8;
     float M = -INFINITY, L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
-        float2 ml[8];
-        float4 x[8];
+    for (int s0 = 0; s0 < nsplit; s0 += BATCH) {
+        float2 ml[BATCH];
+        float4 x[BATCH];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < BATCH; ++j) {
             const int64_t rs = rec + (int64_t)(s0 + j) * stride;
             if (s0 + j < nsplit) {
-                ml[j] = *reinterpret_cast<const float2 *>(ws_ml + rs * 2);
-                x[j] = *reinterpret_cast<const float4 *>(ws_acc + rs * D + d);
+                if constexpr (COHERENT) {
+                    const float *px = ws_acc + rs * D + d;
+                    ml[j] = coherent_load2(ws_ml + rs * 2);
+                    const float2 lo = coherent_load2(px), hi = coherent_load2(px + 2);
+                    x[j] = make_float4(lo.x, lo.y, hi.x, hi.y);
+                } else {
+                    ml[j] = *reinterpret_cast<const float2 *>(ws_ml + rs * 2);
+                    x[j] = *reinterpret_cast<const float4 *>(ws_acc + rs * D + d);
+                }
             } else {
                 ml[j] = make_float2(-INFINITY, 0.f);
                 x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -362,13 +393,13 @@ __device__ inline f32x4 merge_partials(const float *ws_acc, const float *ws_ml, 
         }
         float bm = M;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bm = fmaxf(bm, ml[j].x);
+        for (int j = 0; j < BATCH; ++j) bm = fmaxf(bm, ml[j].x);
         if (bm == -INFINITY) continue;            // no split so far saw a key of this column
         const float c = fast_exp2(M - bm);        // M = -inf: c = 0 (acc and L are still 0)
         acc *= c;
         L *= c;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < BATCH; ++j) {
             const float w = fast_exp2(ml[j].x - bm);   // a split that saw no key: w = 0
             acc[0] += w * x[j].x; acc[1] += w * x[j].y; acc[2] += w * x[j].z; acc[3] += w * x[j].w;
             L += w * ml[j].y;
@@ -715,8 +746,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         // kv_append_attention: this item's share of the new tokens goes into
         // the cache here; the attention below reads them from k_new / v_new
         write_new_tokens<D, F8, PG, NROWB>(a, it, tid, 64 * W);
-        // the first item of a row sets the row's device length
-        if (a.lens_dev != nullptr && tid == 0 && blockIdx.x == a.rows.item0[it.r])
+        // the first item of a row (kv head 0, split 0, its last query tile)
+        // sets the row's device length
+        if (a.lens_dev != nullptr && tid == 0 && it.kvh == 0 && it.split == 0 && it.qtile == it.nq - 1)
             a.lens_dev[it.b] = a.rows.len[it.r];
     }
     // an E4M3 cache stands for code x scale of the head: the K scale joins the
@@ -954,9 +986,68 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
                 E *op = column_out<E>(a, it, col, D) + d;
                 O::store4(op, o * (L > 0.f ? 1.f / L : 0.f));
             } else {
-                const int64_t rec = it.rec0 + col;
-                *reinterpret_cast<float4 *>(a.ws_acc + rec * D + d) = make_float4(o[0], o[1], o[2], o[3]);
-                if (d == 0) *reinterpret_cast<float2 *>(a.ws_ml + rec * 2) = make_float2(M, L);
+                // a partial of a row split across work groups, written through
+                // to the device-coherent level for the merge below
+                float *ap = a.ws_acc + (it.rec0 + col) * (int64_t)D + d;
+                coherent_store2(ap, o[0], o[1]);
+                coherent_store2(ap + 2, o[2], o[3]);
+                if (d == 0) coherent_store2(a.ws_ml + (it.rec0 + col) * 2, M, L);
+            }
+        }
+    }
+
+    // ---- rows split across work groups: the last work group of a (row, kv
+    //      head, query tile) group to finish merges the group's nsplit
+    //      partials, in split order (so the result does not depend on which
+    //      group is last). Each work group waits until its partial stores have
+    //      completed, which for stores at agent scope means they are at the
+    //      device-coherent level, then counts its arrival with one atomic add;
+    //      the last arrival reads every partial at agent scope. No cache
+    //      write-back is needed (a release fence per work group measured
+    //      slower than a separate merge launch). A counter word holds (tag,
+    //      arrivals) and the last arrival leaves it at (tag, 0), ready for the
+    //      next call on this workspace (or the next replay of a captured
+    //      graph). The tag is fixed for the process: a word that does not hold
+    //      it, or holds a count the group cannot reach, is memory no call has
+    //      used yet. Such an arrival's add is void: it counts itself with an
+    //      exchange that takes the word as zero arrivals, and the first
+    //      exchange rewrites the whole word (adds that landed on the old word
+    //      are discarded with it; their arrivals count themselves the same way).
+    if (it.rec0 >= 0 && it.nsplit <= kMergeMaxSplits) {
+        __shared__ int last_arrival;
+        const int64_t rec_first = it.rec0 - (int64_t)it.split * a.cols;
+        unsigned long long *cnt = a.counters + rec_first / a.cols;
+        __builtin_amdgcn_s_waitcnt(0x0f70);            // vmcnt(0): this thread's partial stores completed
+        __syncthreads();
+        if (tid == 0) {
+            constexpr unsigned long long kCountMask = (1ull << kMergeCountBits) - 1;
+            const unsigned long long base = a.merge_tag << kMergeCountBits;
+            auto arrivals = [&](unsigned long long w) -> int {   // -1: a word no call has used yet
+                return (w & ~kCountMask) == base && (int)(w & kCountMask) < it.nsplit ? (int)(w & kCountMask) : -1;
+            };
+            unsigned long long old = __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int arrived = arrivals(old);
+            if (arrived < 0) {
+                old += 1;                                   // the word as this add left it (a first guess)
+                unsigned long long want;
+                do {
+                    arrived = arrivals(old);
+                    if (arrived < 0) arrived = 0;
+                    want = base | (unsigned long long)(arrived + 1);
+                } while (!__hip_atomic_compare_exchange_strong(cnt, &old, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT));
+            }
+            const bool last = arrived + 1 == it.nsplit;
+            if (last) __hip_atomic_store(cnt, base, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_arrival = last;
+        }
+        __syncthreads();
+        if (last_arrival) {
+            for (int task = tid; task < a.cols * DC; task += 64 * W) {
+                const int col = task / DC, d = (task % DC) * 4;
+                if (column_position(it, col, a.group, a.cols) < 0) continue;
+                O::store4(column_out<E>(a, it, col, D) + d,
+                          merge_partials<D, true>(a.ws_acc, a.ws_ml, rec_first + col, a.cols, it.nsplit, d));
             }
         }
     }

@@ -247,8 +247,13 @@ kv_status gqa_attention_workspace_size(const kv_cache *c, int32_t q_heads, int32
  *   workspace     device scratch of at least gqa_attention_workspace_size()
  *                 bytes (may be NULL when that size is 0). It holds the
  *                 unnormalised partial outputs and (max, sum) pairs of key
- *                 ranges split across work groups; every partial is written
- *                 before it is read in the same call, so the contents need no
+ *                 ranges split across work groups, and one arrival counter per
+ *                 split (row, KV head, query tile) of the decode kernel, whose
+ *                 last work group merges the partials. Every partial is
+ *                 written before it is read in the same call, and a counter
+ *                 word that no call of this process has left behind is
+ *                 recognised as such (it matches a random per-process 56-bit
+ *                 tag only with probability 2^-56), so the contents need no
  *                 initialisation. Two calls in flight at once must not share a
  *                 workspace.
  * A call with prefill-kernel rows runs its decode kernel and its zero fill of
@@ -331,7 +336,7 @@ kv_status kv_append_attention_tree(kv_cache *c, const void *k_new, const void *v
  * one after the other. Call it with the cache's device current: the scratch
  * of the current device is used. Every call on a GPU shares that GPU's
  * scratch, which keeps whatever the last call left (nothing in it needs to
- * start at any value: each partial is written before it is read): two calls
+ * start at any value, as for a workspace): two calls
  * that may overlap on one GPU, on different streams or from different
  * threads, race and must be ordered by the caller.
  * Returns KV_ERR_WORKSPACE, with nothing changed, for a call whose partials

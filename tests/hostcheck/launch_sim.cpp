@@ -9,7 +9,9 @@
 //     (the copy kernel, or in kv_append_attention the attention kernels'
 //     items, each token by exactly one item),
 //   * each attention call writes every output row (b, h, t) exactly once,
-//   * each split partial is written once before the combine kernel reads it.
+//   * each split partial is written once before the combine kernel, or the
+//     last work group of its group in the decode kernel, reads it; each
+//     group's arrival counter lies in the workspace past the partials.
 // Buffers are fake addresses registered by the test; nothing is dereferenced.
 
 #include <hip/hip_runtime_api.h>
@@ -36,6 +38,7 @@ std::vector<Region> g_regions;
 std::vector<std::string> g_errors;
 std::map<uintptr_t, int> g_out_rows;   // start address of an output row -> writes
 std::map<int64_t, int> g_records;      // partial record -> writes
+std::map<int64_t, int> g_arrivals;     // decode merge counter -> work groups arrived
 std::map<uintptr_t, int> g_appended;   // 16-byte chunk of K -> writes
 std::vector<int32_t> g_lens_dev;
 std::vector<int32_t> g_table;          // the device block table of a paged cache, as the kernels see it
@@ -69,6 +72,7 @@ void hostcheck_reset() {
     g_errors.clear();
     g_out_rows.clear();
     g_records.clear();
+    g_arrivals.clear();
     g_appended.clear();
     g_lens_dev.clear();
     g_table.clear();
@@ -81,6 +85,7 @@ void hostcheck_region(uintptr_t base, size_t size, const char *name) { g_regions
 void hostcheck_begin_call() {
     g_out_rows.clear();
     g_records.clear();
+    g_arrivals.clear();
 }
 
 int hostcheck_error_count() { return (int)g_errors.size(); }
@@ -227,7 +232,9 @@ hipError_t launch_set_lens(int32_t *lens_dev, const LensTable &t, hipStream_t) {
     return hipSuccess;
 }
 
-static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, int cache_elem) {
+// merge: the decode kernel, whose work groups of a split row count their
+// arrivals and the last one merges the row's partials
+static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, int cache_elem, bool merge) {
     ++g_launches;
     const AttnRows &R = a.rows;
     const int D = a.head_dim;
@@ -286,8 +293,10 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
         const int first_pos = it.base + it.t0;
         const int lo_visible = windowed ? std::max(0, first_pos - a.window + 1) : 0;
         if (it.split == 0 && range_start(first_pos, a.window) > lo_visible) err("attention: range starts too late");
-        if (it.split == it.nsplit - 1 && it.k_begin + R.lsplit[r] < it.base + it.t_end)
+        if (it.split == it.nsplit - 1 && it.k_end != it.base + it.t_end)
             err("attention: splits do not cover the item's keys");
+        if (it.split < it.nsplit - 1 && it.k_end > it.k_begin + R.lsplit[r])
+            err("attention: a split longer than lsplit before the last");
         // every visible key is still held by the ring (positions >= len - max_len)
         if (windowed && lo_visible < std::max(0, R.len[r] - a.max_len)) err("attention: window key evicted");
         const int64_t head = (int64_t)it.b * a.hkv + it.kvh;
@@ -366,6 +375,34 @@ static void sim_attention(const AttnArgs &a, int cols, int key_tile, int elem, i
                 g_records[rec]++;
             }
         }
+        if (merge && it.rec0 >= 0 && it.nsplit <= kMergeMaxSplits) {
+            const int64_t rec_first = (int64_t)it.rec0 - (int64_t)it.split * cols;
+            if (rec_first < 0 || rec_first % cols != 0) err("decode merge: group's first record misplaced");
+            const unsigned long long *cnt = a.counters + rec_first / cols;
+            access(cnt, 8, "ws", "decode merge counter");
+            if ((uintptr_t)cnt < (uintptr_t)(a.ws_ml + a.records * 2)) err("decode merge: counter overlaps partials");
+            if (a.merge_tag == 0 || (a.merge_tag >> (64 - kMergeCountBits)) != 0) err("decode merge: bad tag");
+            const int arrived = ++g_arrivals[rec_first / cols];
+            if (arrived > it.nsplit) err("decode merge: more arrivals than splits");
+            if (arrived == it.nsplit) {
+                // the last work group reads every split's record of each column and writes the output
+                for (int col = 0; col < cols; ++col) {
+                    if (column_position(it, col, a.group, cols) < 0) continue;
+                    for (int s = 0; s < it.nsplit; ++s) {
+                        const int64_t rs = rec_first + col + (int64_t)s * cols;
+                        auto w = g_records.find(rs);
+                        if (w == g_records.end() || w->second != 1)
+                            err("decode merge: partial not written exactly once");
+                        access(a.ws_acc + rs * D, D * 4, "ws", "decode merge acc");
+                        access(a.ws_ml + rs * 2, 8, "ws", "decode merge m,l");
+                    }
+                    const int t = column_t(it, col, a.group), h = column_head(it, col, a.group);
+                    const char *o = (const char *)a.out + (((int64_t)it.b * a.hq + h) * a.T + t) * row_bytes;
+                    access(o, row_bytes, "out", "decode merge out");
+                    g_out_rows[(uintptr_t)o]++;
+                }
+            }
+        }
     }
 }
 
@@ -375,7 +412,7 @@ hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, h
     if (nsub != 1 && nsub != 2 && nsub != 4) err("decode: bad subtile count");
     if (a.cols < a.group || a.cols > 16 * nsub || (nsub > 1 && a.cols <= 8 * nsub))
         err("decode: item columns do not fit the kernel's tiling");
-    sim_attention(a, a.cols, kDecodeKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
+    sim_attention(a, a.cols, kDecodeKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1), true);
     return hipSuccess;
 }
 
@@ -383,7 +420,7 @@ hipError_t launch_prefill(int dtype, int head_dim, const AttnArgs &a, hipStream_
     if (head_dim != a.head_dim) err("prefill: head_dim mismatch");
     if (a.cols != prefill_cols(dtype, head_dim)) err("prefill: columns differ from the kernel's");
     if (a.fuse) err("prefill: fused append requested");
-    sim_attention(a, a.cols, kPrefillKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1));
+    sim_attention(a, a.cols, kPrefillKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1), false);
     return hipSuccess;
 }
 

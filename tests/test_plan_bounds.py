@@ -679,3 +679,29 @@ def test_noalloc_entry_point(sim):
     assert sim.hostcheck_launches() == launches
     lens = (ctypes.c_int32 * B)()
     assert sim.kv_get_lens(c.h, lens) == 0 and list(lens) == c.lens.tolist()
+
+
+@pytest.mark.parametrize("kps, splits, combine", [(0, 32, False), (1024, 8, False), (128, 64, False),
+                                                  (64, 128, True)])
+def test_split_decode_rows_merge(sim, kps, splits, combine):
+    """Decode rows split into at most 64 work groups are merged by the last of
+    them in the decode kernel (after every partial of its group was written,
+    with the group's arrival counter in the workspace past the partials): no
+    combine launch. Rows split further, which only a small keys-per-split
+    policy asks for, go through the combine kernel. Either way every output
+    row is written exactly once."""
+    B, hk, hq, d = 4, 2, 8, 128
+    c = SimCache(sim, B, hk, 8192 + 64, d, "bf16", hq, 4096)
+    for call in _prefix_calls([8191] * B):
+        c.append(call["T"], call["n_new"])
+    sim.kv_cache_set_policy(c.h, 1, kps)
+    c.append(1, [1] * B)
+    launches = sim.hostcheck_launches()
+    ws = c.attention(1, [1] * B)
+    c.check(1)
+    assert sim.hostcheck_launches() - launches == (2 if combine else 1)
+    # partials (d + 2 floats per record, 16 columns per group and split), then
+    # one counter word per group and split, each region 256-byte aligned
+    records = B * hk * splits * 16
+    up = lambda x: (x + 255) // 256 * 256
+    assert ws == up(up(records * d * 4) + records * 8) + records // 16 * 8
