@@ -925,19 +925,10 @@ kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_
         a.v_new = fused->v_new;
         a.lens_dev = c->lens_dev;
     }
-    for (size_t lo = 0; lo < p.dec.size(); lo += kMaxRows) {
-        fill_attn_rows(p.dec, lo, std::min(p.dec.size(), lo + kMaxRows), c->kv_heads, a.rows);
-        if (a.tree) {
-            std::memset(a.parent, -1, sizeof a.parent);
-            for (int j = 0; j < a.rows.n_rows; ++j)
-                for (int u = 0; u < a.rows.nnew[j]; ++u)
-                    a.parent[j][u] = (int8_t)parents[(int64_t)a.rows.b[j] * T + u];
-        }
-        hipError_t e = launch_decode((int)c->dtype, c->head_dim, p.nsub, a, dec_stream);
-        if (e != hipSuccess) return device_fail(e, "gqa_attention (decode kernel)");
-    }
-
-    // padded slots: independent of the attention kernels
+    // padded slots: independent of the attention kernels. First on the
+    // stream: in a mixed call the fill's small work groups share CUs with
+    // the prefill kernel's (which leave registers to spare), where a decode
+    // work group has to wait for a whole CU
     for (size_t lo = 0; lo < p.pad_rows.size(); lo += kMaxRows) {
         ZeroArgs z{};
         z.out = out;
@@ -956,6 +947,18 @@ kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_
         hipError_t e = launch_zero_fill(z, dec_stream);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (zero fill)");
     }
+    for (size_t lo = 0; lo < p.dec.size(); lo += kMaxRows) {
+        fill_attn_rows(p.dec, lo, std::min(p.dec.size(), lo + kMaxRows), c->kv_heads, a.rows);
+        if (a.tree) {
+            std::memset(a.parent, -1, sizeof a.parent);
+            for (int j = 0; j < a.rows.n_rows; ++j)
+                for (int u = 0; u < a.rows.nnew[j]; ++u)
+                    a.parent[j][u] = (int8_t)parents[(int64_t)a.rows.b[j] * T + u];
+        }
+        hipError_t e = launch_decode((int)c->dtype, c->head_dim, p.nsub, a, dec_stream);
+        if (e != hipSuccess) return device_fail(e, "gqa_attention (decode kernel)");
+    }
+
     a.cols = prefill_cols(c->dtype, c->head_dim);
     a.tree = 0;
     a.fuse = 0;                // prefill rows were appended by the copy kernel

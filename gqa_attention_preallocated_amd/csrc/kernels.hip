@@ -1367,15 +1367,18 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
 
     int64_t row_next = 0;                              // cache row of tile i + 1
     if (ntiles > 0) {
+        // K(0), V(0) and K(1) go out together: one round trip to memory
+        // before the first tile, not two (a short item is mostly this)
         const int64_t row0 = km.row(it.k_begin);
-        load(kreg, kbase, row0, it.k_begin);
-        store(kreg, lds_k[0]);
-        __syncthreads();
+        uint4 k0[PCH];
+        load(k0, kbase, row0, it.k_begin);
+        load(vreg, vbase, row0, it.k_begin);
         if (ntiles > 1) {
             row_next = km.row(it.k_begin + KT);
             load(kreg, kbase, row_next, it.k_begin + KT);
         }
-        load(vreg, vbase, row0, it.k_begin);
+        store(k0, lds_k[0]);
+        __syncthreads();
         if (!grp_a && wave_last >= 0) scores(lds_k[0], sc);   // group A computes them in its first step
     }
     int sl = 0;                                        // slot of K(i) and V(i): i % SL
