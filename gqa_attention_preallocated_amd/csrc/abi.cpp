@@ -157,8 +157,12 @@ void plan_attention(const kv_cache *c, const int32_t *lens, int32_t q_heads, int
             pre_rows.push_back(b);
         }
     }
-    // decode: one column width for the launch, at least G so a tile holds a query
+    // decode: one column width for the launch, at least G so a tile holds a query.
+    // A float32 cache at d = 128 takes at most two subtiles (32 columns) when G
+    // allows: its four-subtile instance runs out of registers and spills, so
+    // wider rows get more query tiles instead (their keys are read once per tile)
     int need = std::max(max_dec_cols, G);
+    if (c->dtype == KV_DTYPE_F32 && c->head_dim == 128 && G <= 32) need = std::min(need, 32);
     p.nsub = need <= 16 ? 1 : (need <= 32 ? 2 : 4);
     p.dec_cols = 16 * p.nsub;
 

@@ -192,6 +192,20 @@ template <> struct Op<float> {
         v[j] = x;
         v[j + 1] = y;
     }
+    // the contraction over the first 16 elements only (4 of the 8 steps)
+    __device__ static inline f32x4 mma16(const vec &a, const vec &b, f32x4 c) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+        return c;
+    }
+    // vt_operand over a 16-key tile: keys 4g..4g+3 only (elements 4..7 unused)
+    __device__ static inline vec vt_operand16(const unsigned char *tile, int rs, int d0, int lane) {
+        const int lr = lane & 15, lg = lane >> 4;
+        vec r = zero();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = *reinterpret_cast<const float *>(tile + (lg * 4 + j) * rs + (d0 + lr) * 4);
+        return r;
+    }
     static constexpr int kPad = 16;
     // A operand of O^T += V^T P^T (see the bf16 version): 8 single-element reads
     __device__ static inline vec vt_operand(const unsigned char *tile, int rs, int key0, int d0, int lane) {
@@ -617,14 +631,17 @@ struct ColState {
 // range, and acc / l is unchanged algebraically.
 constexpr float kRescaleLog2 = 8.f;
 
-// One online-softmax step for the 8 raw scores q.k a lane holds for its
-// column (two 16-key blocks: v[0..3] = keys 4g..4g+3, v[4..7] = keys
-// 16+4g..16+4g+3 of a 32-key chunk, g = lane/16); invisible keys are -inf.
-// c = log2(e)/sqrt(d) > 0, so the max of raw scores scaled by c is the max of
-// the scaled scores. Writes p = exp2(v*c - m) and updates the state.
-template <int NB>
-__device__ inline void softmax_step(const float (&v)[8], float c, ColState &st, f32x4 (&acc)[NB], f32x8 &p) {
-    float tmax = smax8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+// One online-softmax step for the N raw scores q.k a lane holds for its
+// column (16-key blocks: v[0..3] = keys 4g..4g+3, v[4..7] = keys
+// 16+4g..16+4g+3 of a 32-key tile, g = lane/16; N = 4: one 16-key block);
+// invisible keys are -inf. c = log2(e)/sqrt(d) > 0, so the max of raw scores
+// scaled by c is the max of the scaled scores. Writes p = exp2(v*c - m)
+// (p[N..7] untouched) and updates the state.
+template <int NB, int N>
+__device__ inline void softmax_step(const float (&v)[N], float c, ColState &st, f32x4 (&acc)[NB], f32x8 &p) {
+    static_assert(N == 4 || N == 8, "one or two 16-key blocks");
+    float tmax = N == 8 ? smax8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7])
+                        : smax(smax(v[0], v[1]), smax(v[2], v[3 % N]));
     tmax = wave_max_across_groups(tmax) * c;
     if (tmax > st.m + kRescaleLog2) {             // st.m = -inf: the first visible key sets it
         const float alpha = fast_exp2(st.m - tmax);   // 0 when st.m = -inf (acc and l are still 0)
@@ -636,36 +653,12 @@ __device__ inline void softmax_step(const float (&v)[8], float c, ColState &st, 
     const float m_use = (st.m == -INFINITY) ? 0.f : st.m;   // no key seen yet: every p is 0
     float lsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < N; ++j) {
         const float e = fast_exp2(fmaf(v[j], c, -m_use));
         p[j] = e;
         lsum += e;
     }
     st.l += lsum;
-}
-
-// The same step over the N = 16 scores of two 32-key chunks (v[0..7] chunk
-// 0, v[8..15] chunk 1, each in the layout above): one max, one rescale test.
-// The running sum is not kept here: the caller accumulates it on the matrix
-// core as an extra output block (acc[NB - 1]), so the rescale covers it too.
-template <int NB, int N>
-__device__ inline void softmax_tile(const float (&v)[N], float c, ColState &st, f32x4 (&acc)[NB], f32x8 &p0,
-                                    f32x8 &p1) {
-    float t0 = smax8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
-    float t1 = smax8(v[8], v[9], v[10], v[11], v[12], v[13], v[14], v[15]);
-    const float tmax = wave_max_across_groups(smax(t0, t1)) * c;
-    if (tmax > st.m + kRescaleLog2) {
-        const float alpha = fast_exp2(st.m - tmax);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
-        st.m = tmax;
-    }
-    const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        p0[j] = fast_exp2(fmaf(v[j], c, -m_use));
-        p1[j] = fast_exp2(fmaf(v[8 + j], c, -m_use));
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -686,7 +679,11 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     using S = Stor<E, F8>;
     using vec = typename O::vec;
     using kraw = typename S::kraw;
-    constexpr int KT = kDecodeKeyTile;            // 32 keys per tile
+    // 32 keys per tile; float32 at d = 128 takes 16-key tiles (half the K and V
+    // registers: with 32 its instances spilled), two per planner tile
+    constexpr int KT = (std::is_same<E, float>::value && D == 128) ? 16 : kDecodeKeyTile;
+    constexpr int NKS = KT / 16;                  // 16-key blocks per tile
+    static_assert(kDecodeKeyTile % KT == 0 && (NKS == 2 || std::is_same<E, float>::value), "key tile");
     constexpr int KC = D >= 32 ? D / 32 : 1;      // 32-wide chunks of d
     constexpr int NB = D / 16;                    // 16-row blocks of O^T
     // columns per work item: a.cols (the planner's choice, at most 16 * NSUB;
@@ -772,7 +769,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     //      the same bytes outstanding per CU (up to 32 columns; wider items
     //      have no registers to spare).
     constexpr int PF = (F8 && NSUB <= 2) ? 2 : 1;
-    kraw kA[2][KC], kB[2][KC];
+    kraw kA[NKS][KC], kB[NKS][KC];
     uint4 vA[VCH], vB[VCH];
     // a tile's keys are consecutive cache rows from km.row(tile): no tile
     // wraps (ring capacities are multiples of kRingAlign, pages of kMinPage,
@@ -786,13 +783,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         vnew = reinterpret_cast<const unsigned char *>(a.v_new) + r0 * NROWB;
     }
     const float kinv = F8 ? a.k_inv[it.kvh] : 1.f, vinv = F8 ? a.v_inv[it.kvh] : 1.f;
-    auto load_tile_as = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile, auto fresh) {
+    auto load_tile_as = [&](kraw (&kop)[NKS][KC], uint4 (&vreg)[VCH], int tile, auto fresh) {
         constexpr bool FRESH = decltype(fresh)::value;
         const int64_t row0 = km.row(tile);
         const unsigned char *kt = kbase + row0 * CROWB;
         const unsigned char *vt = vbase + row0 * CROWB;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
             const int key = ks * 16 + lr;
             const bool ok = tile + key < w_end;
             const bool nw = FRESH && tile + key >= it.base;       // a new key: from k_new
@@ -834,7 +831,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
                          : load_stream(vt + key * CROWB + part * 16);
         }
     };
-    auto load_tile = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
+    auto load_tile = [&](kraw (&kop)[NKS][KC], uint4 (&vreg)[VCH], int tile) {
         if (a.fuse && tile + KT > it.base) {               // uniform over the wave
             load_tile_as(kop, vreg, tile, std::true_type{});
             return;
@@ -870,7 +867,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     for (int s = 0; s < NSUB; ++s) lo_key[s] = pos[s] - a.window + 1 > 0 ? pos[s] - a.window + 1 : 0;
 
     // compute the tile held in (kop, vreg), refilling the set with the next tile
-    auto process = [&](kraw (&kop)[2][KC], uint4 (&vreg)[VCH], int tile) {
+    auto process = [&](kraw (&kop)[NKS][KC], uint4 (&vreg)[VCH], int tile) {
         // V tile into this wave's LDS stage (row-major, padded, compute type)
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
@@ -881,9 +878,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
             }
         }
         // ---- S^T = K Q^T for the 32 keys
-        f32x4 sc[NSUB][2];
+        f32x4 sc[NSUB][NKS];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
             vec kv[KC];
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) kv[kc] = S::widen_k(kop[ks][kc]);
@@ -904,9 +901,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         f32x8 p[NSUB];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
-            float v[8];
+            float v[4 * NKS];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = sc[s][j >> 2][j & 3];
+            for (int j = 0; j < 4 * NKS; ++j) v[j] = sc[s][j >> 2][j & 3];
             if (need_mask) {                      // uniform over the wave
                 // key j is visible iff lo_key <= j <= pos and j < the range end,
                 // and (tree) j is committed or on the column's path to the root
@@ -914,14 +911,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
                 const int lim_lo = lo_key[s] - (tile + lg * 4);
                 const int node0 = tile + lg * 4 - it.base;        // node index of offset 0
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
+                for (int j = 0; j < 4 * NKS; ++j) {
                     const int off = (j >> 2) * 16 + (j & 3);
                     const int u = node0 + off;
                     const bool on_path = u < 0 || (u < 32 && ((anc[s] >> (u & 31)) & 1u));
                     v[j] = (off < lim && off >= lim_lo && (!a.tree || on_path)) ? v[j] : -INFINITY;
                 }
             }
-            softmax_step<NB>(v, score_c, st[s], acc[s], p[s]);
+            softmax_step<NB, 4 * NKS>(v, score_c, st[s], acc[s], p[s]);
         }
 
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's V stores have landed
@@ -930,9 +927,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         // ---- O^T += V^T P^T
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const vec vt = O::vt_operand(lds, RS, 0, nb * 16, lane);
+            if constexpr (NKS == 2) {
+                const vec vt = O::vt_operand(lds, RS, 0, nb * 16, lane);
 #pragma unroll
-            for (int s = 0; s < NSUB; ++s) acc[s][nb] = O::mma(vt, O::from_f32(p[s]), acc[s][nb]);
+                for (int s = 0; s < NSUB; ++s) acc[s][nb] = O::mma(vt, O::from_f32(p[s]), acc[s][nb]);
+            } else {                              // float32, 16-key tiles
+                const vec vt = O::vt_operand16(lds, RS, nb * 16, lane);
+#pragma unroll
+                for (int s = 0; s < NSUB; ++s) acc[s][nb] = O::mma16(vt, p[s], acc[s][nb]);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);   // V^T reads done before the stage is overwritten
         __builtin_amdgcn_wave_barrier();
@@ -1562,7 +1565,14 @@ static hipError_t decode_d(int nsub, const AttnArgs &a, hipStream_t s) {
     const dim3 grid(a.rows.total_items), block(64 * W);
     switch (nsub) {
         case 1: hipLaunchKernelGGL((decode_kernel<E, D, 1, W, F8, PG>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<E, D, 2, W, F8, PG>), grid, block, 0, s, a); break;
+        case 2:
+            // float32 at d = 128: two subtiles need more registers than two
+            // waves per SIMD leave a wave; one wave per SIMD
+            if constexpr (std::is_same<E, float>::value && D == 128)
+                hipLaunchKernelGGL((decode_kernel<E, D, 2, 4, F8, PG>), grid, dim3(256), 0, s, a);
+            else
+                hipLaunchKernelGGL((decode_kernel<E, D, 2, W, F8, PG>), grid, block, 0, s, a);
+            break;
         case 4:
             // four subtiles over rows of 256 bytes or more (in the compute type)
             // need more registers than two waves per SIMD leave a wave, and

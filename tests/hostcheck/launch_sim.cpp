@@ -43,6 +43,7 @@ std::map<uintptr_t, int> g_appended;   // 16-byte chunk of K -> writes
 std::vector<int32_t> g_lens_dev;
 std::vector<int32_t> g_table;          // the device block table of a paged cache, as the kernels see it
 int64_t g_launches = 0;
+int g_last_nsub = 0;                   // subtiles of the last decode launch
 
 void err(const std::string &m) {
     if (g_errors.size() < 64) g_errors.push_back(m);
@@ -93,6 +94,8 @@ int hostcheck_error_count() { return (int)g_errors.size(); }
 const char *hostcheck_error(int i) { return (i >= 0 && i < (int)g_errors.size()) ? g_errors[i].c_str() : ""; }
 
 int64_t hostcheck_launches() { return g_launches; }
+
+int hostcheck_last_decode_nsub() { return g_last_nsub; }
 
 // Writes recorded for output row i of an [rows, row_bytes] array at base.
 int hostcheck_out_row_writes(uintptr_t base, int64_t i, int64_t row_bytes) {
@@ -410,6 +413,7 @@ hipError_t launch_decode(int dtype, int head_dim, int nsub, const AttnArgs &a, h
     if (head_dim != a.head_dim) err("decode: head_dim mismatch");
     // the kernel's register tiling holds 16 * nsub columns; the items use a.cols of them
     if (nsub != 1 && nsub != 2 && nsub != 4) err("decode: bad subtile count");
+    g_last_nsub = nsub;
     if (a.cols < a.group || a.cols > 16 * nsub || (nsub > 1 && a.cols <= 8 * nsub))
         err("decode: item columns do not fit the kernel's tiling");
     sim_attention(a, a.cols, kDecodeKeyTile, dtype == 0 ? 4 : 2, dtype == 0 ? 4 : (dtype == 1 ? 2 : 1), true);

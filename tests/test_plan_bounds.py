@@ -705,3 +705,30 @@ def test_split_decode_rows_merge(sim, kps, splits, combine):
     records = B * hk * splits * 16
     up = lambda x: (x + 255) // 256 * 256
     assert ws == up(up(records * d * 4) + records * 8) + records // 16 * 8
+
+
+@pytest.mark.parametrize("G, T, want", [(4, 16, 2), (4, 8, 2), (4, 4, 1), (8, 8, 2), (64, 1, 4)])
+def test_float32_d128_decode_subtiles(sim, G, T, want):
+    """A float32 cache at d = 128 runs the decode kernel with at most two
+    16-column subtiles when the group allows (its four-subtile instance spills
+    registers): a tree call over G*T > 32 columns gets more query tiles
+    instead, each reading the row's keys. Every output is still written once."""
+    B, hk, d = 2, 2, 128
+    c = SimCache(sim, B, hk, 1024, d, "f32", hk * G, 512)
+    for call in _prefix_calls([300, 77]):
+        c.append(call["T"], call["n_new"])
+    P, I32 = ctypes.c_void_p, ctypes.c_int32
+    sim.gqa_attention_tree.argtypes = [P, P, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32), P, P,
+                                       ctypes.c_size_t, P]
+    sim.hostcheck_last_decode_nsub.restype = ctypes.c_int
+    c.append(T, [T] * B)
+    size = ctypes.c_size_t()
+    assert sim.gqa_attention_workspace_size(c.h, hk * G, T, _i32([T] * B), ctypes.byref(size)) == 0
+    parents = [t - 1 for t in range(T)] * B                     # a chain per row
+    sim.hostcheck_begin_call()
+    a = c.addr
+    st = sim.gqa_attention_tree(c.h, P(a["q"]), hk * G, T, _i32([T] * B), _i32(parents), P(a["out"]),
+                                P(a["ws"]), size.value, None)
+    assert st == 0, sim.kv_last_error()
+    c.check(T)
+    assert sim.hostcheck_last_decode_nsub() == want
