@@ -353,6 +353,41 @@ def run_shard(torch, reps=40):
             "config": {"workload": "llama8b_decode_b32_s4096_tp{1,2,4,8}", "batch": 32, "keys": 4097, "T": 1}}
 
 
+def run_stride(torch, reps=60):
+    """The Llama decode step (B=32, 4,096 cached + 1 new token, one
+    kv_append_attention call, two caches in turn) on linear caches of several
+    max_len: the rows of a (row, KV head) sit max_len x 256 bytes apart."""
+    from gqa_attention_preallocated_amd import KVCache, append_attention
+    import workloads as W
+    sh = W.LLAMA8B_DECODE
+    B, hq, hkv, d = sh.batch, sh.q_heads, sh.kv_heads, sh.head_dim
+    n = [1] * B
+    g = torch.Generator(device="cuda").manual_seed(3)
+    q = (torch.randn(B, hq, 1, d, device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    kn = (torch.randn(B, hkv, 1, d, device="cuda", generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    nbytes = attention_bytes([DECODE_CACHED + 1] * B, n, hq, hkv, d, 1)
+    res = {}
+    for ml in (8192, 8256, 8448, 12288, 16384, 4160):
+        caches = [KVCache(B, hkv, ml, d, device_lens=False) for _ in range(2)]
+        for i, c in enumerate(caches):
+            _fill_gpu_random(torch, c, [DECODE_CACHED] * B, 60 + i)
+
+        def step(i):
+            c = caches[i & 1]
+            append_attention(c, kn, kn, q, n, out=out)
+            c.truncate([DECODE_CACHED] * B)
+
+        t = _time_calls(torch, step, reps)
+        res[str(ml)] = {"us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1)}
+        del caches
+        torch.cuda.empty_cache()
+    for v in res.values():
+        v["vs_8192"] = round(v["us"] / res["8192"]["us"], 4)
+    return {"metric": "decode step time against the cache's max_len (row stride)", "unit": "us",
+            "max_len": res, "config": {"workload": "llama8b_decode_b32_s4096", "batch": B, "keys": DECODE_CACHED + 1}}
+
+
 def run_window(torch, reps=30):
     """Sliding-window decode: B=32 rows, a 4,096-key window over an 8,192-slot ring
     after 20,000 tokens (the ring has wrapped twice), T=1. Two caches in turn."""
@@ -790,7 +825,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "verify", "ragged", "append", "window", "fp8", "tree",
-                                       "paged", "shard", "probe", "cpu"],
+                                       "paged", "shard", "stride", "probe", "cpu"],
                     default=None,
                     help="time one workload only (for profiling); prints its own JSON line")
     ap.add_argument("--copy-probe", action="store_true",
@@ -827,9 +862,10 @@ def main():
     if args.only == "ragged":
         print(json.dumps({"ragged": [run_ragged(torch, seed) for seed in (4, 5, 6)]}), flush=True)
         return
-    if args.only in ("prefill", "verify", "append", "window", "fp8", "tree", "paged", "shard", "probe"):
+    if args.only in ("prefill", "verify", "append", "window", "fp8", "tree", "paged", "shard", "stride", "probe"):
         fn = {"prefill": run_prefill, "verify": run_verify, "append": run_append, "window": run_window,
-              "fp8": run_fp8, "tree": run_tree, "paged": run_paged, "shard": run_shard, "probe": run_probe}[args.only]
+              "fp8": run_fp8, "tree": run_tree, "paged": run_paged, "shard": run_shard, "stride": run_stride,
+              "probe": run_probe}[args.only]
         print(json.dumps({args.only: fn(torch)}), flush=True)
         return
     res = run_decode(torch, args.steps, args.warmup)

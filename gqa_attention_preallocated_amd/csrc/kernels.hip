@@ -700,7 +700,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char lds_all[LDS_BYTES];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    // the wave index is the same in every lane: a scalar, so that tile
+    // positions and per-wave conditions stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     unsigned char *lds = lds_all + wave * STAGE;
     const Item it = decode_item_wave(a.rows, blockIdx.x, a.hkv, a.group, a.cols, a.window);
@@ -867,7 +869,36 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     for (int s = 0; s < NSUB; ++s) lo_key[s] = pos[s] - a.window + 1 > 0 ? pos[s] - a.window + 1 : 0;
 
     // compute the tile held in (kop, vreg), refilling the set with the next tile
-    auto process = [&](kraw (&kop)[NKS][KC], uint4 (&vreg)[VCH], int tile) {
+    // The order the waves take the tiles in. Each round gives wave w its
+    // tile w; rows of a linear or ring cache sit max_len keys apart, and with
+    // a row stride that is not a multiple of 2 MiB the work groups, which all
+    // start together, would stream from unrelated offsets modulo 2 MiB: the
+    // decode step measured up to 23% slower (max_len 8,256 against 8,192). So
+    // a work group starts at the full round that brings its byte address back
+    // to the offset a 2 MiB-aligned row would have, takes the full rounds from
+    // there, wrapping around, and the last, partial round last. phys maps a
+    // tile of the plain order to the tile read in its place. A 2 MiB-aligned
+    // row, and a paged cache (whose pages are not rows), keep the plain order;
+    // so does an E4M3 cache (two tiles in flight), whose registers are full.
+    const int full_end = it.k_begin + (it.k_end - it.k_begin) / step * step;   // end of the full rounds
+    int rot = 0;                                                     // keys the full rounds are rotated by
+    if constexpr (!PG && PF == 1) {
+        constexpr int64_t kPhase = int64_t(1) << 21;
+        const int64_t base = (((int64_t)it.b * a.hkv + it.kvh) * a.max_len + it.k_begin % a.max_len) * CROWB;
+        const int64_t rb = (int64_t)step * CROWB;                   // bytes of one round
+        const int rf = (full_end - it.k_begin) / step;
+        if (rf > 1) rot = (int)((((kPhase - (base & (kPhase - 1))) & (kPhase - 1)) / rb) % rf) * step;
+    }
+    auto phys = [&](int vt) {
+        if (vt >= full_end) return vt;
+        const int t = vt + rot;
+        return t >= full_end ? t - (full_end - it.k_begin) : t;
+    };
+
+    // compute the tile held in (kop, vreg), refilling the set with the next
+    // one; vt is the tile in the plain order, tile the one read in its place
+    auto process = [&](kraw (&kop)[NKS][KC], uint4 (&vreg)[VCH], int vt) {
+        const int tile = phys(vt);
         // V tile into this wave's LDS stage (row-major, padded, compute type)
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
@@ -892,7 +923,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
                 sc[s][ks] = c;
             }
         }
-        if (tile + PF * step < w_end) load_tile(kop, vreg, tile + PF * step);
+        if (vt + PF * step < w_end) load_tile(kop, vreg, phys(vt + PF * step));
 
         // ---- mask (only tiles that straddle the diagonal or the range end),
         //      online softmax in log2 units
@@ -941,9 +972,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         __builtin_amdgcn_wave_barrier();
     };
 
-    if (w_begin < w_end) load_tile(kA, vA, w_begin);
+    if (w_begin < w_end) load_tile(kA, vA, phys(w_begin));
     if constexpr (PF == 2) {
-        if (w_begin + step < w_end) load_tile(kB, vB, w_begin + step);
+        if (w_begin + step < w_end) load_tile(kB, vB, phys(w_begin + step));
         for (int tile = w_begin; tile < w_end; tile += 2 * step) {
             process(kA, vA, tile);
             if (tile + step < w_end) process(kB, vB, tile + step);
