@@ -125,6 +125,10 @@ template <> struct Op<bf16_t> {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
     __device__ static inline vec from_f32(const f32x8 &x) { return __builtin_convertvector(x, vec); }
+    // c * v, rounded to bfloat16 (to nearest, even)
+    __device__ static inline vec scaled(const vec &v, float c) {
+        return __builtin_convertvector(__builtin_convertvector(v, f32x8) * c, vec);
+    }
     // elements j, j+1 (j even) of an operand from two floats (one packed convert)
     __device__ static inline void set_pair(vec &v, int j, float x, float y) {
         typedef __attribute__((ext_vector_type(2))) float f32x2;
@@ -188,6 +192,7 @@ template <> struct Op<float> {
         return c;
     }
     __device__ static inline vec from_f32(const f32x8 &x) { return x; }
+    __device__ static inline vec scaled(const vec &v, float c) { return v * c; }
     __device__ static inline void set_pair(vec &v, int j, float x, float y) {
         v[j] = x;
         v[j + 1] = y;
@@ -1170,14 +1175,26 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     // an E4M3 cache: the K scale joins the score scale, the V scale the output
     const float score_c = F8 ? a.scale_log2 * a.k_scale[it.kvh] : a.scale_log2;
     const float out_c = F8 ? a.v_scale[it.kvh] : 1.f;
+    // Q carries the score scale (log2 e / sqrt(d), times the K scale of an
+    // E4M3 cache), so the score MFMAs give scaled scores; their accumulators
+    // start at -m, the column's reference max, so they give the exponent of
+    // p = exp2(s - m) directly ([GQA] "A strong answer": the 1/sqrt(d) scale).
+    // Rounding q * scale to bfloat16 adds an error of at most 2^-9 of each
+    // product q_i k_i, with random signs over the d terms of a score.
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) qop[s][kc] = O::scaled(qop[s][kc], score_c);
 
     // acc[s][0..NB-1]: O^T rows; acc[s][NB]: a 16-row block whose A operand is
     // all ones, so each of its rows is the column's running sum of p (the
     // same rounded p the output rows use)
     f32x4 acc[NS][NB + 1];
     ColState st[NS];
+    f32x4 bias[NS];          // -m, the reference the scores are taken against (0 before any key)
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
+        bias[s] = f32x4{0.f, 0.f, 0.f, 0.f};
         st[s].m = -INFINITY;
         st[s].l = 0.f;
 #pragma unroll
@@ -1273,10 +1290,9 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
 
     // probability pair u (0..4 NS - 1) of chunk ch of tile i: subtile u / 4,
     // elements 2 (u % 4) and 2 (u % 4) + 1, packed into the PV operand
-    auto prob_pair = [&](int ch, int u, float m) {
+    auto prob_pair = [&](int ch, int u) {
         const int ps = u >> 2, j = (u & 3) * 2;
-        O::set_pair(pb[ch][ps], j, fast_exp2(fmaf(sc[ch][ps][j >> 2][j & 3], score_c, -m)),
-                    fast_exp2(fmaf(sc[ch][ps][(j + 1) >> 2][(j + 1) & 3], score_c, -m)));
+        O::set_pair(pb[ch][ps], j, fast_exp2(sc[ch][ps][j >> 2][j & 3]), fast_exp2(sc[ch][ps][(j + 1) >> 2][(j + 1) & 3]));
     };
     // S^T of one 64-key tile for the wave's columns (prologue: tile 0)
     auto scores = [&](const unsigned char *kl, f32x4 (&out)[2][NS][2]) {
@@ -1286,7 +1302,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
             for (int ks = 0; ks < 2; ++ks) {
                 const int krow = ch * 32 + ks * 16 + lr;
 #pragma unroll
-                for (int s = 0; s < NS; ++s) out[ch][s][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < NS; ++s) out[ch][s][ks] = bias[s];
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
                     const int d0 = kc * 32 + lg * 8;
@@ -1340,7 +1356,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
                 const int q = g - pv_idx(g), kc = q >> 1, ks = q & 1;
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    const f32x4 c0 = kc == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : scn[c][s][ks];
+                    const f32x4 c0 = kc == 0 ? bias[s] : scn[c][s][ks];
                     scn[c][s][ks] = O::mma(op[g % 3], qop[s][kc], c0);
                 }
             }
@@ -1359,7 +1375,8 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     auto softmax_block = [&](int tile) {
         if ((tile + KT > it.k_end) || (tile + KT - 1 > wave_pos_min) || (tile <= wave_pos_max - a.window))
             mask(tile, sc);                              // uniform over the wave
-        float tmax[NS];
+        // the tile's max per column, relative to the reference the scores carry
+        float rel[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             float q4[4];
@@ -1368,23 +1385,36 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
                 const f32x4 x = sc[qq >> 1][s][qq & 1];
                 q4[qq] = smax(smax(smax(x[0], x[1]), x[2]), x[3]);
             }
-            tmax[s] = wave_max_across_groups(smax(smax(smax(q4[0], q4[1]), q4[2]), q4[3])) * score_c;
+            rel[s] = wave_max_across_groups(smax(smax(smax(q4[0], q4[1]), q4[2]), q4[3]));
         }
-        float m_use[NS];
+        // the reference moves (rarely) when a column's first keys arrive or its
+        // max outgrows the reference by more than kRescaleLog2: acc, holding every
+        // PV product of the tiles before, takes the factor, and this tile's
+        // scores are taken against the new reference
+        bool moves = false;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            if (tmax[s] > st[s].m + kRescaleLog2) {
-                const float alpha = fast_exp2(st[s].m - tmax[s]);   // st.m = -inf: 0 (acc is still 0)
+        for (int s = 0; s < NS; ++s) moves |= st[s].m == -INFINITY ? rel[s] > -INFINITY : rel[s] > kRescaleLog2;
+        if (__builtin_amdgcn_ballot_w64(moves)) {        // uniform over the wave
 #pragma unroll
-                for (int nb = 0; nb <= NB; ++nb) acc[s][nb] *= alpha;
-                st[s].m = tmax[s];
+            for (int s = 0; s < NS; ++s) {
+                float shift = 0.f;
+                if (st[s].m == -INFINITY ? rel[s] > -INFINITY : rel[s] > kRescaleLog2) {
+                    const float m_new = (st[s].m == -INFINITY ? 0.f : st[s].m) + rel[s];
+                    const float alpha = fast_exp2(st[s].m - m_new);  // st.m = -inf: 0 (acc is still 0)
+#pragma unroll
+                    for (int nb = 0; nb <= NB; ++nb) acc[s][nb] *= alpha;
+                    st[s].m = m_new;
+                    shift = rel[s];
+                    bias[s] = f32x4{-m_new, -m_new, -m_new, -m_new};
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sc[q >> 1][s][q & 1] -= shift;
             }
-            m_use[s] = (st[s].m == -INFINITY) ? 0.f : st[s].m;    // no key seen yet: every p is 0
         }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
-            for (int u = 0; u < 4 * NS; ++u) prob_pair(ch, u, m_use[u >> 2]);
+            for (int u = 0; u < 4 * NS; ++u) prob_pair(ch, u);
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch)
 #pragma unroll
