@@ -101,6 +101,13 @@ __device__ inline uint4 buffer_load_stream(__amdgpu_buffer_rsrc_t r, int off) {
     const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
     return make_uint4(t.x, t.y, t.z, t.w);
 }
+// The same load without the non-temporal hint: for data other work groups of
+// the same XCD read soon after (the query tiles of one (row, KV head) in the
+// prefill kernel), so their reads hit in L2.
+__device__ inline uint4 buffer_load_shared(__amdgpu_buffer_rsrc_t r, int off) {
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 // ---------------------------------------------------------------------------
 // element traits: 8-element MFMA operands and the 16x16 product
@@ -1211,7 +1218,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     auto load = [&](uint4 (&reg)[PCH], const unsigned char *base, int64_t row0, int tile) {
         const __amdgpu_buffer_rsrc_t r = buffer_view(base + row0 * CROWB, imin(it.k_end - tile, KT) * CROWB);
 #pragma unroll
-        for (int i = 0; i < PCH; ++i) reg[i] = buffer_load_stream(r, (tid + NT * i) * 16);
+        for (int i = 0; i < PCH; ++i) reg[i] = buffer_load_shared(r, (tid + NT * i) * 16);
     };
     // into LDS in the compute type (an E4M3 chunk of 16 codes becomes 32 bytes)
     auto store = [&](const uint4 (&reg)[PCH], unsigned char *dst) {
