@@ -1146,7 +1146,12 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     // conditions and tile positions stay in scalar registers and branches
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
-    const Item it = decode_item_wave(a.rows, blockIdx.x, a.hkv, a.group, C, a.window);
+    Item it = decode_item_wave(a.rows, blockIdx.x, a.hkv, a.group, C, a.window);
+    // the key range in scalar registers: the loop's tile positions, cache rows
+    // and buffer views are then scalar work (more item fields in scalar
+    // registers made this instance spill)
+    it.k_begin = __builtin_amdgcn_readfirstlane(it.k_begin);
+    it.k_end = __builtin_amdgcn_readfirstlane(it.k_end);
 
     int pos[NS];
     vec qop[NS][KC];
@@ -1199,9 +1204,11 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     f32x4 acc[NS][NB + 1];
     ColState st[NS];
     f32x4 bias[NS];          // -m, the reference the scores are taken against (0 before any key)
+    float thr[NS];           // the reference moves when the tile's max exceeds it: -inf before any key
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         bias[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        thr[s] = -INFINITY;
         st[s].m = -INFINITY;
         st[s].l = 0.f;
 #pragma unroll
@@ -1382,7 +1389,8 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     auto softmax_block = [&](int tile) {
         if ((tile + KT > it.k_end) || (tile + KT - 1 > wave_pos_min) || (tile <= wave_pos_max - a.window))
             mask(tile, sc);                              // uniform over the wave
-        // the tile's max per column, relative to the reference the scores carry
+        // the max of the lane's scores per subtile, relative to the reference
+        // the scores carry
         float rel[NS];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -1392,25 +1400,29 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
                 const f32x4 x = sc[qq >> 1][s][qq & 1];
                 q4[qq] = smax(smax(smax(x[0], x[1]), x[2]), x[3]);
             }
-            rel[s] = wave_max_across_groups(smax(smax(smax(q4[0], q4[1]), q4[2]), q4[3]));
+            rel[s] = smax(smax(smax(q4[0], q4[1]), q4[2]), q4[3]);
         }
         // the reference moves (rarely) when a column's first keys arrive or its
-        // max outgrows the reference by more than kRescaleLog2: acc, holding every
-        // PV product of the tiles before, takes the factor, and this tile's
-        // scores are taken against the new reference
+        // max outgrows the reference by more than kRescaleLog2 (thr): acc,
+        // holding every PV product of the tiles before, takes the factor, and
+        // this tile's scores are taken against the new reference. A column's
+        // max exceeds thr iff one of its lanes' maxima does, so the column
+        // maxima are only formed when some lane's does.
         bool moves = false;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) moves |= st[s].m == -INFINITY ? rel[s] > -INFINITY : rel[s] > kRescaleLog2;
+        for (int s = 0; s < NS; ++s) moves |= rel[s] > thr[s];
         if (__builtin_amdgcn_ballot_w64(moves)) {        // uniform over the wave
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 float shift = 0.f;
-                if (st[s].m == -INFINITY ? rel[s] > -INFINITY : rel[s] > kRescaleLog2) {
+                rel[s] = wave_max_across_groups(rel[s]);
+                if (rel[s] > thr[s]) {
                     const float m_new = (st[s].m == -INFINITY ? 0.f : st[s].m) + rel[s];
                     const float alpha = fast_exp2(st[s].m - m_new);  // st.m = -inf: 0 (acc is still 0)
 #pragma unroll
                     for (int nb = 0; nb <= NB; ++nb) acc[s][nb] *= alpha;
                     st[s].m = m_new;
+                    thr[s] = kRescaleLog2;
                     shift = rel[s];
                     bias[s] = f32x4{-m_new, -m_new, -m_new, -m_new};
                 }
