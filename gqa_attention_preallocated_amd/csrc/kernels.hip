@@ -1160,11 +1160,16 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     for (int s = 0; s < NS; ++s) {
         const int col = wave * WC + s * 16 + lr;
         pos[s] = column_position(it, col, a.group, C);
-        const E *qp = pos[s] >= 0 ? column_q<E>(a, it, col, D) : nullptr;
+        // every lane loads from a valid address (a padding column from the
+        // item's column 0, which is always real); the zeros of padding
+        // columns and of d0 >= D are selected when Q is scaled, after the
+        // first K and V loads have gone out (loads under a condition made the
+        // compiler wait for each before issuing the next)
+        const E *qp = column_q<E>(a, it, pos[s] >= 0 ? col : 0, D);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             const int d0 = kc * 32 + lg * 8;
-            qop[s][kc] = (qp != nullptr && d0 < D) ? O::gload(qp + d0) : O::zero();
+            qop[s][kc] = O::gload(qp + (d0 < D ? d0 : 0));
         }
     }
     {
@@ -1192,11 +1197,16 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     // start at -m, the column's reference max, so they give the exponent of
     // p = exp2(s - m) directly ([GQA] "A strong answer": the 1/sqrt(d) scale).
     // Rounding q * scale to bfloat16 adds an error of at most 2^-9 of each
-    // product q_i k_i, with random signs over the d terms of a score.
+    // product q_i k_i, with random signs over the d terms of a score. The
+    // scaling waits for the Q loads, so it runs after the first K and V loads
+    // are issued (one memory round trip for both).
+    auto scale_q = [&]() {
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) qop[s][kc] = O::scaled(qop[s][kc], score_c);
+            for (int kc = 0; kc < KC; ++kc)
+                qop[s][kc] = (pos[s] >= 0 && kc * 32 + lg * 8 < D) ? O::scaled(qop[s][kc], score_c) : O::zero();
+    };
 
     // acc[s][0..NB-1]: O^T rows; acc[s][NB]: a 16-row block whose A operand is
     // all ones, so each of its rows is the column's running sum of p (the
@@ -1460,6 +1470,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
             row_next = km.row(it.k_begin + KT);
             load(kreg, kbase, row_next, it.k_begin + KT);
         }
+        scale_q();
         store(k0, lds_k[0]);
         __syncthreads();
         if (!grp_a && wave_last >= 0) scores(lds_k[0], sc);   // group A computes them in its first step
