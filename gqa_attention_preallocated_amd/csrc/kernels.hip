@@ -717,7 +717,11 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     unsigned char *lds = lds_all + wave * STAGE;
-    const Item it = decode_item_wave(a.rows, blockIdx.x, a.hkv, a.group, a.cols, a.window);
+    Item it = decode_item_wave(a.rows, blockIdx.x, a.hkv, a.group, a.cols, a.window);
+    // the key range in scalar registers: tile positions and cache rows are
+    // then scalar work
+    it.k_begin = __builtin_amdgcn_readfirstlane(it.k_begin);
+    it.k_end = __builtin_amdgcn_readfirstlane(it.k_end);
 
     // this wave's share of the item's keys: every W-th 32-key tile from its
     // own, so at any time the work group streams one contiguous run of K and
@@ -802,18 +806,29 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         const int64_t row0 = km.row(tile);
         const unsigned char *kt = kbase + row0 * CROWB;
         const unsigned char *vt = vbase + row0 * CROWB;
+        // A key at or past the range end (only in a range's last tile) is read
+        // from the range's last key when the tile holds no new keys: its score
+        // is masked and its p is 0, so any finite row will do, and the loads
+        // then need no condition (loads under a condition made the compiler
+        // wait for the tiles in flight before the next tile's work)
+        const int last = w_end - 1 - tile;                    // >= 0: the tile starts below w_end
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int key = ks * 16 + lr;
             const bool ok = tile + key < w_end;
             const bool nw = FRESH && tile + key >= it.base;       // a new key: from k_new
             const int t = tile + key - it.base;
+            const int keyc = ok ? key : last;
             if constexpr (KPAIR) {
 #pragma unroll
                 for (int j = 0; j < KC / 2; ++j) {
                     const int off = dmap(2 * j);                  // codes: byte = d
-                    const uint4 w = !ok ? make_uint4(0, 0, 0, 0)
-                                  : nw ? new_chunk<F8, NROWB>(knew, t, off, kinv) : load_stream(kt + key * CROWB + off);
+                    uint4 w;
+                    if constexpr (FRESH)
+                        w = !ok ? make_uint4(0, 0, 0, 0)
+                            : nw ? new_chunk<F8, NROWB>(knew, t, off, kinv) : load_stream(kt + key * CROWB + off);
+                    else
+                        w = load_stream(kt + keyc * CROWB + off);
                     kop[ks][2 * j] = make_uint2(w.x, w.y);
                     kop[ks][2 * j + 1] = make_uint2(w.z, w.w);
                 }
@@ -821,7 +836,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
                     const int d0 = dmap(kc);
-                    if (!(ok && d0 < D)) {
+                    if constexpr (!FRESH && D >= 32) {
+                        kop[ks][kc] = S::load_k(kt + keyc * CROWB + d0 * S::kBytes);   // d0 < D for every lane
+                    } else if (!(ok && d0 < D)) {
                         kop[ks][kc] = S::zero_k();
                     } else if (nw) {
                         if constexpr (F8)
@@ -838,11 +855,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         for (int i = 0; i < VCH; ++i) {
             const int c = lane + 64 * i;
             const int key = c / CPK, part = c % CPK;
-            const bool ok = (c < KT * CPK) && (tile + key < w_end);
-            const bool nw = FRESH && tile + key >= it.base;
-            vreg[i] = !ok ? make_uint4(0, 0, 0, 0)
-                    : nw ? new_chunk<F8, NROWB>(vnew, tile + key - it.base, part * 16, vinv)
-                         : load_stream(vt + key * CROWB + part * 16);
+            if constexpr (!FRESH && (KT * CPK) % 64 == 0) {
+                vreg[i] = load_stream(vt + (tile + key < w_end ? key : last) * CROWB + part * 16);
+            } else {
+                const bool ok = (c < KT * CPK) && (tile + key < w_end);
+                const bool nw = FRESH && tile + key >= it.base;
+                vreg[i] = !ok ? make_uint4(0, 0, 0, 0)
+                        : nw ? new_chunk<F8, NROWB>(vnew, tile + key - it.base, part * 16, vinv)
+                             : load_stream(vt + key * CROWB + part * 16);
+            }
         }
     };
     auto load_tile = [&](kraw (&kop)[NKS][KC], uint4 (&vreg)[VCH], int tile) {
@@ -909,7 +930,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
 
     // compute the tile held in (kop, vreg), refilling the set with the next
     // one; vt is the tile in the plain order, tile the one read in its place
-    auto process = [&](kraw (&kop)[NKS][KC], uint4 (&vreg)[VCH], int vt) {
+    // STEADY: the caller knows the tile PF rounds ahead exists and holds no
+    // new keys, so the prefetch needs no test and takes the plain load path
+    auto process = [&](kraw (&kop)[NKS][KC], uint4 (&vreg)[VCH], int vt, auto steady) {
         const int tile = phys(vt);
         // V tile into this wave's LDS stage (row-major, padded, compute type)
 #pragma unroll
@@ -935,7 +958,14 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
                 sc[s][ks] = c;
             }
         }
-        if (vt + PF * step < w_end) load_tile(kop, vreg, phys(vt + PF * step));
+        if constexpr (decltype(steady)::value) {
+            load_tile_as(kop, vreg, phys(vt + PF * step), std::false_type{});
+            // the loads stay here: left to itself the scheduler sank them past
+            // the pair's second tile, a tile's work later
+            __builtin_amdgcn_sched_barrier(0);
+        } else if (vt + PF * step < w_end) {
+            load_tile(kop, vreg, phys(vt + PF * step));
+        }
 
         // ---- mask (only tiles that straddle the diagonal or the range end),
         //      online softmax in log2 units
@@ -987,12 +1017,22 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
     if (w_begin < w_end) load_tile(kA, vA, phys(w_begin));
     if constexpr (PF == 2) {
         if (w_begin + step < w_end) load_tile(kB, vB, phys(w_begin + step));
-        for (int tile = w_begin; tile < w_end; tile += 2 * step) {
-            process(kA, vA, tile);
-            if (tile + step < w_end) process(kB, vB, tile + step);
+        // While both tiles of a pair and both of their prefetches exist and
+        // hold no new keys, every pass issues the same loads: the compiler can
+        // then count them and waits for the current tile only, leaving the
+        // next one in flight (with a test on each prefetch it waited for both)
+        const int lim = a.fuse ? imin(w_end, it.base) : w_end;
+        int tile = w_begin;
+        for (; tile + 3 * step + KT <= lim; tile += 2 * step) {
+            process(kA, vA, tile, std::true_type{});
+            process(kB, vB, tile + step, std::true_type{});
+        }
+        for (; tile < w_end; tile += 2 * step) {
+            process(kA, vA, tile, std::false_type{});
+            if (tile + step < w_end) process(kB, vB, tile + step, std::false_type{});
         }
     } else {
-        for (int tile = w_begin; tile < w_end; tile += step) process(kA, vA, tile);
+        for (int tile = w_begin; tile < w_end; tile += step) process(kA, vA, tile, std::false_type{});
     }
 
     // ---- merge the W waves' partials in LDS, one 16-column subtile at a time
