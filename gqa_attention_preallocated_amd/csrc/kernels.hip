@@ -1014,24 +1014,35 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(AttnArgs a) {
         __builtin_amdgcn_wave_barrier();
     };
 
-    if (w_begin < w_end) load_tile(kA, vA, phys(w_begin));
     if constexpr (PF == 2) {
-        if (w_begin + step < w_end) load_tile(kB, vB, phys(w_begin + step));
         // While both tiles of a pair and both of their prefetches exist and
         // hold no new keys, every pass issues the same loads: the compiler can
         // then count them and waits for the current tile only, leaving the
-        // next one in flight (with a test on each prefetch it waited for both)
+        // next one in flight (with a test on each prefetch it waited for both).
+        // The first two tiles then take the same plain loads, on a path of
+        // their own, so the loop is entered with the loads in flight that it
+        // loops with.
         const int lim = a.fuse ? imin(w_end, it.base) : w_end;
         int tile = w_begin;
-        for (; tile + 3 * step + KT <= lim; tile += 2 * step) {
-            process(kA, vA, tile, std::true_type{});
-            process(kB, vB, tile + step, std::true_type{});
+        if (w_begin + 3 * step + KT <= lim) {
+            load_tile_as(kA, vA, phys(w_begin), std::false_type{});
+            __builtin_amdgcn_sched_barrier(0);     // all of A's loads before B's, as in the loop
+            load_tile_as(kB, vB, phys(w_begin + step), std::false_type{});
+            __builtin_amdgcn_sched_barrier(0);
+            for (; tile + 3 * step + KT <= lim; tile += 2 * step) {
+                process(kA, vA, tile, std::true_type{});
+                process(kB, vB, tile + step, std::true_type{});
+            }
+        } else {
+            if (w_begin < w_end) load_tile(kA, vA, phys(w_begin));
+            if (w_begin + step < w_end) load_tile(kB, vB, phys(w_begin + step));
         }
         for (; tile < w_end; tile += 2 * step) {
             process(kA, vA, tile, std::false_type{});
             if (tile + step < w_end) process(kB, vB, tile + step, std::false_type{});
         }
     } else {
+        if (w_begin < w_end) load_tile(kA, vA, phys(w_begin));
         for (int tile = w_begin; tile < w_end; tile += step) process(kA, vA, tile, std::false_type{});
     }
 
