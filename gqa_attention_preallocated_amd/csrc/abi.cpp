@@ -971,49 +971,59 @@ kv_status attention_launch(kv_cache *c, const Plan &p, const void *q, int32_t q_
         hipError_t e = launch_prefill((int)c->dtype, c->head_dim, a, st);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (prefill kernel)");
     }
+    // rows split across work groups and not merged in the decode kernel:
+    // merge their partials. The prefill rows' merge needs only the prefill
+    // kernel, so it runs on the caller's stream before the join, beside the
+    // decode kernel's tail; decode rows split more than kMergeMaxSplits ways
+    // (only a small fixed keys-per-split policy asks for that) wait for it.
+    auto combine = [&](const std::vector<std::pair<const RowPlan *, int>> &split_rows) -> kv_status {
+        for (size_t lo = 0; lo < split_rows.size(); lo += kMaxRows) {
+            CombineArgs m{};
+            m.out = out;
+            m.ws_acc = a.ws_acc;
+            m.ws_ml = a.ws_ml;
+            m.batch = c->batch;
+            m.T = T;
+            m.hq = q_heads;
+            m.hkv = c->kv_heads;
+            m.group = p.group;
+            m.head_dim = c->head_dim;
+            m.records = p.records;
+            const size_t hi = std::min(split_rows.size(), lo + kMaxRows);
+            m.rows.n_rows = (int32_t)(hi - lo);
+            int32_t blocks = 0;
+            for (size_t i = lo; i < hi; ++i) {
+                const RowPlan &r = *split_rows[i].first;
+                const int j = (int)(i - lo);
+                m.rows.b[j] = r.b;
+                m.rows.nnew[j] = r.nnew;
+                m.rows.nsplit[j] = r.nsplit;
+                m.rows.pbase[j] = (int32_t)r.pbase;
+                m.rows.cols[j] = split_rows[i].second;
+                m.rows.blk0[j] = blocks;
+                const int per_group = (int)ceil_div((int64_t)split_rows[i].second * (c->head_dim / 4), 256);
+                blocks += c->kv_heads * r.nq * per_group;
+            }
+            m.rows.blk0[m.rows.n_rows] = blocks;
+            m.rows.total_blocks = blocks;
+            hipError_t e = launch_combine((int)c->dtype, c->head_dim, m, st);
+            if (e != hipSuccess) return device_fail(e, "gqa_attention (combine kernel)");
+        }
+        return KV_OK;
+    };
+    std::vector<std::pair<const RowPlan *, int>> pre_split, dec_split;
+    for (auto &r : p.pre)
+        if (r.nsplit > 1) pre_split.push_back({&r, prefill_cols(c->dtype, c->head_dim)});
+    for (auto &r : p.dec)
+        if (r.nsplit > kMergeMaxSplits) dec_split.push_back({&r, p.dec_cols});
+    kv_status cs = combine(pre_split);
+    if (cs != KV_OK) return cs;
     if (mixed) {
         hipError_t e = side_stream_join(c->side, st);
         if (e != hipSuccess) return device_fail(e, "gqa_attention (side stream)");
     }
-    // rows split across work groups and not merged in the decode kernel:
-    // merge their partials
-    std::vector<std::pair<const RowPlan *, int>> split_rows;
-    for (auto &r : p.pre)
-        if (r.nsplit > 1) split_rows.push_back({&r, prefill_cols(c->dtype, c->head_dim)});
-    for (auto &r : p.dec)
-        if (r.nsplit > kMergeMaxSplits) split_rows.push_back({&r, p.dec_cols});
-    for (size_t lo = 0; lo < split_rows.size(); lo += kMaxRows) {
-        CombineArgs m{};
-        m.out = out;
-        m.ws_acc = a.ws_acc;
-        m.ws_ml = a.ws_ml;
-        m.batch = c->batch;
-        m.T = T;
-        m.hq = q_heads;
-        m.hkv = c->kv_heads;
-        m.group = p.group;
-        m.head_dim = c->head_dim;
-        m.records = p.records;
-        const size_t hi = std::min(split_rows.size(), lo + kMaxRows);
-        m.rows.n_rows = (int32_t)(hi - lo);
-        int32_t blocks = 0;
-        for (size_t i = lo; i < hi; ++i) {
-            const RowPlan &r = *split_rows[i].first;
-            const int j = (int)(i - lo);
-            m.rows.b[j] = r.b;
-            m.rows.nnew[j] = r.nnew;
-            m.rows.nsplit[j] = r.nsplit;
-            m.rows.pbase[j] = (int32_t)r.pbase;
-            m.rows.cols[j] = split_rows[i].second;
-            m.rows.blk0[j] = blocks;
-            const int per_group = (int)ceil_div((int64_t)split_rows[i].second * (c->head_dim / 4), 256);
-            blocks += c->kv_heads * r.nq * per_group;
-        }
-        m.rows.blk0[m.rows.n_rows] = blocks;
-        m.rows.total_blocks = blocks;
-        hipError_t e = launch_combine((int)c->dtype, c->head_dim, m, st);
-        if (e != hipSuccess) return device_fail(e, "gqa_attention (combine kernel)");
-    }
+    cs = combine(dec_split);
+    if (cs != KV_OK) return cs;
     return KV_OK;
 }
 }  // namespace
