@@ -367,6 +367,14 @@ __device__ inline Item decode_item_wave(const AttnRows &R, int item, int hkv, in
     return decode_item_at(f, r, item, hkv, group, cols, window);
 }
 
+// A wave-uniform 64-bit value moved to scalar registers (each half through
+// its own readfirstlane, as unsigned 32-bit values: the builtin returns int)
+__device__ inline uint64_t uniform_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // Partial records written and read by different work groups of one launch
 // (the decode kernel's merge): agent-scope accesses, which reach the
 // device-coherent level rather than stopping in (or hitting a stale line of)
@@ -1240,6 +1248,20 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     const unsigned char *kbase = reinterpret_cast<const unsigned char *>(a.k);
     const unsigned char *vbase = reinterpret_cast<const unsigned char *>(a.v);
     KeyRows<PG> km(a, it, it.k_begin);
+    if constexpr (!PG) {
+        // linear and ring caches: K and V of the (row, KV head) block from
+        // scalar registers (the item's fields are vector values), so a tile's
+        // address is scalar arithmetic, not 64-bit vector work per load
+        const int64_t off = (int64_t)uniform_u64((uint64_t)km.head_row) * CROWB;
+        kbase += off;
+        vbase += off;
+    }
+    // cache row of a tile's first key: within the block above (linear and
+    // ring), or of the whole pool (paged)
+    auto tile_row = [&](int tile) -> int64_t {
+        if constexpr (PG) return km.row(tile);
+        else return tile % a.max_len;
+    };
     // an E4M3 cache: the K scale joins the score scale, the V scale the output
     const float score_c = F8 ? a.scale_log2 * a.k_scale[it.kvh] : a.scale_log2;
     const float out_c = F8 ? a.v_scale[it.kvh] : 1.f;
@@ -1280,7 +1302,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     // thread chunk c = tid + 256 i is key c / CPK, bytes (c % CPK) * 16.. of the
     // tile: byte offset c * 16 from the tile's first key. Keys at or past
     // k_end (and chunks past the tile) fall outside the view and read as zero.
-    // a tile's keys are consecutive cache rows from km.row(tile), which the
+    // a tile's keys are consecutive cache rows from tile_row(tile), which the
     // K load of a tile looks up and the V load of the same tile reuses (no
     // tile wraps or crosses a page: see decode)
     auto load = [&](uint4 (&reg)[PCH], const unsigned char *base, int64_t row0, int tile) {
@@ -1513,12 +1535,12 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
     if (ntiles > 0) {
         // K(0), V(0) and K(1) go out together: one round trip to memory
         // before the first tile, not two (a short item is mostly this)
-        const int64_t row0 = km.row(it.k_begin);
+        const int64_t row0 = tile_row(it.k_begin);
         uint4 k0[PCH];
         load(k0, kbase, row0, it.k_begin);
         load(vreg, vbase, row0, it.k_begin);
         if (ntiles > 1) {
-            row_next = km.row(it.k_begin + KT);
+            row_next = tile_row(it.k_begin + KT);
             load(kreg, kbase, row_next, it.k_begin + KT);
         }
         scale_q();
@@ -1537,7 +1559,7 @@ __global__ __launch_bounds__(64 * PW) __attribute__((amdgpu_waves_per_eu(PW == 8
         // barrier, so they have the barrier wait as well as one iteration
         int64_t row_k2 = 0;
         if (i + 2 < ntiles) {
-            row_k2 = km.row(tile + 2 * KT);
+            row_k2 = tile_row(tile + 2 * KT);
             load(kreg, kbase, row_k2, tile + 2 * KT);
         }
         if (has_next) load(vreg, vbase, row_next, tile + KT);
